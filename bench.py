@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA hot path on one MI355X.
+
+One step = one chunkwise prefill (kda_chunk_fwd) of the K3-shape
+single-sequence workload: T = 4096 tokens, H = 96 heads, d_k = d_v = 128,
+bf16 inputs, fp32 state, h0 = 0 (the workload the headline "KDA prefill
+tokens/s @H=96, d=128" is quoted on).  Inputs are seeded synthetic tensors
+resident in HBM before timing; two input sets alternate so that consecutive
+steps do not hit in the 256 MiB Infinity Cache.  The decode half of the
+metric (decode state GB/s) is measured in the same run on the batched
+decode workload (256 sequences x 96 heads, one token each, state updated in
+place) and reported under "decode".
+
+Prints ONE JSON line.  `--gpus N` with N > 1 exits: this build is single-GPU.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/s @H=96,d=128 (% MFMA peak); decode state GB/s (% HBM)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA (2.5 PFLOP/s)
+D = 128
+
+
+def flops_per_head_token(C=64):
+    """Algorithmic flops per (token, head) of chunkwise KDA counted at chunk
+    length C: 6 d^2 for the three state products plus the causal halves of
+    the chunk-local products and the triangular solve."""
+    return 6 * D * D + D * (5 * C + 3) + C * C / 3.0
+
+
+def prefill_bytes(T, H, N, esize=2, h0=False):
+    """Algorithmic HBM bytes of one prefill: q, k, v, log_alpha (d each),
+    beta, o (d) per (token, head), plus 64 KiB per (sequence, head) for h_T
+    (and h0 when given)."""
+    per_ht = esize * (4 * D + 1 + D)
+    state = N * H * D * D * 4
+    return T * H * per_ht + state * (2 if h0 else 1)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gated_delta_rule_27_amd", "csrc")
+    for fn in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, fn), "rb") as f:
+            h.update(fn.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(name, src_hash):
+    """HBM bytes per launch measured with rocprofv3 counters, from the
+    committed summary; None if absent or taken on another kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{name}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_hash") != src_hash:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def time_launches(fn, steps, warmup, stream):
+    """Run fn `warmup` times, then `steps` times with a HIP event pair around
+    each launch on `stream`; returns (wall seconds, per-launch ms list)."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        fn(warmup + i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, [a.elapsed_time(b) for a, b in ev]
+
+
+def cpu_baseline(T, H):
+    """The fp32 CPU oracle on the whole prefill workload, on this host."""
+    import kda_inputs
+    import oracle
+    d = kda_inputs.prefill_inputs(T, H, dtype="bf16", device="cpu", seed=1001)
+    args = [kda_inputs.to_numpy(d[k]) for k in ("q", "k", "v", "log_alpha", "beta")]
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    oracle.fwd(*args, precision="f32", nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": round(T / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"whole prefill workload (T={T}, H={H}, d=128), fp32 oracle, "
+                      f"{dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--chunk", type=int, default=0, help="override the chunk length")
+    ap.add_argument("--split", type=int, default=0, help="override the column split")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
+              "the path is not sharded across GPUs", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_27_amd as kda
+    import kda_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py: no ROCm device", file=sys.stderr)
+        sys.exit(1)
+    if not os.path.exists(kda.LIB_PATH):
+        from gated_delta_rule_27_amd import build
+        build.build()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    # ---------------- prefill: T=4096, H=96, bf16 ----------------
+    T, H, N = 4096, 96, 1
+    sets = [kda_inputs.prefill_inputs(T, H, dtype="bf16", device=dev, seed=s)
+            for s in (1001, 1101)]
+    o = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+    hT = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
+
+    def step(i):
+        d = sets[i % 2]
+        kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"],
+                          chunk=args.chunk, dv_split=args.split, o=o, h_T=hT)
+
+    wall, ms = time_launches(step, args.steps, args.warmup, stream)
+    assert torch.isfinite(o.float()).all().item(), "non-finite prefill output"
+    avg_ms = sum(ms) / len(ms)
+    tokens_per_s = T * args.steps / wall
+    nbytes = prefill_bytes(T, H, N)
+    achieved = nbytes / (avg_ms * 1e-3) / 1e9
+    src_hash = kernel_source_hash()
+    traffic = read_traffic("chunk_fwd_T4096_H96_bf16", src_hash)
+    flops = T * H * flops_per_head_token(64)
+    mfma_frac = flops / (avg_ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "kda_prefill_T4096_H96_d128_bf16", "T": T, "H": H, "d": D,
+                   "sequences": N, "h0": "zero", "chunk": args.chunk or "auto",
+                   "dv_split": args.split or "auto"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "kda::chunk_kernel",
+                     "kernel_ms": round(avg_ms, 5), "algorithmic_bytes": nbytes},
+        "mfma": {"flops_per_step": flops, "counted_at_chunk": 64,
+                 "frac_of_bf16_peak": round(mfma_frac, 4)},
+        "kernel_source_hash": src_hash,
+    }
+    del sets
+    torch.cuda.empty_cache()
+
+    # ---------------- decode: 256 x 96 states, one token ----------------
+    if not args.no_decode:
+        B = 256
+        dd = kda_inputs.decode_inputs(B, H, dtype="bf16", device=dev, seed=1002)
+        od = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
+
+        def dstep(i):
+            kda.kda_decode_step(dd["q"], dd["k"], dd["v"], dd["log_alpha"], dd["beta"],
+                                dd["S"], o=od)
+
+        dwall, dms = time_launches(dstep, args.steps, args.warmup, stream)
+        davg = sum(dms) / len(dms)
+        state_bytes = B * H * D * D * 4 * 2
+        total_bytes = B * H * (D * D * 4 * 2 + 2 * (4 * D + 1 + D))
+        out["decode"] = {
+            "workload": "kda_decode_B256_H96_d128_bf16",
+            "state_GBps": round(state_bytes / (davg * 1e-3) / 1e9, 1),
+            "total_GBps": round(total_bytes / (davg * 1e-3) / 1e9, 1),
+            "ms_per_step": round(davg, 5),
+            "roofline": {"bound": "hbm",
+                         "achieved": round(total_bytes / (davg * 1e-3) / 1e9, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(total_bytes / (davg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "traffic": read_traffic("decode_B256_H96_bf16", src_hash),
+                         "kernel": "kda::decode_kernel"},
+        }
+        del dd
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(T, H)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,192 @@
+"""MI355X (gfx950) Kimi Delta Attention: Python binding of libkda.so.
+
+Thin ctypes marshalling over the C ABI in ``include/kda.h``; every step of
+the computation runs in the HIP kernels of ``csrc/``.  PyTorch supplies the
+device memory and the current stream only.  There is no fallback: if the
+library is not built, or a tensor is not on a ROCm device, the call raises.
+
+Functions (same names as the C entry points):
+
+* ``kda_chunk_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, ...)``
+  -> ``(o, h_T)``  chunkwise prefill over packed sequences;
+* ``kda_decode_step(q, k, v, log_alpha, beta, S)`` -> ``o``  one recurrent
+  step, ``S`` updated in place;
+* ``kda_chunk_fwd_workspace_size``, ``kda_status_str``, ``kda_abi_version``.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkda.so")
+
+KDA_F32, KDA_BF16 = 0, 1
+HEAD_DIM = 128
+
+_lib = None
+
+
+class KDAError(RuntimeError):
+    """A nonzero kda_status from the library."""
+
+    def __init__(self, code, msg):
+        super().__init__(msg)
+        self.code = code
+
+
+def lib():
+    """The loaded libkda.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is not built; run `python -m gated_delta_rule_27_amd.build` "
+                "(or __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        L.kda_abi_version.restype = ctypes.c_int
+        L.kda_abi_version.argtypes = []
+        L.kda_status_str.restype = ctypes.c_char_p
+        L.kda_status_str.argtypes = [ctypes.c_int]
+        L.kda_chunk_fwd_workspace_size.restype = sz
+        L.kda_chunk_fwd_workspace_size.argtypes = [i64, i32, i32, i32, i32, ctypes.c_int]
+        L.kda_chunk_fwd.restype = ctypes.c_int
+        L.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
+                                    ctypes.c_int, vp, vp, vp, sz, vp]
+        L.kda_chunk_fwd_ex.restype = ctypes.c_int
+        L.kda_chunk_fwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
+                                       ctypes.c_int, vp, vp, vp, sz, i32, i32, vp]
+        L.kda_decode_step.restype = ctypes.c_int
+        L.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                      ctypes.c_int, vp, vp]
+        _lib = L
+    return _lib
+
+
+def kda_abi_version():
+    return lib().kda_abi_version()
+
+
+def kda_status_str(code):
+    return lib().kda_status_str(int(code)).decode()
+
+
+def kda_chunk_fwd_workspace_size(T_total, N, H, Dk=HEAD_DIM, Dv=HEAD_DIM, dtype=KDA_BF16):
+    return lib().kda_chunk_fwd_workspace_size(int(T_total), int(N), int(H), int(Dk),
+                                              int(Dv), int(dtype))
+
+
+def _check(code):
+    if code != 0:
+        raise KDAError(code, kda_status_str(code))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _dev(t, name, dtype=None):
+    torch = _torch()
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a ROCm device (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def kda_chunk_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, chunk=0,
+                  dv_split=0, o=None, h_T=None, store_state=True):
+    """Chunkwise KDA prefill.
+
+    q, k, log_alpha: [T, H, 128]; v: [T, H, 128]; beta: [T, H]; all bf16 or
+    all fp32 on one device.  h0: [N, H, 128, 128] fp32 or None (zeros).
+    cu_seqlens: int32 [N+1] device offsets or None (one sequence).
+    Returns (o [T, H, 128] in the input dtype, h_T fp32 [N, H, 128, 128] or
+    None if store_state is False).  `chunk` / `dv_split` override the
+    library's tuning choice (0 = automatic).
+    """
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("beta", beta)):
+        _dev(t, name, q.dtype)
+    dt = _dtype_code(q)
+    if q.dim() != 3:
+        raise ValueError("q must be [T, H, D]")
+    T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if k.shape != q.shape or log_alpha.shape != q.shape or v.shape[:2] != (T, H) \
+            or tuple(beta.shape) != (T, H):
+        raise ValueError("inconsistent shapes")
+    if cu_seqlens is not None:
+        _dev(cu_seqlens, "cu_seqlens", torch.int32)
+        N = cu_seqlens.numel() - 1
+    else:
+        N = 1
+    _dev(h0, "h0", torch.float32)
+    if h0 is not None and tuple(h0.shape) != (N, H, Dk, Dv):
+        raise ValueError("h0 must be [N, H, Dk, Dv]")
+    if o is None:
+        o = torch.empty((T, H, Dv), dtype=q.dtype, device=q.device)
+    _dev(o, "o", q.dtype)
+    if store_state and h_T is None:
+        h_T = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    if not store_state:
+        h_T = None
+    _dev(h_T, "h_T", torch.float32)
+    ws_bytes = kda_chunk_fwd_workspace_size(T, N, H, Dk, Dv, dt)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    _check(lib().kda_chunk_fwd_ex(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0), _ptr(cu_seqlens),
+        N, T, H, Dk, Dv, dt, _ptr(o), _ptr(h_T), _ptr(ws), ws_bytes, int(chunk),
+        int(dv_split), _stream(q.device)))
+    return o, h_T
+
+
+def kda_decode_step(q, k, v, log_alpha, beta, S, *, o=None):
+    """One recurrent KDA step for B sequences; S [B, H, 128, 128] fp32 is
+    updated in place.  q, k, log_alpha, v: [B, H, 128]; beta: [B, H].
+    Returns o [B, H, 128] in the input dtype."""
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("beta", beta)):
+        _dev(t, name, q.dtype)
+    _dev(S, "S", torch.float32)
+    dt = _dtype_code(q)
+    B, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if k.shape != q.shape or log_alpha.shape != q.shape or v.shape[:2] != (B, H) \
+            or tuple(beta.shape) != (B, H) or tuple(S.shape) != (B, H, Dk, Dv):
+        raise ValueError("inconsistent shapes")
+    if o is None:
+        o = torch.empty((B, H, Dv), dtype=q.dtype, device=q.device)
+    _dev(o, "o", q.dtype)
+    _check(lib().kda_decode_step(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S), B, H, Dk, Dv, dt,
+        _ptr(o), _stream(q.device)))
+    return o
+
+
+__all__ = ["kda_chunk_fwd", "kda_decode_step", "kda_chunk_fwd_workspace_size",
+           "kda_status_str", "kda_abi_version", "KDAError", "lib", "LIB_PATH"]

@@ -1,0 +1,185 @@
+// kda_api.cpp -- the C ABI of libkda.so (declared in include/kda.h).
+//
+// Every entry point validates its arguments on the host before touching the
+// HIP runtime, so all error paths are reachable (and tested) without a GPU.
+// Kernel launches are asynchronous on the caller's stream.
+#include "kda.h"
+
+#include <stdint.h>
+
+#include <initializer_list>
+#include <limits>
+
+#include "kda_launch.h"
+
+namespace {
+
+struct Span {
+    uintptr_t lo = 0, hi = 0;  // [lo, hi); empty spans overlap nothing
+};
+
+Span span(const void* p, uint64_t bytes) {
+    Span s;
+    if (p && bytes) {
+        s.lo = reinterpret_cast<uintptr_t>(p);
+        s.hi = s.lo + bytes;
+    }
+    return s;
+}
+
+bool overlaps(const Span& a, const Span& b) {
+    return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+bool overlaps_any(const Span& a, std::initializer_list<Span> others) {
+    for (const Span& b : others)
+        if (overlaps(a, b)) return true;
+    return false;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool valid_dtype(kda_dtype dt) { return dt == KDA_F32 || dt == KDA_BF16; }
+
+uint64_t esize(kda_dtype dt) { return dt == KDA_F32 ? 4u : 2u; }
+
+// Largest element count a single tensor may have (keeps byte sizes in range).
+constexpr uint64_t kMaxElems = (uint64_t)1 << 56;
+
+}  // namespace
+
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_status_str(kda_status s) {
+    switch (s) {
+        case KDA_OK: return "KDA_OK";
+        case KDA_ERR_NULL_ARG: return "KDA_ERR_NULL_ARG: a required pointer is NULL";
+        case KDA_ERR_BAD_SHAPE: return "KDA_ERR_BAD_SHAPE: unsupported size or option";
+        case KDA_ERR_BAD_DTYPE: return "KDA_ERR_BAD_DTYPE: dtype is not KDA_F32 or KDA_BF16";
+        case KDA_ERR_MISALIGNED: return "KDA_ERR_MISALIGNED: a pointer is not 16-byte aligned";
+        case KDA_ERR_ALIAS: return "KDA_ERR_ALIAS: an output overlaps an input or another output";
+        case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace too small";
+        case KDA_ERR_DEVICE: return "KDA_ERR_DEVICE: a HIP call or kernel launch failed";
+    }
+    return "KDA_ERR_UNKNOWN";
+}
+
+size_t kda_chunk_fwd_workspace_size(int64_t T_total, int32_t N, int32_t H, int32_t Dk,
+                                    int32_t Dv, kda_dtype dt) {
+    (void)T_total;
+    (void)N;
+    (void)H;
+    (void)Dk;
+    (void)Dv;
+    (void)dt;
+    return 0;  // the fused chunk kernel keeps every intermediate on chip
+}
+
+kda_status kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* log_alpha,
+                            const void* beta, const float* h0, const int32_t* cu_seqlens,
+                            int32_t N, int64_t T_total, int32_t H, int32_t Dk, int32_t Dv,
+                            kda_dtype dt, void* o, float* h_T, void* workspace,
+                            size_t workspace_bytes, int32_t chunk, int32_t dv_split,
+                            hipStream_t stream) {
+    if (!valid_dtype(dt)) return KDA_ERR_BAD_DTYPE;
+    if (N < 1 || T_total < 0 || H < 1 || Dk != kda::kHeadDim || Dv != kda::kHeadDim)
+        return KDA_ERR_BAD_SHAPE;
+    if (!cu_seqlens && N != 1) return KDA_ERR_BAD_SHAPE;
+    const uint64_t row = (uint64_t)H * kda::kHeadDim;
+    if ((uint64_t)T_total > kMaxElems / row) return KDA_ERR_BAD_SHAPE;
+    if ((uint64_t)N * (uint64_t)H * 8u > (uint64_t)std::numeric_limits<int32_t>::max())
+        return KDA_ERR_BAD_SHAPE;
+    if (chunk != 0 && chunk != 16 && chunk != 32) return KDA_ERR_BAD_SHAPE;
+    if (dv_split != 0 && dv_split != 1 && dv_split != 2 && dv_split != 4) return KDA_ERR_BAD_SHAPE;
+
+    if (T_total > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERR_NULL_ARG;
+
+    for (const void* p : {q, k, v, log_alpha, beta, (const void*)h0, (const void*)o,
+                          (const void*)h_T, (const void*)workspace})
+        if (p && !aligned(p, 16)) return KDA_ERR_MISALIGNED;
+    if (cu_seqlens && !aligned(cu_seqlens, 4)) return KDA_ERR_MISALIGNED;
+
+    const uint64_t es = esize(dt);
+    const uint64_t nTok = (uint64_t)T_total * row;
+    const uint64_t nState = (uint64_t)N * H * kda::kHeadDim * kda::kHeadDim;
+    const Span sq = span(q, nTok * es), sk = span(k, nTok * es), sv = span(v, nTok * es),
+               sg = span(log_alpha, nTok * es), sb = span(beta, (uint64_t)T_total * H * es),
+               sh0 = span(h0, h0 ? nState * 4 : 0),
+               scu = span(cu_seqlens, cu_seqlens ? (uint64_t)(N + 1) * 4 : 0),
+               so = span(o, nTok * es), shT = span(h_T, h_T ? nState * 4 : 0),
+               sws = span(workspace, workspace_bytes);
+    if (overlaps_any(so, {sq, sk, sv, sg, sb, sh0, scu, sws})) return KDA_ERR_ALIAS;
+    if (overlaps_any(shT, {sq, sk, sv, sg, sb, sh0, scu, so, sws})) return KDA_ERR_ALIAS;
+
+    const size_t need = kda_chunk_fwd_workspace_size(T_total, N, H, Dk, Dv, dt);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
+
+    int c = 0, s = 0;
+    kda::chunk_default_config((int)dt, T_total, N, H, &c, &s);
+    if (chunk) c = chunk;
+    if (dv_split) s = dv_split;
+    if (!kda::chunk_config_supported((int)dt, c, s)) return KDA_ERR_BAD_SHAPE;
+
+    kda::ChunkArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.log_alpha = log_alpha;
+    a.beta = beta;
+    a.h0 = h0;
+    a.cu_seqlens = cu_seqlens;
+    a.N = N;
+    a.T_total = T_total;
+    a.H = H;
+    a.o = o;
+    a.h_T = h_T;
+    if (kda::launch_chunk(a, (int)dt, c, s, stream) != hipSuccess) return KDA_ERR_DEVICE;
+    return KDA_OK;
+}
+
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* log_alpha,
+                         const void* beta, const float* h0, const int32_t* cu_seqlens, int32_t N,
+                         int64_t T_total, int32_t H, int32_t Dk, int32_t Dv, kda_dtype dt,
+                         void* o, float* h_T, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+    return kda_chunk_fwd_ex(q, k, v, log_alpha, beta, h0, cu_seqlens, N, T_total, H, Dk, Dv, dt,
+                            o, h_T, workspace, workspace_bytes, 0, 0, stream);
+}
+
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* log_alpha,
+                           const void* beta, float* S, int32_t B, int32_t H, int32_t Dk,
+                           int32_t Dv, kda_dtype dt, void* o, hipStream_t stream) {
+    if (!valid_dtype(dt)) return KDA_ERR_BAD_DTYPE;
+    if (B < 0 || H < 1 || Dk != kda::kHeadDim || Dv != kda::kHeadDim) return KDA_ERR_BAD_SHAPE;
+    if ((uint64_t)B * (uint64_t)H > (uint64_t)std::numeric_limits<int32_t>::max())
+        return KDA_ERR_BAD_SHAPE;
+    if (B > 0 && (!q || !k || !v || !log_alpha || !beta || !S || !o)) return KDA_ERR_NULL_ARG;
+    for (const void* p : {q, k, v, log_alpha, beta, (const void*)S, (const void*)o})
+        if (p && !aligned(p, 16)) return KDA_ERR_MISALIGNED;
+
+    const uint64_t es = esize(dt);
+    const uint64_t nVec = (uint64_t)B * H * kda::kHeadDim;
+    const Span sq = span(q, nVec * es), sk = span(k, nVec * es), sv = span(v, nVec * es),
+               sg = span(log_alpha, nVec * es), sb = span(beta, (uint64_t)B * H * es),
+               sS = span(S, nVec * kda::kHeadDim * 4), so = span(o, nVec * es);
+    if (overlaps_any(so, {sq, sk, sv, sg, sb, sS})) return KDA_ERR_ALIAS;
+    if (overlaps_any(sS, {sq, sk, sv, sg, sb})) return KDA_ERR_ALIAS;
+    if (B == 0) return KDA_OK;
+
+    kda::DecodeArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.log_alpha = log_alpha;
+    a.beta = beta;
+    a.S = S;
+    a.B = B;
+    a.H = H;
+    a.o = o;
+    if (kda::launch_decode(a, (int)dt, stream) != hipSuccess) return KDA_ERR_DEVICE;
+    return KDA_OK;
+}
+
+}  // extern "C"

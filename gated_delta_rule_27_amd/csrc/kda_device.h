@@ -1,0 +1,115 @@
+// kda_device.h -- device-side building blocks shared by the KDA kernels
+// (gfx950 / CDNA4).  Internal header of libkda.so.
+//
+// MFMA fragments.  All matrix products use 16x16 output tiles held as four
+// fp32 per lane: lane l holds column (l % 16) and rows 4*(l/16) .. +3.
+// For a contraction over k, lane group g = l/16 of the A operand (row
+// l % 16) and of the B operand (column l % 16) must hold the SAME k indices;
+// which ones is free.  This library assigns, per k-block:
+//   bf16 16x16x32 : elements 0..3 -> k = kb + 4g + 0..3,
+//                   elements 4..7 -> k = kb + 16 + 4g + 0..3;
+//   bf16 16x16x16 : elements 0..3 -> k = kb + 4g + 0..3;
+//   fp32 16x16x4  : four MFMAs j = 0..3, MFMA j uses k = kb + 4g + j.
+// With that choice an fp32 accumulator tile (rows 4g..4g+3 in the lane) is
+// directly a B operand over its 16 rows, so products that chain (state ->
+// pseudo-values -> new state) never leave registers.  An A operand is read
+// from LDS as a row with k contiguous.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+
+typedef __bf16 bf16;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // RNE
+
+__device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
+
+// ---- MFMA wrappers ---------------------------------------------------------
+
+__device__ __forceinline__ floatx4 mma_bf16_k32(bf16x8 a, bf16x8 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ floatx4 mma_bf16_k16(bf16x4 a, bf16x4 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+        __builtin_bit_cast(shortx4, a), __builtin_bit_cast(shortx4, b), c, 0, 0, 0);
+}
+
+// k = 16 in fp32: four 16x16x4 MFMAs, MFMA j on element j of a and b.
+__device__ __forceinline__ floatx4 mma_f32_k16(floatx4 a, floatx4 b, floatx4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
+    return c;
+}
+
+// ---- fragments -------------------------------------------------------------
+
+// bf16 operand over k-block [kb, kb+32) from an LDS row (k contiguous).
+__device__ __forceinline__ bf16x8 frag_k32(const bf16* row, int kb, int g) {
+    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row + kb + 4 * g);
+    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + kb + 16 + 4 * g);
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// bf16 operand over k-block [kb, kb+16).
+__device__ __forceinline__ bf16x4 frag_k16(const bf16* row, int kb, int g) {
+    return *reinterpret_cast<const bf16x4*>(row + kb + 4 * g);
+}
+
+// fp32 operand over k-block [kb, kb+16).
+__device__ __forceinline__ floatx4 frag_k16(const float* row, int kb, int g) {
+    return *reinterpret_cast<const floatx4*>(row + kb + 4 * g);
+}
+
+// B operand from accumulator tiles: rows kb..kb+15 (lo) and kb+16..kb+31 (hi).
+__device__ __forceinline__ bf16x8 acc_frag_k32(floatx4 lo, floatx4 hi) {
+    return bf16x8{(bf16)lo[0], (bf16)lo[1], (bf16)lo[2], (bf16)lo[3],
+                  (bf16)hi[0], (bf16)hi[1], (bf16)hi[2], (bf16)hi[3]};
+}
+__device__ __forceinline__ bf16x4 acc_frag_k16(floatx4 t) {
+    return bf16x4{(bf16)t[0], (bf16)t[1], (bf16)t[2], (bf16)t[3]};
+}
+
+// ---- wavefront reductions ---------------------------------------------------
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+// ---- vector global loads of 4 or 8 elements ----------------------------------
+
+template <typename T>
+struct Vec16;  // 16 bytes of T
+template <>
+struct Vec16<float> {
+    static constexpr int N = 4;
+    typedef floatx4 type;
+};
+template <>
+struct Vec16<bf16> {
+    static constexpr int N = 8;
+    typedef bf16x8 type;
+};
+
+}  // namespace kda

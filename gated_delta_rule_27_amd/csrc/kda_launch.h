@@ -1,0 +1,50 @@
+// kda_launch.h -- internal interface between the C ABI (kda_api.cpp) and the
+// kernel launchers (kda_chunk.hip, kda_decode.hip).  Arguments arrive here
+// already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int kHeadDim = 128;  // d_k = d_v of the K3 KDA head
+
+struct ChunkArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* log_alpha;
+    const void* beta;
+    const float* h0;          // may be null (zero state)
+    const int32_t* cu_seqlens;  // device, may be null (one sequence)
+    int32_t N;
+    int64_t T_total;
+    int32_t H;
+    void* o;
+    float* h_T;               // may be null
+};
+
+struct DecodeArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* log_alpha;
+    const void* beta;
+    float* S;
+    int32_t B;
+    int32_t H;
+    void* o;
+};
+
+// dtype: 0 = fp32, 1 = bf16 (kda_dtype values).
+// chunk in {16, 32}; split = workgroups per head (value-column slices).
+bool chunk_config_supported(int dtype, int chunk, int split);
+void chunk_default_config(int dtype, int64_t T_total, int32_t N, int32_t H,
+                          int* chunk, int* split);
+hipError_t launch_chunk(const ChunkArgs& a, int dtype, int chunk, int split,
+                        hipStream_t stream);
+
+hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream);
+
+}  // namespace kda

@@ -1,0 +1,155 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention library
+ *          (libkda.so, built from gated_delta_rule_27_amd/csrc).
+ *
+ * The operation.  Per head, on a d_k x d_v fp32 state S (row i = key
+ * channel, column j = value channel), every token t applies
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,
+ *     o_t = S_t^T q_t,          alpha_t = exp(log_alpha_t) per key channel,
+ *
+ * ("Kimi K3 Architecture Explained", Step 3 "Forgetting, Channel by
+ * Channel", the KDA equation; "An infra-oriented diagram of Kimi K3", KDA
+ * card).  Decay acts on the old state before the erase and the write, and
+ * the read uses the state after the token's own update ("From GPT-2 to
+ * Kimi K3, from first principles", ch. 5 "Read the recurrence as four
+ * verbs" and ch. 6 "Chunkwise execution").  There is no 1/sqrt(d_k) factor
+ * on the read (the pages give none; q and k are L2-normalised upstream).
+ *
+ * Two regimes, as in the pages' mode rule (ch. 6 "Training, prefill, and
+ * decode use different paths"): multi-token prefill runs chunkwise
+ * (kda_chunk_fwd), a single cached token runs one fused recurrent step
+ * (kda_decode_step).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers to contiguous row-major
+ *     memory, 16-byte aligned.  The caller owns every buffer; the library
+ *     never allocates or frees device memory and keeps no state between
+ *     calls except a per-device property cache.
+ *   - Work is enqueued on `stream` (NULL = the default stream); no call
+ *     synchronises the stream.  Buffers must stay valid until the queued
+ *     work has finished.
+ *   - Arguments are validated on the host before any HIP call; on an error
+ *     nothing is launched and the outputs are untouched.  KDA_ERR_DEVICE
+ *     reports a launch failure (the outputs are then unspecified).
+ *   - d_k = d_v = 128 (the K3 head shape, "An infra-oriented diagram of
+ *     Kimi K3", KDA card).  Other sizes return KDA_ERR_BAD_SHAPE.
+ *   - Input contract (not checked, never clamped): log_alpha in [-5, 0]
+ *     (the K3 lower-bounded log-decay, "From GPT-2 to Kimi K3", ch. 5
+ *     "K3's lower-bounded decay"), beta in [0, 1].  Inside the contract the
+ *     chunk kernels' decay factors stay finite (a 16-token tile's reciprocal
+ *     cumulative decay is below e^80).
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_NULL_ARG = 1,   /* a required pointer is NULL                    */
+    KDA_ERR_BAD_SHAPE = 2,  /* a size <= 0 (or < 0 where 0 is allowed),
+                               d_k or d_v != 128, N != 1 without cu_seqlens,
+                               or an unsupported chunk / split override      */
+    KDA_ERR_BAD_DTYPE = 3,  /* dtype is not a kda_dtype                      */
+    KDA_ERR_MISALIGNED = 4, /* a pointer is not 16-byte aligned              */
+    KDA_ERR_ALIAS = 5,      /* an output overlaps an input or another output */
+    KDA_ERR_WORKSPACE = 6,  /* workspace smaller than the size reported      */
+    KDA_ERR_DEVICE = 7      /* a HIP call or kernel launch failed            */
+} kda_status;
+
+/* Storage type of q, k, v, log_alpha, beta and o.  States are always fp32. */
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/* Bytes of device workspace kda_chunk_fwd needs for these sizes (0 means
+ * workspace may be NULL).  Never fails; returns 0 for invalid sizes. */
+size_t kda_chunk_fwd_workspace_size(int64_t T_total, int32_t N, int32_t H,
+                                    int32_t Dk, int32_t Dv, kda_dtype dt);
+
+/*
+ * Chunkwise prefill over N packed sequences.
+ *
+ *   q, k, log_alpha : [T_total, H, Dk]  dt
+ *   v               : [T_total, H, Dv]  dt
+ *   beta            : [T_total, H]      dt
+ *   h0              : [N, H, Dk, Dv] fp32, read only; NULL = zero state
+ *   cu_seqlens      : [N + 1] int32 DEVICE offsets of the packed sequences
+ *                     ("An infra-oriented diagram of Kimi K3": several
+ *                     documents share the packed tokens, cumulative offsets
+ *                     keep their boundaries); NULL = one sequence (N == 1).
+ *                     Precondition (not checked): cu[0] = 0, non-decreasing,
+ *                     cu[N] = T_total.  Zero-length sequences are allowed
+ *                     (their h_T is h0).
+ *   o               : [T_total, H, Dv]  dt (output; round-to-nearest-even
+ *                     from fp32 for bf16)
+ *   h_T             : [N, H, Dk, Dv] fp32 final states; NULL = not stored.
+ *                     Must not overlap h0: a stored snapshot is never
+ *                     mutated ("From GPT-2 to Kimi K3", ch. 14 "Serving a
+ *                     hybrid cache": restored snapshots are read-only).
+ *   workspace       : device scratch of at least
+ *                     kda_chunk_fwd_workspace_size(...) bytes (may be NULL
+ *                     when that size is 0).
+ * The state resets to h0[n] (or zero) at every sequence start; chunks are
+ * aligned to each sequence's first token and the last chunk may be partial.
+ * T_total == 0 is allowed (only h_T is written).
+ */
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
+                         const void* log_alpha, const void* beta,
+                         const float* h0, const int32_t* cu_seqlens, int32_t N,
+                         int64_t T_total, int32_t H, int32_t Dk, int32_t Dv,
+                         kda_dtype dt, void* o, float* h_T, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * kda_chunk_fwd with explicit tuning choices.  chunk = tokens per chunk
+ * (16, 32 or 64; 0 = library choice); dv_split = number of workgroups that
+ * share one head's value columns (1, 2, 4 or 8; 0 = library choice).  The
+ * chunk length is a tuning parameter, not a property of the recurrence
+ * ("From GPT-2 to Kimi K3", ch. 6 "Chunkwise execution"): every choice
+ * computes the same function up to rounding.  Unsupported combinations
+ * return KDA_ERR_BAD_SHAPE.
+ */
+kda_status kda_chunk_fwd_ex(const void* q, const void* k, const void* v,
+                            const void* log_alpha, const void* beta,
+                            const float* h0, const int32_t* cu_seqlens,
+                            int32_t N, int64_t T_total, int32_t H, int32_t Dk,
+                            int32_t Dv, kda_dtype dt, void* o, float* h_T,
+                            void* workspace, size_t workspace_bytes,
+                            int32_t chunk, int32_t dv_split,
+                            hipStream_t stream);
+
+/*
+ * One recurrent step for B independent sequences (single-token cached
+ * decode; "From GPT-2 to Kimi K3", ch. 6, the fused recurrent path).
+ *
+ *   q, k, log_alpha : [B, H, Dk]  dt
+ *   v               : [B, H, Dv]  dt
+ *   beta            : [B, H]      dt
+ *   S               : [B, H, Dk, Dv] fp32, updated IN PLACE to S_t
+ *   o               : [B, H, Dv]  dt, o = S_t^T q
+ * B == 0 is allowed (nothing is launched).
+ */
+kda_status kda_decode_step(const void* q, const void* k, const void* v,
+                           const void* log_alpha, const void* beta, float* S,
+                           int32_t B, int32_t H, int32_t Dk, int32_t Dv,
+                           kda_dtype dt, void* o, hipStream_t stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* kda_status_str(kda_status s);
+
+/* KDA_ABI_VERSION of the built library. */
+int kda_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H */

@@ -1,0 +1,150 @@
+"""The C ABI on the CPU: the library loads, exports what include/kda.h
+declares, and every argument error is reported before any HIP call.
+
+No test here launches work: the pointers are fake (never dereferenced),
+and every call is one that validation rejects.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_27_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+OK, NULL_ARG, BAD_SHAPE, BAD_DTYPE, MISALIGNED, ALIAS, WORKSPACE, DEVICE = range(8)
+F32, BF16 = 0, 1
+D = 128
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(kda.LIB_PATH):
+        from gated_delta_rule_27_amd import build
+        build.build()
+    return kda.lib()
+
+
+def declared_functions():
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert {"kda_chunk_fwd", "kda_chunk_fwd_ex", "kda_decode_step",
+            "kda_chunk_fwd_workspace_size", "kda_status_str", "kda_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings(L):
+    assert kda.kda_abi_version() == 1
+    for code in range(8):
+        s = kda.kda_status_str(code)
+        assert s.startswith("KDA_")
+    assert kda.kda_status_str(99) == "KDA_ERR_UNKNOWN"
+    assert kda.kda_chunk_fwd_workspace_size(4096, 1, 96) == 0
+
+
+# fake, 16-byte aligned, non-overlapping device addresses
+BASE = 1 << 40
+GAP = 1 << 36
+
+
+def P(i, off=0):
+    return ctypes.c_void_p(BASE + i * GAP + off)
+
+
+def chunk(L, **kw):
+    a = dict(q=P(0), k=P(1), v=P(2), g=P(3), b=P(4), h0=P(5), cu=P(6), N=1, T=64, H=2,
+             Dk=D, Dv=D, dt=BF16, o=P(7), hT=P(8), ws=None, wsb=0, chunk=0, split=0,
+             stream=None)
+    a.update(kw)
+    return L.kda_chunk_fwd_ex(a["q"], a["k"], a["v"], a["g"], a["b"], a["h0"], a["cu"],
+                              a["N"], a["T"], a["H"], a["Dk"], a["Dv"], a["dt"], a["o"],
+                              a["hT"], a["ws"], a["wsb"], a["chunk"], a["split"], a["stream"])
+
+
+def decode(L, **kw):
+    a = dict(q=P(0), k=P(1), v=P(2), g=P(3), b=P(4), S=P(5), B=4, H=2, Dk=D, Dv=D, dt=BF16,
+             o=P(6), stream=None)
+    a.update(kw)
+    return L.kda_decode_step(a["q"], a["k"], a["v"], a["g"], a["b"], a["S"], a["B"], a["H"],
+                             a["Dk"], a["Dv"], a["dt"], a["o"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=2), BAD_DTYPE),
+    (dict(dt=-1), BAD_DTYPE),
+    (dict(Dk=64), BAD_SHAPE),
+    (dict(Dv=256), BAD_SHAPE),
+    (dict(N=0), BAD_SHAPE),
+    (dict(H=0), BAD_SHAPE),
+    (dict(T=-1), BAD_SHAPE),
+    (dict(N=2, cu=None), BAD_SHAPE),
+    (dict(chunk=48), BAD_SHAPE),
+    (dict(chunk=8), BAD_SHAPE),
+    (dict(split=3), BAD_SHAPE),
+    (dict(split=8), BAD_SHAPE),
+    (dict(q=None), NULL_ARG),
+    (dict(k=None), NULL_ARG),
+    (dict(v=None), NULL_ARG),
+    (dict(g=None), NULL_ARG),
+    (dict(b=None), NULL_ARG),
+    (dict(o=None), NULL_ARG),
+    (dict(q=P(0, 8)), MISALIGNED),
+    (dict(o=P(7, 4)), MISALIGNED),
+    (dict(h0=P(5, 2)), MISALIGNED),
+    (dict(hT=P(8, 12)), MISALIGNED),
+    (dict(cu=P(6, 2)), MISALIGNED),
+    (dict(o=P(0, 64)), ALIAS),           # o inside q
+    (dict(o=P(4)), ALIAS),               # o on beta
+    (dict(hT=P(5)), ALIAS),              # h_T on h0: snapshots are read only
+    (dict(hT=P(7, 256)), ALIAS),         # h_T inside o
+    (dict(hT=P(6)), ALIAS),              # h_T on cu_seqlens
+])
+def test_chunk_argument_errors(L, kw, code):
+    assert chunk(L, **kw) == code
+
+
+def test_chunk_error_precedence(L):
+    # dtype before shape before null before alignment before aliasing
+    assert chunk(L, dt=5, Dk=1, q=None) == BAD_DTYPE
+    assert chunk(L, Dk=1, q=None) == BAD_SHAPE
+    assert chunk(L, q=None, o=P(7, 4)) == NULL_ARG
+    assert chunk(L, o=P(0, 4)) == MISALIGNED
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=7), BAD_DTYPE),
+    (dict(B=-1), BAD_SHAPE),
+    (dict(H=0), BAD_SHAPE),
+    (dict(Dk=32), BAD_SHAPE),
+    (dict(S=None), NULL_ARG),
+    (dict(o=None), NULL_ARG),
+    (dict(q=None), NULL_ARG),
+    (dict(S=P(5, 8)), MISALIGNED),
+    (dict(o=P(5, 4096)), ALIAS),         # o inside the state
+    (dict(o=P(1)), ALIAS),
+    (dict(S=P(2, 64)), ALIAS),           # state over v
+])
+def test_decode_argument_errors(L, kw, code):
+    assert decode(L, **kw) == code
+
+
+def test_empty_decode_launches_nothing(L):
+    # B == 0 is a valid no-op that returns before any HIP call
+    assert decode(L, B=0, q=None, k=None, v=None, g=None, b=None, S=None, o=None) == OK
+
+
+def test_binding_refuses_host_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(4, 2, D, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="ROCm device"):
+        kda.kda_chunk_fwd(x, x, x, x, torch.zeros(4, 2, dtype=torch.bfloat16))

@@ -1,0 +1,155 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle,
+element by element, on the same seeded inputs.
+
+Tolerance (normwise, max|x - ref| / max|ref| per output tensor): 1e-4 for
+fp32 inputs, 2e-2 for bf16 inputs with fp32 state and accumulation.
+Small cases span several chunks and a ragged tail; the five workloads run
+at full size in the launch configuration the benchmark times, the largest
+two checked on sampled (document, head) units.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kda_inputs
+import oracle
+from gpu_util import TOL, case, check, gpu_prefill, need_gpu, np_, oracle_prefill
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    # dtype, lengths, H, h0_std, chunk, split
+    ("f32", [128], 2, None, 16, 0),             # the tiny workload, chunk 16
+    ("f32", [100], 3, 0.5, 16, 1),
+    ("f32", [100], 3, 0.5, 16, 2),
+    ("f32", [100], 3, 0.5, 16, 4),
+    ("f32", [100], 3, 0.5, 32, 1),
+    ("f32", [100], 3, 0.5, 32, 4),
+    ("bf16", [100], 3, 0.5, 16, 1),
+    ("bf16", [100], 3, 0.5, 32, 1),
+    ("bf16", [100], 3, 0.5, 32, 2),
+    ("bf16", [100], 3, 0.5, 32, 4),
+    ("f32", [0, 1, 37, 16, 100, 5], 2, 0.3, 16, 0),   # varlen with empty docs
+    ("f32", [0, 1, 37, 16, 100, 5], 2, 0.3, 32, 0),
+    ("bf16", [0, 1, 37, 16, 100, 5], 2, 0.3, 32, 0),
+    ("bf16", [1000], 8, None, 0, 0),
+    ("bf16", [333, 31, 700], 4, 0.02, 0, 0),
+]
+
+
+@pytest.mark.parametrize("dtype,lengths,H,h0_std,chunk,split", SMALL)
+def test_small_parity(dtype, lengths, H, h0_std, chunk, split):
+    kda = need_gpu()
+    T = sum(lengths)
+    case(f"small dtype={dtype} lengths={lengths} H={H} h0_std={h0_std} chunk={chunk} split={split}")
+    d = kda_inputs.prefill_inputs(T, H, dtype=dtype, device="cuda", seed=42 + T + H,
+                                  lengths=lengths if len(lengths) > 1 else None,
+                                  h0_std=h0_std)
+    o, hT = gpu_prefill(kda, d, chunk, split)
+    ro, rh = oracle_prefill(d)
+    check("o", np_(o), ro, TOL[dtype])
+    check("h_T", np_(hT), rh, TOL[dtype])
+
+
+def test_all_empty_sequences_return_h0():
+    kda = need_gpu()
+    case("T_total = 0 with three empty documents")
+    H = 2
+    h0 = torch.randn(3, H, 128, 128, device="cuda")
+    z = torch.empty(0, H, 128, dtype=torch.bfloat16, device="cuda")
+    b = torch.empty(0, H, dtype=torch.bfloat16, device="cuda")
+    cu = torch.zeros(4, dtype=torch.int32, device="cuda")
+    o, hT = kda.kda_chunk_fwd(z, z, z, z, b, h0=h0, cu_seqlens=cu)
+    torch.cuda.synchronize()
+    assert o.shape == (0, H, 128)
+    assert torch.equal(hT, h0)
+
+
+def test_workload_tiny_prefill():
+    """The tiny workload: T=128, H=2, fp32, chunk 16, h0 = 0."""
+    kda = need_gpu()
+    case("workload tiny_prefill_T128_H2_f32 chunk=16")
+    d = kda_inputs.config_inputs(0, device="cuda")
+    o, hT = gpu_prefill(kda, d, chunk=16)
+    ro, rh = oracle_prefill(d)
+    check("o", np_(o), ro, TOL["f32"])
+    check("h_T", np_(hT), rh, TOL["f32"])
+
+
+def test_workload_prefill_4k():
+    """Single-sequence K3-shape prefill, T=4096, H=96, bf16: every head."""
+    kda = need_gpu()
+    case("workload prefill_T4096_H96_bf16 (default launch)")
+    d = kda_inputs.config_inputs(1, device="cuda")
+    o, hT = gpu_prefill(kda, d)
+    ro, rh = oracle_prefill(d)
+    check("o", np_(o), ro, TOL["bf16"])
+    check("h_T", np_(hT), rh, TOL["bf16"])
+
+
+def test_workload_decode_batch256():
+    """Batched decode: 256 x 96 states, one token, S updated in place."""
+    kda = need_gpu()
+    case("workload decode_B256_H96_bf16")
+    d = kda_inputs.config_inputs(2, device="cuda")
+    S0 = np_(d["S"]).copy()
+    ro, rS = oracle.decode(np_(d["q"]), np_(d["k"]), np_(d["v"]), np_(d["log_alpha"]),
+                           np_(d["beta"]), S0)
+    o = kda.kda_decode_step(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S"])
+    torch.cuda.synchronize()
+    check("o", np_(o), ro, TOL["bf16"])
+    # the state is fp32 end to end: hold it to the fp32 bar
+    check("S", np_(d["S"]), rS, TOL["f32"])
+
+
+def _sampled_units(cu, H, rng, k):
+    """(document, head) units: the longest document's head 0 and last head,
+    plus k seeded random units."""
+    lens = np.diff(cu)
+    longest = int(np.argmax(lens))
+    units = [(longest, 0), (longest, H - 1)]
+    for _ in range(k):
+        units.append((int(rng.integers(0, len(lens))), int(rng.integers(0, H))))
+    return units
+
+
+def test_workload_varlen_16docs():
+    """Varlen packed prefill: 16 documents U{512..8192}, per-document h0,
+    H=96, bf16.  Full GPU run; oracle on sampled (document, head) units."""
+    kda = need_gpu()
+    d = kda_inputs.config_inputs(3, device="cuda")
+    cu = d["cu_seqlens"].cpu().numpy().astype(np.int64)
+    case(f"workload varlen_prefill_16docs_H96_bf16 T={int(cu[-1])}")
+    o, hT = gpu_prefill(kda, d)
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([1003, 98])))
+    H = d["q"].shape[1]
+    for (n, h) in _sampled_units(cu, H, rng, 6):
+        s, e = int(cu[n]), int(cu[n + 1])
+        sl = lambda t: np_(t[s:e, h:h + 1].contiguous())
+        ro, rh = oracle.fwd(sl(d["q"]), sl(d["k"]), sl(d["v"]), sl(d["log_alpha"]),
+                            np_(d["beta"][s:e, h:h + 1].contiguous()),
+                            h0=np_(d["h0"][n:n + 1, h:h + 1].contiguous()))
+        print(f"  unit doc={n} (len {e - s}) head={h}", flush=True)
+        check("o", np_(o[s:e, h:h + 1].contiguous()), ro, TOL["bf16"])
+        check("h_T", np_(hT[n:n + 1, h:h + 1].contiguous()), rh, TOL["bf16"])
+
+
+def test_workload_prefill_1m_sampled_heads():
+    """Long-context prefill, T=1,048,576, H=96, bf16.  Full GPU run; the
+    oracle replays all tokens of heads {0, 95} and two seeded heads."""
+    kda = need_gpu()
+    case("workload prefill_T1048576_H96_bf16: generating inputs on the device")
+    d = kda_inputs.config_inputs(4, device="cuda")
+    case("workload prefill_T1048576_H96_bf16: GPU run")
+    o, hT = gpu_prefill(kda, d)
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([1004, 98])))
+    heads = [0, 95] + [int(x) for x in rng.choice(np.arange(1, 95), size=2, replace=False)]
+    sl = lambda t: np_(t[:, heads].contiguous())
+    case(f"oracle on heads {heads} over all tokens")
+    ro, rh = oracle.fwd(sl(d["q"]), sl(d["k"]), sl(d["v"]), sl(d["log_alpha"]),
+                        np_(d["beta"][:, heads].contiguous()), dv_block=32)
+    go, gh = np_(o[:, heads].contiguous()), np_(hT[:, heads].contiguous())
+    for i, h in enumerate(heads):
+        print(f"  head {h}", flush=True)
+        check("o", go[:, i], ro[:, i], TOL["bf16"])
+        check("h_T", gh[:, i], rh[:, i], TOL["bf16"])

@@ -1,0 +1,120 @@
+"""GPU properties that hold at any size: chunk-length and column-split
+invariance, bitwise determinism, read-only inputs and h0, resume
+equivalence, varlen = independent runs, decode = one-token prefill."""
+import numpy as np
+import pytest
+import torch
+
+import kda_inputs
+from gpu_util import TOL, case, check, gpu_prefill, need_gpu, np_, oracle_prefill
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chunk_and_split_invariance(dtype):
+    """The chunk length and the column split are tuning choices: every
+    combination matches the oracle (and each other) within tolerance."""
+    kda = need_gpu()
+    case(f"chunk/split invariance dtype={dtype} T=517 H=4")
+    d = kda_inputs.prefill_inputs(517, 4, dtype=dtype, device="cuda", seed=5, h0_std=0.1)
+    ro, rh = oracle_prefill(d)
+    outs = {}
+    for c in (16, 32):
+        for s in (1, 2, 4):
+            print(f"  chunk={c} split={s}", flush=True)
+            o, hT = gpu_prefill(kda, d, c, s)
+            check("o", np_(o), ro, TOL[dtype])
+            check("h_T", np_(hT), rh, TOL[dtype])
+            outs[(c, s)] = (np_(o), np_(hT))
+    # the column split changes no arithmetic: same chunk length, same bits
+    for c in (16, 32):
+        for s in (2, 4):
+            assert np.array_equal(outs[(c, s)][0], outs[(c, 1)][0])
+            assert np.array_equal(outs[(c, s)][1], outs[(c, 1)][1])
+
+
+def test_deterministic_and_inputs_untouched():
+    kda = need_gpu()
+    case("determinism + read-only inputs, bf16 T=1024 H=16 with h0")
+    d = kda_inputs.prefill_inputs(1024, 16, dtype="bf16", device="cuda", seed=6,
+                                  lengths=[300, 724], h0_std=0.02)
+    before = {k: v.clone() for k, v in d.items() if isinstance(v, torch.Tensor)}
+    o1, h1 = gpu_prefill(kda, d)
+    o2, h2 = gpu_prefill(kda, d)
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+    for k, v in before.items():
+        assert torch.equal(d[k], v), f"{k} was modified"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_resume_equals_single_pass(dtype):
+    """fwd(T1 + T2) equals fwd(T2, h0 = h_T(T1)) up to rounding."""
+    kda = need_gpu()
+    case(f"resume dtype={dtype} T=700 split at 333")
+    T, T1, H = 700, 333, 3
+    d = kda_inputs.prefill_inputs(T, H, dtype=dtype, device="cuda", seed=7, h0_std=0.1)
+    o, hT = gpu_prefill(kda, d)
+    a = {k: (v[:T1] if k in ("q", "k", "v", "log_alpha", "beta") else v) for k, v in d.items()}
+    o1, h1 = gpu_prefill(kda, a)
+    b = {k: (v[T1:].contiguous() if k in ("q", "k", "v", "log_alpha", "beta") else v)
+         for k, v in d.items()}
+    b["h0"] = h1
+    o2, h2 = gpu_prefill(kda, b)
+    check("o", np_(torch.cat([o1, o2])), np_(o), TOL[dtype])
+    check("h_T", np_(h2), np_(hT), TOL[dtype])
+
+
+def test_varlen_equals_separate_runs():
+    kda = need_gpu()
+    case("varlen vs separate runs, bf16 lengths [64, 1, 0, 95]")
+    lens = [64, 1, 0, 95]
+    d = kda_inputs.prefill_inputs(sum(lens), 2, dtype="bf16", device="cuda", seed=8,
+                                  lengths=lens, h0_std=0.1)
+    o, hT = gpu_prefill(kda, d)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    for n in range(len(lens)):
+        s, e = int(cu[n]), int(cu[n + 1])
+        sub = {k: (v[s:e].contiguous() if k in ("q", "k", "v", "log_alpha", "beta") else v)
+               for k, v in d.items()}
+        sub["h0"] = d["h0"][n:n + 1].contiguous()
+        sub["cu_seqlens"] = None
+        on, hn = gpu_prefill(kda, sub)
+        assert torch.equal(on, o[s:e])
+        assert torch.equal(hn[0], hT[n])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_equals_one_token_prefill(dtype):
+    """The fused recurrent step and the chunk path agree on T = 1."""
+    kda = need_gpu()
+    case(f"decode vs one-token prefill dtype={dtype} B=7 H=5")
+    B, H = 7, 5
+    dd = kda_inputs.decode_inputs(B, H, dtype=dtype, device="cuda", seed=9, state_std=0.3)
+    S = dd["S"].clone()
+    od = kda.kda_decode_step(dd["q"], dd["k"], dd["v"], dd["log_alpha"], dd["beta"], S)
+    cu = torch.arange(B + 1, dtype=torch.int32, device="cuda")
+    oc, hc = kda.kda_chunk_fwd(dd["q"], dd["k"], dd["v"], dd["log_alpha"], dd["beta"],
+                               h0=dd["S"], cu_seqlens=cu)
+    torch.cuda.synchronize()
+    check("o", np_(od), np_(oc), TOL[dtype])
+    check("S", np_(S), np_(hc), TOL[dtype])
+
+
+def test_decode_repeated_steps_track_oracle():
+    """Eight decode steps in a row stay on the oracle's trajectory (fp32)."""
+    kda = need_gpu()
+    import oracle
+    case("decode 8 consecutive steps fp32 B=3 H=4")
+    B, H = 3, 4
+    S = kda_inputs.decode_inputs(B, H, dtype="f32", device="cuda", seed=10, state_std=0.5)["S"]
+    Sref = np_(S).astype(np.float64)
+    for step in range(8):
+        dd = kda_inputs.decode_inputs(B, H, dtype="f32", device="cuda", seed=100 + step,
+                                      decay_mu=-3.0)
+        o = kda.kda_decode_step(dd["q"], dd["k"], dd["v"], dd["log_alpha"], dd["beta"], S)
+        ro, Sref = oracle.decode(np_(dd["q"]), np_(dd["k"]), np_(dd["v"]),
+                                 np_(dd["log_alpha"]), np_(dd["beta"]), Sref)
+        torch.cuda.synchronize()
+        check(f"o step {step}", np_(o), ro, TOL["f32"])
+    check("S", np_(S), Sref, TOL["f32"])

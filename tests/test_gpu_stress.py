@@ -1,0 +1,109 @@
+"""Stress variants the workloads alone under-test: with the workloads'
+decay (mean log alpha about -2.5) the state forgets within a few tokens, so
+a kernel that mishandles the carried state can still pass them.  These
+cases use slow decay (log alpha = -5 sigmoid(N(mu, 1)), mu = -4 or -8),
+no decay at all, beta at its endpoints, one-hot keys and random h0, at fp32
+and the 1e-4 bar."""
+import numpy as np
+import pytest
+import torch
+
+import kda_inputs
+from gpu_util import TOL, case, check, gpu_prefill, need_gpu, np_, oracle_prefill
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("mu", [-4.0, -8.0])
+@pytest.mark.parametrize("chunk", [16, 32])
+def test_slow_decay_fp32(mu, chunk):
+    kda = need_gpu()
+    case(f"slow decay mu={mu} chunk={chunk} fp32 T=2000 H=3 random h0")
+    d = kda_inputs.prefill_inputs(2000, 3, dtype="f32", device="cuda", seed=20,
+                                  decay_mu=mu, h0_std=0.5)
+    o, hT = gpu_prefill(kda, d, chunk)
+    ro, rh = oracle_prefill(d)
+    check("o", np_(o), ro, TOL["f32"])
+    check("h_T", np_(hT), rh, TOL["f32"])
+
+
+@pytest.mark.parametrize("chunk", [16, 32])
+def test_no_decay_delta_rule_fp32(chunk):
+    """log alpha = 0: the plain delta rule, state never decays."""
+    kda = need_gpu()
+    case(f"log_alpha = 0 chunk={chunk} fp32 T=1500 H=2 random h0")
+    d = kda_inputs.prefill_inputs(1500, 2, dtype="f32", device="cuda", seed=21,
+                                  zero_decay=True, h0_std=0.5)
+    o, hT = gpu_prefill(kda, d, chunk)
+    ro, rh = oracle_prefill(d)
+    check("o", np_(o), ro, TOL["f32"])
+    check("h_T", np_(hT), rh, TOL["f32"])
+
+
+@pytest.mark.parametrize("beta", [0.0, 1.0])
+def test_beta_endpoints_fp32(beta):
+    kda = need_gpu()
+    case(f"beta = {beta} fp32 T=300 H=2 slow decay")
+    d = kda_inputs.prefill_inputs(300, 2, dtype="f32", device="cuda", seed=22,
+                                  decay_mu=-4.0, beta_const=beta, h0_std=0.5)
+    o, hT = gpu_prefill(kda, d)
+    ro, rh = oracle_prefill(d)
+    check("o", np_(o), ro, TOL["f32"])
+    check("h_T", np_(hT), rh, TOL["f32"])
+
+
+def test_decay_at_bound_fp32():
+    """log alpha = -5 everywhere (the bound): the 16-token tile factors reach
+    e^80 and must stay finite and exact."""
+    kda = need_gpu()
+    case("log_alpha = -5 everywhere fp32 T=200 H=2")
+    d = kda_inputs.prefill_inputs(200, 2, dtype="f32", device="cuda", seed=23, h0_std=0.5)
+    d["log_alpha"].fill_(-5.0)
+    for c in (16, 32):
+        o, hT = gpu_prefill(kda, d, c)
+        ro, rh = oracle_prefill(d)
+        check(f"o chunk={c}", np_(o), ro, TOL["f32"])
+        check(f"h_T chunk={c}", np_(hT), rh, TOL["f32"])
+
+
+def test_one_hot_keys_fp32():
+    kda = need_gpu()
+    case("one-hot keys fp32 T=400 H=2 slow decay")
+    T, H = 400, 2
+    d = kda_inputs.prefill_inputs(T, H, dtype="f32", device="cuda", seed=24,
+                                  decay_mu=-4.0, h0_std=0.5)
+    g = torch.Generator(device="cuda").manual_seed(24)
+    idx = torch.randint(0, 128, (T, H), device="cuda", generator=g)
+    k = torch.zeros_like(d["k"])
+    k.scatter_(2, idx[..., None], 1.0)
+    d["k"] = k
+    o, hT = gpu_prefill(kda, d)
+    ro, rh = oracle_prefill(d)
+    check("o", np_(o), ro, TOL["f32"])
+    check("h_T", np_(hT), rh, TOL["f32"])
+
+
+def test_slow_decay_bf16():
+    """bf16 inputs with slow decay: rounding of the bf16 MFMA operands must
+    not accumulate over a long memory."""
+    kda = need_gpu()
+    case("slow decay mu=-4 bf16 T=4096 H=4 random h0")
+    d = kda_inputs.prefill_inputs(4096, 4, dtype="bf16", device="cuda", seed=25,
+                                  decay_mu=-4.0, h0_std=0.02)
+    o, hT = gpu_prefill(kda, d)
+    ro, rh = oracle_prefill(d)
+    check("o", np_(o), ro, TOL["bf16"])
+    check("h_T", np_(hT), rh, TOL["bf16"])
+
+
+def test_long_slow_decay_fp32_sampled():
+    """A long sequence (T = 65536) with slow decay at fp32: error must not
+    grow along the chain.  Heads 0 and 1 of 2 checked in full."""
+    kda = need_gpu()
+    case("long slow decay mu=-8 fp32 T=65536 H=2")
+    d = kda_inputs.prefill_inputs(65536, 2, dtype="f32", device="cuda", seed=26,
+                                  decay_mu=-8.0, h0_std=0.5)
+    o, hT = gpu_prefill(kda, d)
+    ro, rh = oracle_prefill(d)
+    check("o", np_(o), ro, TOL["f32"])
+    check("h_T", np_(hT), rh, TOL["f32"])
