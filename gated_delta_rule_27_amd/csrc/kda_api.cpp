@@ -58,7 +58,7 @@ const char* kda_status_str(kda_status s) {
         case KDA_ERR_NULL_ARG: return "KDA_ERR_NULL_ARG: a required pointer is NULL";
         case KDA_ERR_BAD_SHAPE: return "KDA_ERR_BAD_SHAPE: unsupported size or option";
         case KDA_ERR_BAD_DTYPE: return "KDA_ERR_BAD_DTYPE: dtype is not KDA_F32 or KDA_BF16";
-        case KDA_ERR_MISALIGNED: return "KDA_ERR_MISALIGNED: a pointer is not 16-byte aligned";
+        case KDA_ERR_MISALIGNED: return "KDA_ERR_MISALIGNED: a pointer is not suitably aligned";
         case KDA_ERR_ALIAS: return "KDA_ERR_ALIAS: an output overlaps an input or another output";
         case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace too small";
         case KDA_ERR_DEVICE: return "KDA_ERR_DEVICE: a HIP call or kernel launch failed";
@@ -96,9 +96,11 @@ kda_status kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const v
 
     if (T_total > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERR_NULL_ARG;
 
-    for (const void* p : {q, k, v, log_alpha, beta, (const void*)h0, (const void*)o,
+    for (const void* p : {q, k, v, log_alpha, (const void*)h0, (const void*)o,
                           (const void*)h_T, (const void*)workspace})
         if (p && !aligned(p, 16)) return KDA_ERR_MISALIGNED;
+    // beta rows are H elements, so a token offset keeps only element alignment
+    if (beta && !aligned(beta, esize(dt))) return KDA_ERR_MISALIGNED;
     if (cu_seqlens && !aligned(cu_seqlens, 4)) return KDA_ERR_MISALIGNED;
 
     const uint64_t es = esize(dt);
@@ -156,8 +158,9 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const vo
     if ((uint64_t)B * (uint64_t)H > (uint64_t)std::numeric_limits<int32_t>::max())
         return KDA_ERR_BAD_SHAPE;
     if (B > 0 && (!q || !k || !v || !log_alpha || !beta || !S || !o)) return KDA_ERR_NULL_ARG;
-    for (const void* p : {q, k, v, log_alpha, beta, (const void*)S, (const void*)o})
+    for (const void* p : {q, k, v, log_alpha, (const void*)S, (const void*)o})
         if (p && !aligned(p, 16)) return KDA_ERR_MISALIGNED;
+    if (beta && !aligned(beta, esize(dt))) return KDA_ERR_MISALIGNED;
 
     const uint64_t es = esize(dt);
     const uint64_t nVec = (uint64_t)B * H * kda::kHeadDim;

@@ -522,13 +522,9 @@ hipError_t launch(const ChunkArgs& a, hipStream_t stream) {
     typedef ChunkCfg<TIn, C, NW, NCT> K;
     const int split = kHeadDim / K::DV;
     auto kern = chunk_kernel<TIn, C, NW, NCT>;
-    static bool attr_set = false;  // per instantiation; the value is device-independent
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)K::bytes);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)K::bytes);
+    if (e != hipSuccess) return e;
     const int64_t nwg = (int64_t)a.N * a.H * split;
     if (nwg == 0) return hipSuccess;
     kern<<<dim3((unsigned)nwg), dim3(K::NT), K::bytes, stream>>>(
@@ -558,9 +554,14 @@ bool chunk_config_supported(int dtype, int chunk, int split) {
 void chunk_default_config(int dtype, int64_t T_total, int32_t N, int32_t H, int* chunk,
                           int* split) {
     (void)T_total;
-    *chunk = dtype == 0 ? 16 : 32;
     const int64_t chains = (int64_t)N * H;
-    *split = chains >= 512 ? 1 : (chains >= 256 ? 2 : 4);
+    if (dtype == 0) {
+        *chunk = 16;
+        *split = chains >= 512 ? 1 : (chains >= 256 ? 2 : 4);
+    } else {
+        *chunk = 16;
+        *split = chains >= 256 ? 1 : 2;
+    }
 }
 
 hipError_t launch_chunk(const ChunkArgs& a, int dtype, int chunk, int split,
@@ -569,6 +570,7 @@ hipError_t launch_chunk(const ChunkArgs& a, int dtype, int chunk, int split,
         return chunk == 16 ? launch_split<float, 16>(a, split, stream)
                            : launch_split<float, 32>(a, split, stream);
     }
+    if (chunk == 16 && split <= 2) return launch_chunk_ws(a, split, stream);
     return chunk == 16 ? launch_split<bf16, 16>(a, split, stream)
                        : launch_split<bf16, 32>(a, split, stream);
 }

@@ -89,6 +89,41 @@ __device__ __forceinline__ bf16x4 acc_frag_k16(floatx4 t) {
     return bf16x4{(bf16)t[0], (bf16)t[1], (bf16)t[2], (bf16)t[3]};
 }
 
+// ---- DPP lane shifts within a row of 16 lanes --------------------------------
+// row_shr:n (lane r reads lane r - n of its row) and row_shl:n (lane r reads
+// lane r + n); lanes whose source falls outside the row keep `fill`.
+template <int N>
+__device__ __forceinline__ float row_shr(float src, float fill) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, fill),
+                                           __builtin_bit_cast(int, src), 0x110 + N, 0xF, 0xF,
+                                           false));
+}
+template <int N>
+__device__ __forceinline__ float row_shl(float src, float fill) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, fill),
+                                           __builtin_bit_cast(int, src), 0x100 + N, 0xF, 0xF,
+                                           false));
+}
+
+// Inclusive prefix product over the 16 lanes of a row (lane r: x_0 ... x_r).
+__device__ __forceinline__ float row_prefix_prod(float x) {
+    x *= row_shr<1>(x, 1.f);
+    x *= row_shr<2>(x, 1.f);
+    x *= row_shr<4>(x, 1.f);
+    x *= row_shr<8>(x, 1.f);
+    return x;
+}
+// Inclusive suffix product over the 16 lanes of a row (lane r: x_r ... x_15).
+__device__ __forceinline__ float row_suffix_prod(float x) {
+    x *= row_shl<1>(x, 1.f);
+    x *= row_shl<2>(x, 1.f);
+    x *= row_shl<4>(x, 1.f);
+    x *= row_shl<8>(x, 1.f);
+    return x;
+}
+
 // ---- wavefront reductions ---------------------------------------------------
 
 __device__ __forceinline__ float wave_sum(float x) {

@@ -39,7 +39,11 @@ struct DecodeArgs {
 
 // dtype: 0 = fp32, 1 = bf16 (kda_dtype values).
 // chunk in {16, 32}; split = workgroups per head (value-column slices).
+// bf16 with chunk 16 and split 1 or 2 runs the wave-specialised pipelined
+// kernel (kda_chunk_ws.hip); every other combination runs the phase-serial
+// kernel (kda_chunk.hip).
 bool chunk_config_supported(int dtype, int chunk, int split);
+hipError_t launch_chunk_ws(const ChunkArgs& a, int split, hipStream_t stream);
 void chunk_default_config(int dtype, int64_t T_total, int32_t N, int32_t H,
                           int* chunk, int* split);
 hipError_t launch_chunk(const ChunkArgs& a, int dtype, int chunk, int split,

@@ -23,7 +23,10 @@
  *
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers to contiguous row-major
- *     memory, 16-byte aligned.  The caller owns every buffer; the library
+ *     memory, 16-byte aligned, except beta (aligned to its element size,
+ *     since its rows are only H elements) and cu_seqlens (4-byte aligned).
+ *     Every [.., 128] row is 16-byte aligned when its base is, so slices at
+ *     any token offset stay valid.  The caller owns every buffer; the library
  *     never allocates or frees device memory and keeps no state between
  *     calls except a per-device property cache.
  *   - Work is enqueued on `stream` (NULL = the default stream); no call
@@ -61,7 +64,7 @@ typedef enum {
                                d_k or d_v != 128, N != 1 without cu_seqlens,
                                or an unsupported chunk / split override      */
     KDA_ERR_BAD_DTYPE = 3,  /* dtype is not a kda_dtype                      */
-    KDA_ERR_MISALIGNED = 4, /* a pointer is not 16-byte aligned              */
+    KDA_ERR_MISALIGNED = 4, /* a pointer breaks the alignment rules above    */
     KDA_ERR_ALIAS = 5,      /* an output overlaps an input or another output */
     KDA_ERR_WORKSPACE = 6,  /* workspace smaller than the size reported      */
     KDA_ERR_DEVICE = 7      /* a HIP call or kernel launch failed            */

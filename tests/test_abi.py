@@ -103,6 +103,8 @@ def decode(L, **kw):
     (dict(h0=P(5, 2)), MISALIGNED),
     (dict(hT=P(8, 12)), MISALIGNED),
     (dict(cu=P(6, 2)), MISALIGNED),
+    (dict(b=P(4, 1)), MISALIGNED),       # beta: element alignment only
+    (dict(b=P(4, 3), dt=F32), MISALIGNED),
     (dict(o=P(0, 64)), ALIAS),           # o inside q
     (dict(o=P(4)), ALIAS),               # o on beta
     (dict(hT=P(5)), ALIAS),              # h_T on h0: snapshots are read only
@@ -111,6 +113,13 @@ def decode(L, **kw):
 ])
 def test_chunk_argument_errors(L, kw, code):
     assert chunk(L, **kw) == code
+
+
+def test_beta_needs_only_element_alignment(L):
+    # a bf16 beta at an odd token offset is 2-byte aligned: accepted by the
+    # alignment check (the call then fails later on aliasing, before any launch)
+    assert chunk(L, b=P(4, 6), o=P(4)) == ALIAS
+    assert chunk(L, b=P(4, 4), dt=F32, o=P(4)) == ALIAS
 
 
 def test_chunk_error_precedence(L):

@@ -27,11 +27,16 @@ def test_chunk_and_split_invariance(dtype):
             check("o", np_(o), ro, TOL[dtype])
             check("h_T", np_(hT), rh, TOL[dtype])
             outs[(c, s)] = (np_(o), np_(hT))
-    # the column split changes no arithmetic: same chunk length, same bits
-    for c in (16, 32):
-        for s in (2, 4):
-            assert np.array_equal(outs[(c, s)][0], outs[(c, 1)][0])
-            assert np.array_equal(outs[(c, s)][1], outs[(c, 1)][1])
+    # within one kernel the column split changes no arithmetic: same bits.
+    # (bf16 with chunk 16 and split <= 2 runs the pipelined kernel, the other
+    # combinations the phase-serial one.)
+    same = [[(16, 1), (16, 2)], [(32, 1), (32, 2), (32, 4)]]
+    if dtype == "f32":
+        same = [[(16, 1), (16, 2), (16, 4)], [(32, 1), (32, 2), (32, 4)]]
+    for group in same:
+        for key in group[1:]:
+            assert np.array_equal(outs[key][0], outs[group[0]][0]), key
+            assert np.array_equal(outs[key][1], outs[group[0]][1]), key
 
 
 def test_deterministic_and_inputs_untouched():
