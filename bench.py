@@ -118,6 +118,9 @@ def main():
     ap.add_argument("--split", type=int, default=0, help="override the column split")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy three times, as the "
+                         "reference kernel for scaling HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
@@ -179,7 +182,7 @@ def main():
                    "dv_split": args.split or "auto"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "kda::chunk_kernel",
+                     "traffic": traffic, "kernel": "kda::chunk_ws_kernel",
                      "kernel_ms": round(avg_ms, 5), "algorithmic_bytes": nbytes},
         "mfma": {"flops_per_step": flops, "counted_at_chunk": 64,
                  "frac_of_bf16_peak": round(mfma_frac, 4)},
@@ -216,6 +219,15 @@ def main():
         }
         del dd
         torch.cuda.empty_cache()
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = {"read": src.numel() * 4, "write": dst.numel() * 4}
+        del src, dst
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(T, H)
