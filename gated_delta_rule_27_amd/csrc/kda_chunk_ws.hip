@@ -13,26 +13,27 @@
 //   T = (I + A)^{-1} diag(beta)
 //   U = T (V - Ktil S0),  O = Qtil S0 + P U,  S_C = Diag(Gamma) S0 + Kvec^T U.
 //
-// Why a second kernel.  Per chunk, the state-independent work (running decay
-// products, operand scaling, Gram tiles, the triangular solve) is a chain of
+// Why a second kernel.  Per chunk, the state-independent work (decay
+// factors, operand scaling, Gram tiles, the triangular solve) is a chain of
 // short dependent steps with little parallelism inside one chunk, while the
 // state update is a chain over chunks.  The pages' FlashKDA note describes
 // overlapping the token-parallel work with the head-parallel state
 // propagation ("From GPT-2 to Kimi K3", ch. 6 "Training, prefill, and decode
-// use different paths").  Here the overlap is inside one workgroup of eight
-// wavefronts, two per SIMD:
-//   waves 0-3 (state): own 16 * NCT value columns of the 128 x 128 state
-//     each, in MFMA accumulators for the whole sequence; run the state chain
-//     for chunk c;
-//   waves 4-7 (prep): stage raw inputs of chunk c+4 into LDS, build the
-//     decay-scaled operands of chunk c+3 (lane = token x 8 channels; the
-//     running decay products over the chunk are DPP scans across the 16
-//     lanes of a row), the Gram tiles of chunk c+2 (wave 4: A, wave 5: P)
-//     and the triangular solve of chunk c+1 (wave 6).
+// use different paths").  Here the overlap is inside one workgroup of twelve
+// wavefronts, three per SIMD:
+//   waves 0-3 (state): each owns 16 * NCT value columns of the 128 x 128
+//     state in MFMA accumulators for the whole sequence and runs the state
+//     chain of chunk c; its V values arrive by its own register prefetch;
+//   waves 4-11 (prep), lane = (token r, 4 key channels): load q, k, log_alpha
+//     of chunk c+3 straight into the lanes that use them (PD chunks ahead),
+//     take the cumulative log-decay over the chunk's 16 tokens as a DPP scan
+//     across the 16 lanes of a row and write the decay-scaled operands;
+//     prep waves 4 and 5 (of the eight) also form the Gram tiles of chunk c+2
+//     (A and P) and prep waves 0-3 the triangular solve of chunk c+1 (lane =
+//     one element of the 16 x 16 inverse).
 // Every stage reads only what an earlier iteration wrote, so one barrier per
-// chunk is the only synchronisation.  LDS holds two raw-input slots, four
-// operand slots and two A-tile slots (ring buffers indexed by chunk).  The
-// prep waves keep PD chunks of 16-byte input loads in flight in registers.
+// chunk is the only synchronisation.  LDS holds ring buffers indexed by
+// chunk, each as deep as its value lives (77 KB in all).
 //
 // Workgroup order is XCD-aware: the `split` workgroups that share one
 // (sequence, head) get ids with the same residue mod 8, i.e. the same XCD
@@ -48,55 +49,49 @@ namespace {
 
 constexpr int kWsC = 16;      // tokens per chunk
 constexpr int kXcds = 8;      // MI355X accelerator complex dies
+constexpr float kLog2e = 1.4426950408889634f;
+
+// 2^x on the transcendental unit (v_exp_f32); |x| stays far inside its range here
+__device__ __forceinline__ float exp2f_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <int NCT, int PD>
 struct WsCfg {
     static constexpr int NSW = 4;                // state waves
-    static constexpr int NT = 512;               // 4 state + 4 prep waves
+    static constexpr int NPW = 8;                // prep waves
+    static constexpr int NT = 64 * (NSW + NPW);  // 768 threads
     static constexpr int DV = 16 * NCT * NSW;    // value columns per workgroup
     static constexpr int KP = kHeadDim + 8;      // bf16 stride of [token][channel]
     static constexpr int TP = kWsC + 8;          // bf16 stride of [.][token]
-    static constexpr int VPR = DV + 8;           // bf16 stride of V rows
     static constexpr int AP = 20;                // fp32 stride of the A tile
-    static constexpr int VR = DV / 8;            // 16-byte vectors per V row
 
-    // raw-input slot
-    static constexpr size_t rQ = 0;
-    static constexpr size_t rK = rQ + kWsC * KP * 2;
-    static constexpr size_t rG = rK + kWsC * KP * 2;
-    static constexpr size_t rV = rG + kWsC * KP * 2;
-    static constexpr size_t rB = rV + kWsC * VPR * 2;
-    static constexpr size_t rawBytes = rB + 64;
-    // operand slot
-    static constexpr size_t oKn = 0;                          // -Ktil  [r][i]
-    static constexpr size_t oQs = oKn + kWsC * KP * 2;        //  Qtil  [r][i]
-    static constexpr size_t oKh = oQs + kWsC * KP * 2;        //  Khat  [s][i]
-    static constexpr size_t oKvT = oKh + kWsC * KP * 2;       //  Kvec^T [i][s]
-    static constexpr size_t oT = oKvT + kHeadDim * TP * 2;    //  T     [r][s]
-    static constexpr size_t oP = oT + kWsC * TP * 2;          //  P     [r][s]
-    static constexpr size_t oV = oP + kWsC * TP * 2;          //  V     [r][j]
-    static constexpr size_t oBeta = oV + kWsC * VPR * 2;      //  beta  fp32
-    static constexpr size_t oGam = oBeta + 64;                //  Gamma fp32
-    static constexpr size_t opsBytes = oGam + kHeadDim * 4;
-    static constexpr size_t aBytes = kWsC * AP * 4;
-
-    static constexpr size_t RAW0 = 0;
-    static constexpr size_t OPS0 = 2 * rawBytes;
-    static constexpr size_t SA0 = OPS0 + 4 * opsBytes;
-    static constexpr size_t bytes = SA0 + 2 * aBytes;
+    static constexpr size_t szTok = kWsC * KP * 2;        // [16][128] bf16
+    static constexpr size_t szKvT = kHeadDim * TP * 2;    // [128][16] bf16
+    static constexpr size_t szTile = kWsC * TP * 2;       // [16][16] bf16
+    static constexpr size_t szA = kWsC * AP * 4;          // [16][16] fp32
+    // ring buffers; chunk y's operands are written by the prep stage three
+    // iterations before the state stage reads them
+    static constexpr size_t KN0 = 0;                        // -Ktil, 4 slots
+    static constexpr size_t QS0 = KN0 + 4 * szTok;          //  Qtil, 4 slots
+    static constexpr size_t KVT0 = QS0 + 4 * szTok;         //  Kvec^T, 4 slots
+    static constexpr size_t GAM0 = KVT0 + 4 * szKvT;        //  Gamma, 4 slots
+    static constexpr size_t KH0 = GAM0 + 4 * 512;           //  Khat, 2 slots
+    static constexpr size_t BETA0 = KH0 + 2 * szTok;        //  beta, 3 slots
+    static constexpr size_t A0 = BETA0 + 3 * 64;            //  A, 2 slots
+    static constexpr size_t P0 = A0 + 2 * szA;              //  P, 3 slots
+    static constexpr size_t T0 = P0 + 3 * szTile;           //  T, 2 slots
+    static constexpr size_t bytes = T0 + 2 * szTile;
 
     static_assert(bytes <= 160 * 1024, "LDS budget");
-    static_assert(rawBytes % 16 == 0 && opsBytes % 16 == 0, "slot alignment");
 };
 
 template <int NCT, int PD>
-__global__ __launch_bounds__(512) void chunk_ws_kernel(
+__global__ __launch_bounds__(768) void chunk_ws_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ log_alpha, const bf16* __restrict__ beta,
     const float* __restrict__ h0, const int32_t* __restrict__ cu_seqlens, int64_t T_total,
     int32_t H, int32_t split, int32_t units, bf16* __restrict__ o, float* __restrict__ h_T) {
     typedef WsCfg<NCT, PD> K;
-    constexpr int KP = K::KP, TP = K::TP, VPR = K::VPR, AP = K::AP, DV = K::DV, VR = K::VR;
+    constexpr int KP = K::KP, TP = K::TP, AP = K::AP, DV = K::DV;
 
     // XCD-aware id: slices of one unit share the id's residue mod 8
     const int x = blockIdx.x;
@@ -109,58 +104,112 @@ __global__ __launch_bounds__(512) void chunk_ws_kernel(
     const int h = unit % H;
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    auto kn_s = [&](int y) { return reinterpret_cast<bf16*>(smem + K::KN0 + (y & 3) * K::szTok); };
+    auto qs_s = [&](int y) { return reinterpret_cast<bf16*>(smem + K::QS0 + (y & 3) * K::szTok); };
+    auto kvt_s = [&](int y) { return reinterpret_cast<bf16*>(smem + K::KVT0 + (y & 3) * K::szKvT); };
+    auto gam_s = [&](int y) { return reinterpret_cast<float*>(smem + K::GAM0 + (y & 3) * 512); };
+    auto kh_s = [&](int y) { return reinterpret_cast<bf16*>(smem + K::KH0 + (y & 1) * K::szTok); };
+    auto beta_s = [&](int y) { return reinterpret_cast<float*>(smem + K::BETA0 + (y % 3) * 64); };
+    auto a_s = [&](int y) { return reinterpret_cast<float*>(smem + K::A0 + (y & 1) * K::szA); };
+    auto p_s = [&](int y) { return reinterpret_cast<bf16*>(smem + K::P0 + (y % 3) * K::szTile); };
+    auto t_s = [&](int y) { return reinterpret_cast<bf16*>(smem + K::T0 + (y & 1) * K::szTile); };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    // wave index as a scalar: the role branch below is wave-uniform
+    // wave index as a scalar: the role branches below are wave-uniform
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15;
     const int g = lane >> 4;
 
     const int64_t bos = cu_seqlens ? (int64_t)cu_seqlens[n] : 0;
     const int64_t eos = cu_seqlens ? (int64_t)cu_seqlens[n + 1] : T_total;
-    const int nch = (int)((eos - bos + kWsC - 1) / kWsC);
-    // pipeline iterations c = -4 .. nit-5: stage s of iteration c handles chunk c + s
-    const int nit = (nch + 4 + PD - 1) / PD * PD;
+    const int64_t seqlen = eos - bos;
+    const int nch = (int)((seqlen + kWsC - 1) / kWsC);
     const size_t rowstride = (size_t)H * kHeadDim;
     const size_t headoff = (size_t)h * kHeadDim;
+    const size_t cstride = (size_t)kWsC * rowstride;  // elements per chunk of tokens
     const int col0 = slice * DV;
-
-    auto raw = [&](int slot) { return smem + K::RAW0 + (size_t)slot * K::rawBytes; };
-    auto ops = [&](int slot) { return smem + K::OPS0 + (size_t)slot * K::opsBytes; };
-    auto satile = [&](int slot) {
-        return reinterpret_cast<float*>(smem + K::SA0 + (size_t)slot * K::aBytes);
+    // pipeline iterations c = -3 .. nit-4: the prep stage of iteration c
+    // handles chunk c+3, the Gram stage c+2, the solve c+1, the state c
+    const int nit = (nch + 3 + PD - 1) / PD * PD;
+    auto chunk_len = [&](int yc) {
+        const int64_t rem = seqlen - (int64_t)kWsC * yc;
+        return (int)(rem < 0 ? 0 : (rem < kWsC ? rem : kWsC));
     };
+
+    // An empty sequence has no chunks: only h_T = h0 is written, and no
+    // input pointer is touched (they may be null when T_total is 0).  The
+    // branch is uniform over the workgroup, so no barrier is skipped.
+    if (nch == 0) {
+        if (wave < K::NSW && h_T) {
+            const float* src = h0 ? h0 + ((size_t)n * (size_t)H + h) * (kHeadDim * kHeadDim) : nullptr;
+            float* dst = h_T + ((size_t)n * (size_t)H + h) * (kHeadDim * kHeadDim);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                const int j = col0 + 16 * (NCT * wave + ct) + l16;
+#pragma unroll
+                for (int it = 0; it < 8; ++it)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int idx = (16 * it + 4 * g + e) * kHeadDim + j;
+                        dst[idx] = src ? src[idx] : 0.f;
+                    }
+            }
+        }
+        return;
+    }
 
     if (wave < K::NSW) {
         // ======================= state waves =======================
-        // the 128 x (16 * NCT) state slice of this wave, in accumulators
         floatx4 S[NCT][8];
-        const float* src = h0 ? h0 + ((size_t)n * (size_t)H + h) * (kHeadDim * kHeadDim) : nullptr;
+        {
+            const float* src = h0 ? h0 + ((size_t)n * (size_t)H + h) * (kHeadDim * kHeadDim) : nullptr;
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            const int j = col0 + 16 * (NCT * wave + ct) + l16;
+            for (int ct = 0; ct < NCT; ++ct) {
+                const int j = col0 + 16 * (NCT * wave + ct) + l16;
 #pragma unroll
-            for (int it = 0; it < 8; ++it)
+                for (int it = 0; it < 8; ++it)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    S[ct][it][e] = src ? src[(16 * it + 4 * g + e) * kHeadDim + j] : 0.f;
+                    for (int e = 0; e < 4; ++e)
+                        S[ct][it][e] = src ? src[(16 * it + 4 * g + e) * kHeadDim + j] : 0.f;
+            }
         }
-        for (int c = -4; c < nit - 4; ++c) {
+        // V of a chunk: rows 4g..4g+3 of this lane's columns, two chunks in
+        // flight (clamped addresses past the end: those rows never reach an
+        // output, since their beta is zero)
+        bf16 vr[2][NCT][4];
+        auto load_v = [&](auto slot_c, int yc) {
+            constexpr int sv = decltype(slot_c)::value;
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                const int j = col0 + 16 * (NCT * wave + ct) + l16;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    // yc is -1 in the first pipeline iteration: rows before the
+                    // sequence start are clamped like rows past its end
+                    const int64_t r = (int64_t)kWsC * yc + 4 * g + e;
+                    const size_t off =
+                        (r >= 0 && r < seqlen) ? (size_t)(bos + r) * rowstride + headoff + j : 0;
+                    vr[sv][ct][e] = v[off];
+                }
+            }
+        };
+        load_v(std::integral_constant<int, 0>{}, 0);
+        load_v(std::integral_constant<int, 1>{}, 1);
+
+        auto state_iter = [&](auto slot_c, int c) {
+            constexpr int sv = decltype(slot_c)::value;  // == c & 1
             if (c >= 0 && c < nch) {
-                const unsigned char* O = ops(c & 3);
-                const bf16* Kn = reinterpret_cast<const bf16*>(O + K::oKn) + l16 * KP;
-                const bf16* Qs = reinterpret_cast<const bf16*>(O + K::oQs) + l16 * KP;
-                const bf16* Vv = reinterpret_cast<const bf16*>(O + K::oV);
-                const float* Gm = reinterpret_cast<const float*>(O + K::oGam);
+                const bf16* Kn = kn_s(c) + l16 * KP;
+                const bf16* Qs = qs_s(c) + l16 * KP;
+                const float* Gm = gam_s(c);
                 const int64_t t0 = bos + (int64_t)kWsC * c;
-                const int len = (int)((eos - t0) < kWsC ? (eos - t0) : kWsC);
+                const int len = chunk_len(c);
                 floatx4 X[NCT], Ov[NCT], U[NCT];
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) {
-                    const int jl = 16 * (NCT * wave + ct) + l16;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) X[ct][e] = (float)Vv[(4 * g + e) * VPR + jl];
+                    for (int e = 0; e < 4; ++e) X[ct][e] = (float)vr[sv][ct][e];
                     Ov[ct] = zero4();
                 }
                 // X = V - Ktil S, O = Qtil S
@@ -176,10 +225,8 @@ __global__ __launch_bounds__(512) void chunk_ws_kernel(
                     }
                 }
                 // U = T X, O += P U
-                const bf16x4 at =
-                    frag_k16(reinterpret_cast<const bf16*>(O + K::oT) + l16 * TP, 0, g);
-                const bf16x4 ap =
-                    frag_k16(reinterpret_cast<const bf16*>(O + K::oP) + l16 * TP, 0, g);
+                const bf16x4 at = frag_k16(t_s(c) + l16 * TP, 0, g);
+                const bf16x4 ap = frag_k16(p_s(c) + l16 * TP, 0, g);
                 bf16x4 ub[NCT];
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) {
@@ -198,7 +245,7 @@ __global__ __launch_bounds__(512) void chunk_ws_kernel(
                     }
                 }
                 // S <- Diag(Gamma) S + Kvec^T U
-                const bf16* KvT = reinterpret_cast<const bf16*>(O + K::oKvT);
+                const bf16* KvT = kvt_s(c);
 #pragma unroll
                 for (int it = 0; it < 8; ++it) {
                     const floatx4 gm = *reinterpret_cast<const floatx4*>(Gm + 16 * it + 4 * g);
@@ -208,7 +255,15 @@ __global__ __launch_bounds__(512) void chunk_ws_kernel(
                         S[ct][it] = mma_bf16_k16(a, ub[ct], S[ct][it] * gm);
                 }
             }
+            // refill this V slot with chunk c+2, unconditionally, so the memory
+            // counter stays exact
+            load_v(slot_c, c + 2);
             __syncthreads();
+        };
+        for (int c = -3; c < nit - 3; c += 2) {
+            // -3 is odd: keep the V slot equal to c & 1
+            state_iter(std::integral_constant<int, 1>{}, c);
+            state_iter(std::integral_constant<int, 0>{}, c + 1);
         }
         if (h_T) {
             float* dst = h_T + ((size_t)n * (size_t)H + h) * (kHeadDim * kHeadDim);
@@ -226,168 +281,148 @@ __global__ __launch_bounds__(512) void chunk_ws_kernel(
     }
 
     // ========================= prep waves =========================
-    const int pt = tid - K::NSW * 64;  // 0..255
-    // register slots of in-flight input loads: chunk x lives in slot x % PD
-    bf16x8 rq[PD], rk[PD], rg[PD], rv[PD];
+    const int pw = wave - K::NSW;   // 0..7
+    const int r = l16;              // token of the chunk
+    const int ch0 = 16 * pw + 4 * g;  // first of this lane's 4 key channels
+    // register slots of in-flight loads: chunk y lives in slot y % PD.  All
+    // lanes issue the same loads for every chunk, from clamped (valid)
+    // addresses, so the memory counter stays exact; rows past the end of the
+    // sequence are zeroed when used.
+    bf16x4 rq[PD], rk[PD], rg[PD];
     bf16 rb[PD];
-    auto load_chunk = [&](auto slot_c, int xc) {
+    const size_t oq0 = (size_t)(bos + r) * rowstride + headoff + ch0;
+    const size_t ob0 = (size_t)(bos + r) * H + h;
+    auto load_chunk = [&](auto slot_c, int yc) {
         constexpr int s = decltype(slot_c)::value;
-        const int64_t t0 = bos + (int64_t)kWsC * xc;
-        const int len = (int)((eos - t0) < kWsC ? (eos - t0) : kWsC);
-        const int r = pt >> 4, cv = pt & 15;
-        const bf16x8 z = {};
-        const size_t off = (size_t)(t0 + r) * rowstride + headoff + 8 * cv;
-        const bool ok = r < len;
-        rq[s] = ok ? *reinterpret_cast<const bf16x8*>(q + off) : z;
-        rk[s] = ok ? *reinterpret_cast<const bf16x8*>(k + off) : z;
-        rg[s] = ok ? *reinterpret_cast<const bf16x8*>(log_alpha + off) : z;
-        rv[s] = z;
-        if (pt < kWsC * VR) {
-            const int rr = pt / VR, vc = pt % VR;
-            if (rr < len)
-                rv[s] = *reinterpret_cast<const bf16x8*>(
-                    v + (size_t)(t0 + rr) * rowstride + headoff + col0 + 8 * vc);
-        }
-        rb[s] = (pt < len) ? beta[(size_t)(t0 + pt) * H + h] : (bf16)0.f;
+        const int64_t row = (int64_t)kWsC * yc + r;
+        const bool ok = row >= 0 && row < seqlen;
+        const size_t oq = ok ? oq0 + (size_t)yc * cstride : 0;
+        const size_t ob = ok ? ob0 + (size_t)yc * kWsC * H : 0;
+        rq[s] = *reinterpret_cast<const bf16x4*>(q + oq);
+        rk[s] = *reinterpret_cast<const bf16x4*>(k + oq);
+        rg[s] = *reinterpret_cast<const bf16x4*>(log_alpha + oq);
+        rb[s] = beta[ob];
     };
-    if (0 < nch) load_chunk(std::integral_constant<int, 0>{}, 0);
-    if constexpr (PD > 1) if (1 < nch) load_chunk(std::integral_constant<int, 1 % PD>{}, 1);
-    if constexpr (PD > 2) if (2 < nch) load_chunk(std::integral_constant<int, 2 % PD>{}, 2);
-    if constexpr (PD > 3) if (3 < nch) load_chunk(std::integral_constant<int, 3 % PD>{}, 3);
+    load_chunk(std::integral_constant<int, 0>{}, 0);
+    if constexpr (PD > 1) load_chunk(std::integral_constant<int, 1 % PD>{}, 1);
+    if constexpr (PD > 2) load_chunk(std::integral_constant<int, 2 % PD>{}, 2);
+    if constexpr (PD > 3) load_chunk(std::integral_constant<int, 3 % PD>{}, 3);
 
-    auto iter = [&](auto slot_c, int c) {
-        constexpr int s = decltype(slot_c)::value;
-        // (1) raw inputs of chunk c+4 -> LDS, then refill this register slot
-        const int xc = c + 4;
-        if (xc < nch) {
-            unsigned char* R = raw(xc & 1);
-            const int r = pt >> 4, cv = pt & 15;
-            *reinterpret_cast<bf16x8*>(R + K::rQ + (r * KP + 8 * cv) * 2) = rq[s];
-            *reinterpret_cast<bf16x8*>(R + K::rK + (r * KP + 8 * cv) * 2) = rk[s];
-            *reinterpret_cast<bf16x8*>(R + K::rG + (r * KP + 8 * cv) * 2) = rg[s];
-            if (pt < kWsC * VR) {
-                const int rr = pt / VR, vc = pt % VR;
-                *reinterpret_cast<bf16x8*>(R + K::rV + (rr * VPR + 8 * vc) * 2) = rv[s];
-            }
-            if (pt < kWsC) reinterpret_cast<bf16*>(R + K::rB)[pt] = rb[s];
-            if (xc + PD < nch) load_chunk(slot_c, xc + PD);
-        }
-        // (2) decay products and scaled operands of chunk c+3.  Lane =
-        // (token r = lane % 16, channel octet): the running products over
-        // the chunk's 16 tokens are DPP scans across the lanes of a row.
+    auto prep_iter = [&](auto slot_c, int c) {
+        constexpr int s = decltype(slot_c)::value;  // == (c + 3) % PD
+        // (1) decay factors and scaled operands of chunk c+3
         const int yc = c + 3;
-        if (yc >= 0 && yc < nch) {
-            const unsigned char* R = raw(yc & 1);
-            unsigned char* O = ops(yc & 3);
-            const int r = l16;
-            const int i0 = 8 * (4 * (wave - K::NSW) + g);  // first channel of the octet
-            const bf16x8 gq = *reinterpret_cast<const bf16x8*>(R + K::rQ + (r * KP + i0) * 2);
-            const bf16x8 gk = *reinterpret_cast<const bf16x8*>(R + K::rK + (r * KP + i0) * 2);
-            const bf16x8 gg = *reinterpret_cast<const bf16x8*>(R + K::rG + (r * KP + i0) * 2);
-            bf16x8 kn, qs, kh;
-            float gam[8];
+        if (yc < nch) {
+            const int len = chunk_len(yc);
+            float kf[4], qf[4], lg[4];
+            float bt = (float)rb[s];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float al = __expf((float)gg[e]);
-                const float E = row_prefix_prod(al);                     // exp(G_r)
-                const float Hs = row_shl<1>(row_suffix_prod(al), 1.f);  // exp(G_C - G_r)
-                gam[e] = E * Hs;                                          // exp(G_C)
-                const float kr = (float)gk[e], qr = (float)gq[e];
-                const float kH = kr * Hs;
-                kn[e] = (bf16)(-kr * E);
-                qs[e] = (bf16)(qr * E);
-                kh[e] = (bf16)(kH * (1.f / fmaxf(gam[e], 1.17549435e-38f)));
-                reinterpret_cast<bf16*>(O + K::oKvT)[(i0 + e) * TP + r] = (bf16)kH;
+            for (int e = 0; e < 4; ++e) {
+                kf[e] = (float)rk[s][e];
+                qf[e] = (float)rq[s][e];
+                lg[e] = (float)rg[s][e] * kLog2e;
             }
-            *reinterpret_cast<bf16x8*>(O + K::oKn + (r * KP + i0) * 2) = kn;
-            *reinterpret_cast<bf16x8*>(O + K::oQs + (r * KP + i0) * 2) = qs;
-            *reinterpret_cast<bf16x8*>(O + K::oKh + (r * KP + i0) * 2) = kh;
-            if (r == 0) {
-                float* G = reinterpret_cast<float*>(O + K::oGam) + i0;
-                *reinterpret_cast<floatx4*>(G) = floatx4{gam[0], gam[1], gam[2], gam[3]};
-                *reinterpret_cast<floatx4*>(G + 4) = floatx4{gam[4], gam[5], gam[6], gam[7]};
+            if (len < kWsC && r >= len) {  // rows past the end: no decay, no write
+#pragma unroll
+                for (int e = 0; e < 4; ++e) kf[e] = qf[e] = lg[e] = 0.f;
+                bt = 0.f;
             }
-            if (pt < kWsC * VR) {
-                const int rr = pt / VR, vc = pt % VR;
-                *reinterpret_cast<bf16x8*>(O + K::oV + (rr * VPR + 8 * vc) * 2) =
-                    *reinterpret_cast<const bf16x8*>(R + K::rV + (rr * VPR + 8 * vc) * 2);
+            bf16x4 kn, qs, kh;
+            floatx4 gam;
+            bf16* KvT = kvt_s(yc);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float P = row_prefix_sum(lg[e]);        // G_r / ln 2
+                const float Sx = row_suffix_sum_excl(lg[e]);  // (G_C - G_r) / ln 2
+                const float E = exp2f_fast(P);                // exp(G_r)       <= 1
+                const float Einv = exp2f_fast(-P);            // exp(-G_r)      <= e^80
+                const float Hs = exp2f_fast(Sx);              // exp(G_C - G_r) <= 1
+                gam[e] = E * Hs;                              // exp(G_C)
+                kn[e] = (bf16)(-kf[e] * E);
+                qs[e] = (bf16)(qf[e] * E);
+                kh[e] = (bf16)(kf[e] * Einv);
+                KvT[(ch0 + e) * TP + r] = (bf16)(kf[e] * Hs);
             }
-            if (pt < kWsC)
-                reinterpret_cast<float*>(O + K::oBeta)[pt] =
-                    (float)reinterpret_cast<const bf16*>(R + K::rB)[pt];
+            *reinterpret_cast<bf16x4*>(kn_s(yc) + r * KP + ch0) = kn;
+            *reinterpret_cast<bf16x4*>(qs_s(yc) + r * KP + ch0) = qs;
+            *reinterpret_cast<bf16x4*>(kh_s(yc) + r * KP + ch0) = kh;
+            if (r == 0) *reinterpret_cast<floatx4*>(gam_s(yc) + ch0) = gam;
+            if (pw == 0 && g == 0) beta_s(yc)[r] = bt;
         }
-        // (3) Gram tiles of chunk c+2 (transposed products: acc(s, r))
+        load_chunk(slot_c, yc + PD);
+        // (2) Gram tiles of chunk c+2 (transposed products: acc(s, r))
         const int zc = c + 2;
-        if (zc >= 0 && zc < nch && (wave == K::NSW || wave == K::NSW + 1)) {
-            unsigned char* O = ops(zc & 3);
-            const bf16* arow = reinterpret_cast<const bf16*>(O + K::oKh) + l16 * KP;
-            const bool isP = wave == K::NSW + 1;
-            const bf16* brow =
-                reinterpret_cast<const bf16*>(O + (isP ? K::oQs : K::oKn)) + l16 * KP;
+        if (zc >= 0 && zc < nch && (pw == 4 || pw == 5)) {
+            const bf16* arow = kh_s(zc) + l16 * KP;
+            const bool isP = pw == 5;
+            const bf16* brow = (isP ? qs_s(zc) : kn_s(zc)) + l16 * KP;
             floatx4 acc = zero4();
 #pragma unroll
             for (int kb = 0; kb < kHeadDim; kb += 32)
                 acc = mma_bf16_k32(frag_k32(arow, kb, g), frag_k32(brow, kb, g), acc);
             if (!isP) {
-                // A[r][s] = beta_r (Ktil_r . Khat_s), strictly lower (Kn = -Ktil);
-                // stored transposed, AT[s][r], for the column sweep of the solve
-                const float br = reinterpret_cast<const float*>(O + K::oBeta)[l16];
-                float* AT = satile(zc & 1);
+                // A[r][s] = beta_r (Ktil_r . Khat_s), strictly lower (Kn = -Ktil)
+                const float br = beta_s(zc)[l16];
+                floatx4 out;
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    AT[(4 * g + e) * AP + l16] = (4 * g + e >= l16) ? 0.f : -acc[e] * br;
+                for (int e = 0; e < 4; ++e) out[e] = (4 * g + e >= l16) ? 0.f : -acc[e] * br;
+                *reinterpret_cast<floatx4*>(a_s(zc) + l16 * AP + 4 * g) = out;
             } else {
                 bf16x4 out;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) out[e] = (bf16)((4 * g + e > l16) ? 0.f : acc[e]);
-                *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(O + K::oP) + l16 * TP +
-                                           4 * g) = out;
+                *reinterpret_cast<bf16x4*>(p_s(zc) + l16 * TP + 4 * g) = out;
             }
         }
-        // (4) UT transform of chunk c+1: column `lane` of (I + A)^{-1}, times
-        // beta_lane, by a sweep over the columns of A (next column prefetched)
+        // (3) UT transform of chunk c+1 on prep waves 0-3: lane = (row
+        // l16, column 4 * pw + g) of X = (I + A)^{-1}; forward elimination
+        // down the columns of A, the pivot X[sc][c] broadcast along the row
+        // of 16 lanes by DPP.
         const int wc = c + 1;
-        if (wc >= 0 && wc < nch && wave == K::NSW + 2 && lane < 16) {
-            const float* AT = satile(wc & 1);
-            unsigned char* O = ops(wc & 3);
-            float xr[16];
+        if (wc >= 0 && wc < nch && pw < 4) {
+            const float* Arow = a_s(wc) + l16 * AP;
+            float a[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) xr[r] = (r == lane) ? 1.f : 0.f;
-            floatx4 col[4], nxt[4];
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const floatx4 v4 = *reinterpret_cast<const floatx4*>(Arow + 4 * q4);
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) col[q4] = *reinterpret_cast<const floatx4*>(AT + 4 * q4);
-#pragma unroll
-            for (int sc = 0; sc < 15; ++sc) {
-                if (sc < 14) {
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4)
-                        nxt[q4] = *reinterpret_cast<const floatx4*>(AT + (sc + 1) * AP + 4 * q4);
-                }
-                const float xs = xr[sc];
-#pragma unroll
-                for (int r = sc + 1; r < 16; ++r) xr[r] -= col[r >> 2][r & 3] * xs;
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) col[q4] = nxt[q4];
+                for (int e = 0; e < 4; ++e) a[4 * q4 + e] = v4[e];
             }
-            const float bc = reinterpret_cast<const float*>(O + K::oBeta)[lane];
-            bf16* Tt = reinterpret_cast<bf16*>(O + K::oT);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) Tt[r * TP + lane] = (bf16)(xr[r] * bc);
+            const int col = 4 * pw + g;
+            float xv = (l16 == col) ? 1.f : 0.f;
+            // A[r][sc] = 0 for sc >= r, so lanes above the pivot are unchanged
+            xv -= a[0] * row_bcast<0>(xv);
+            xv -= a[1] * row_bcast<1>(xv);
+            xv -= a[2] * row_bcast<2>(xv);
+            xv -= a[3] * row_bcast<3>(xv);
+            xv -= a[4] * row_bcast<4>(xv);
+            xv -= a[5] * row_bcast<5>(xv);
+            xv -= a[6] * row_bcast<6>(xv);
+            xv -= a[7] * row_bcast<7>(xv);
+            xv -= a[8] * row_bcast<8>(xv);
+            xv -= a[9] * row_bcast<9>(xv);
+            xv -= a[10] * row_bcast<10>(xv);
+            xv -= a[11] * row_bcast<11>(xv);
+            xv -= a[12] * row_bcast<12>(xv);
+            xv -= a[13] * row_bcast<13>(xv);
+            xv -= a[14] * row_bcast<14>(xv);
+            t_s(wc)[l16 * TP + col] = (bf16)(xv * beta_s(wc)[col]);
         }
         __syncthreads();
     };
 
-    for (int c = -4; c < nit - 4; c += PD) {
-        iter(std::integral_constant<int, 0>{}, c);
-        if constexpr (PD > 1) iter(std::integral_constant<int, 1 % PD>{}, c + 1);
-        if constexpr (PD > 2) iter(std::integral_constant<int, 2 % PD>{}, c + 2);
-        if constexpr (PD > 3) iter(std::integral_constant<int, 3 % PD>{}, c + 3);
+    for (int c = -3; c < nit - 3; c += PD) {
+        prep_iter(std::integral_constant<int, 0>{}, c);
+        if constexpr (PD > 1) prep_iter(std::integral_constant<int, 1 % PD>{}, c + 1);
+        if constexpr (PD > 2) prep_iter(std::integral_constant<int, 2 % PD>{}, c + 2);
+        if constexpr (PD > 3) prep_iter(std::integral_constant<int, 3 % PD>{}, c + 3);
     }
 }
 
 template <int NCT, int PD>
 hipError_t launch_ws_t(const ChunkArgs& a, hipStream_t stream) {
     typedef WsCfg<NCT, PD> K;
+    static_assert(PD % 2 == 0, "the state waves step two chunks per trip");
     const int split = kHeadDim / K::DV;
     auto kern = chunk_ws_kernel<NCT, PD>;
     hipError_t e = hipFuncSetAttribute((const void*)kern,

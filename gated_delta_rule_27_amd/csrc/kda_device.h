@@ -107,6 +107,44 @@ __device__ __forceinline__ float row_shl(float src, float fill) {
                                            false));
 }
 
+// Lane N of each row of 16 lanes, broadcast to the whole row (row_newbcast).
+template <int N>
+__device__ __forceinline__ float row_bcast(float x) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x),
+                                           0x150 + N, 0xF, 0xF, false));
+}
+
+// Shift with zero fill (lanes whose source is outside the row read 0); the
+// compiler fuses these into the consuming add (v_add_f32_dpp).
+template <int N>
+__device__ __forceinline__ float row_shr0(float src) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, src),
+                                                                 0x110 + N, 0xF, 0xF, true));
+}
+template <int N>
+__device__ __forceinline__ float row_shl0(float src) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, src),
+                                                                 0x100 + N, 0xF, 0xF, true));
+}
+
+// Inclusive prefix sum over the 16 lanes of a row (lane r: x_0 + ... + x_r).
+__device__ __forceinline__ float row_prefix_sum(float x) {
+    x += row_shr0<1>(x);
+    x += row_shr0<2>(x);
+    x += row_shr0<4>(x);
+    x += row_shr0<8>(x);
+    return x;
+}
+// Exclusive suffix sum over the 16 lanes of a row (lane r: x_{r+1} + ... + x_15).
+__device__ __forceinline__ float row_suffix_sum_excl(float x) {
+    x += row_shl0<1>(x);
+    x += row_shl0<2>(x);
+    x += row_shl0<4>(x);
+    x += row_shl0<8>(x);
+    return row_shl0<1>(x);
+}
+
 // Inclusive prefix product over the 16 lanes of a row (lane r: x_0 ... x_r).
 __device__ __forceinline__ float row_prefix_prod(float x) {
     x *= row_shr<1>(x, 1.f);
