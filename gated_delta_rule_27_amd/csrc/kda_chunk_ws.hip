@@ -196,6 +196,10 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(
         };
         load_v(std::integral_constant<int, 0>{}, 0);
         load_v(std::integral_constant<int, 1>{}, 1);
+        // this lane's output column at row 4g of chunk 0; rows and chunks
+        // are uniform offsets from it
+        bf16* const o_lane = o + (size_t)(bos + 4 * g) * rowstride + headoff + col0 +
+                             16 * NCT * wave + l16;
 
         auto state_iter = [&](auto slot_c, int c) {
             constexpr int sv = decltype(slot_c)::value;  // == c & 1
@@ -203,7 +207,6 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(
                 const bf16* Kn = kn_s(c) + l16 * KP;
                 const bf16* Qs = qs_s(c) + l16 * KP;
                 const float* Gm = gam_s(c);
-                const int64_t t0 = bos + (int64_t)kWsC * c;
                 const int len = chunk_len(c);
                 floatx4 X[NCT], Ov[NCT], U[NCT];
 #pragma unroll
@@ -234,14 +237,12 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(
                     ub[ct] = acc_frag_k16(U[ct]);
                     Ov[ct] = mma_bf16_k16(ap, ub[ct], Ov[ct]);
                 }
+                bf16* const oc = o_lane + (size_t)c * cstride;
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) {
-                    const int j = col0 + 16 * (NCT * wave + ct) + l16;
+                for (int e = 0; e < 4; ++e) {
+                    if (4 * g + e < len) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 4 * g + e;
-                        if (r < len)
-                            o[(size_t)(t0 + r) * rowstride + headoff + j] = (bf16)Ov[ct][e];
+                        for (int ct = 0; ct < NCT; ++ct) oc[e * rowstride + 16 * ct] = (bf16)Ov[ct][e];
                     }
                 }
                 // S <- Diag(Gamma) S + Kvec^T U
@@ -322,10 +323,15 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(
                 qf[e] = (float)rq[s][e];
                 lg[e] = (float)rg[s][e] * kLog2e;
             }
-            if (len < kWsC && r >= len) {  // rows past the end: no decay, no write
+            if (len < kWsC) {  // uniform: only the last chunk has rows past the end
+                const bool dead = r >= len;  // such rows neither decay nor write
 #pragma unroll
-                for (int e = 0; e < 4; ++e) kf[e] = qf[e] = lg[e] = 0.f;
-                bt = 0.f;
+                for (int e = 0; e < 4; ++e) {
+                    kf[e] = dead ? 0.f : kf[e];
+                    qf[e] = dead ? 0.f : qf[e];
+                    lg[e] = dead ? 0.f : lg[e];
+                }
+                bt = dead ? 0.f : bt;
             }
             bf16x4 kn, qs, kh;
             floatx4 gam;
@@ -333,11 +339,10 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float P = row_prefix_sum(lg[e]);        // G_r / ln 2
-                const float Sx = row_suffix_sum_excl(lg[e]);  // (G_C - G_r) / ln 2
                 const float E = exp2f_fast(P);                // exp(G_r)       <= 1
                 const float Einv = exp2f_fast(-P);            // exp(-G_r)      <= e^80
-                const float Hs = exp2f_fast(Sx);              // exp(G_C - G_r) <= 1
-                gam[e] = E * Hs;                              // exp(G_C)
+                gam[e] = row_bcast<15>(E);                    // exp(G_C): E of the last token
+                const float Hs = gam[e] * Einv;               // exp(G_C - G_r) <= 1
                 kn[e] = (bf16)(-kf[e] * E);
                 qs[e] = (bf16)(qf[e] * E);
                 kh[e] = (bf16)(kf[e] * Einv);
