@@ -430,24 +430,31 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(
                 }
             }
         }
+        // (bf16: P U accumulates in its own tile and is added on the VALU, so
+        // no accumulator passes from the fp32 MFMA chain above to a bf16 MFMA)
 #pragma unroll
         for (int mt = 0; mt < NB; ++mt) {
             const TOp* rp = sP + (16 * mt + l16) * CP;
             if constexpr (kBF16 && C >= 32) {
+                floatx4 PU[NCT];
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) PU[ct] = zero4();
 #pragma unroll
                 for (int pb2 = 0; pb2 < NB / 2; ++pb2) {
                     if (32 * pb2 > 16 * mt + 15) continue;
                     const bf16x8 a = frag_k32(rp, 32 * pb2, g);
 #pragma unroll
                     for (int ct = 0; ct < NCT; ++ct)
-                        O[ct][mt] = mma_bf16_k32(
-                            a, acc_frag_k32(U[ct][2 * pb2], U[ct][2 * pb2 + 1]), O[ct][mt]);
+                        PU[ct] = mma_bf16_k32(
+                            a, acc_frag_k32(U[ct][2 * pb2], U[ct][2 * pb2 + 1]), PU[ct]);
                 }
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) O[ct][mt] += PU[ct];
             } else if constexpr (kBF16) {
                 const bf16x4 a = frag_k16(rp, 0, g);
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct)
-                    O[ct][mt] = mma_bf16_k16(a, acc_frag_k16(U[ct][0]), O[ct][mt]);
+                    O[ct][mt] += mma_bf16_k16(a, acc_frag_k16(U[ct][0]), zero4());
             } else {
 #pragma unroll
                 for (int kt = 0; kt <= mt; ++kt) {

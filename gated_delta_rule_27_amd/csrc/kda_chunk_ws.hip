@@ -19,12 +19,12 @@
 // state update is a chain over chunks.  The pages' FlashKDA note describes
 // overlapping the token-parallel work with the head-parallel state
 // propagation ("From GPT-2 to Kimi K3", ch. 6 "Training, prefill, and decode
-// use different paths").  Here the overlap is inside one workgroup of twelve
-// wavefronts, three per SIMD:
-//   waves 0-3 (state): each owns 16 * NCT value columns of the 128 x 128
+// use different paths").  Here the overlap is inside one workgroup of NSW + 8
+// wavefronts (12 for a 64-column slice, 16 for all 128 columns):
+//   waves 0..NSW-1 (state): each owns 16 * NCT value columns of the 128 x 128
 //     state in MFMA accumulators for the whole sequence and runs the state
 //     chain of chunk c; its V values arrive by its own register prefetch;
-//   waves 4-11 (prep), lane = (token r, 4 key channels): load q, k, log_alpha
+//   the next 8 waves (prep), lane = (token r, 4 key channels): load q, k, log_alpha
 //     of chunk c+3 straight into the lanes that use them (PD chunks ahead),
 //     take the cumulative log-decay over the chunk's 16 tokens as a DPP scan
 //     across the 16 lanes of a row and write the decay-scaled operands;
@@ -54,11 +54,11 @@ constexpr float kLog2e = 1.4426950408889634f;
 // 2^x on the transcendental unit (v_exp_f32); |x| stays far inside its range here
 __device__ __forceinline__ float exp2f_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <int NCT, int PD>
+template <int NCT, int NSW_, int PD>
 struct WsCfg {
-    static constexpr int NSW = 4;                // state waves
+    static constexpr int NSW = NSW_;             // state waves
     static constexpr int NPW = 8;                // prep waves
-    static constexpr int NT = 64 * (NSW + NPW);  // 768 threads
+    static constexpr int NT = 64 * (NSW + NPW);  // threads
     static constexpr int DV = 16 * NCT * NSW;    // value columns per workgroup
     static constexpr int KP = kHeadDim + 8;      // bf16 stride of [token][channel]
     static constexpr int TP = kWsC + 8;          // bf16 stride of [.][token]
@@ -84,13 +84,13 @@ struct WsCfg {
     static_assert(bytes <= 160 * 1024, "LDS budget");
 };
 
-template <int NCT, int PD>
-__global__ __launch_bounds__(768) void chunk_ws_kernel(
+template <int NCT, int NSW, int PD>
+__global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ log_alpha, const bf16* __restrict__ beta,
     const float* __restrict__ h0, const int32_t* __restrict__ cu_seqlens, int64_t T_total,
     int32_t H, int32_t split, int32_t units, bf16* __restrict__ o, float* __restrict__ h_T) {
-    typedef WsCfg<NCT, PD> K;
+    typedef WsCfg<NCT, NSW, PD> K;
     constexpr int KP = K::KP, TP = K::TP, AP = K::AP, DV = K::DV;
 
     // XCD-aware id: slices of one unit share the id's residue mod 8
@@ -235,7 +235,7 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(
                 for (int ct = 0; ct < NCT; ++ct) {
                     U[ct] = mma_bf16_k16(at, acc_frag_k16(X[ct]), zero4());
                     ub[ct] = acc_frag_k16(U[ct]);
-                    Ov[ct] = mma_bf16_k16(ap, ub[ct], Ov[ct]);
+                    Ov[ct] = mma_bf16_k16_as_k32(ap, ub[ct], Ov[ct]);  // same opcode as Qtil S
                 }
                 bf16* const oc = o_lane + (size_t)c * cstride;
 #pragma unroll
@@ -424,12 +424,12 @@ __global__ __launch_bounds__(768) void chunk_ws_kernel(
     }
 }
 
-template <int NCT, int PD>
+template <int NCT, int NSW, int PD>
 hipError_t launch_ws_t(const ChunkArgs& a, hipStream_t stream) {
-    typedef WsCfg<NCT, PD> K;
+    typedef WsCfg<NCT, NSW, PD> K;
     static_assert(PD % 2 == 0, "the state waves step two chunks per trip");
     const int split = kHeadDim / K::DV;
-    auto kern = chunk_ws_kernel<NCT, PD>;
+    auto kern = chunk_ws_kernel<NCT, NSW, PD>;
     hipError_t e = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)K::bytes);
     if (e != hipSuccess) return e;
@@ -447,8 +447,8 @@ hipError_t launch_ws_t(const ChunkArgs& a, hipStream_t stream) {
 
 hipError_t launch_chunk_ws(const ChunkArgs& a, int split, hipStream_t stream) {
     switch (split) {
-        case 1: return launch_ws_t<2, 4>(a, stream);
-        case 2: return launch_ws_t<1, 4>(a, stream);
+        case 1: return launch_ws_t<1, 8, 4>(a, stream);  // 16 waves, 128 columns
+        case 2: return launch_ws_t<1, 4, 4>(a, stream);  // 12 waves, 64 columns
         default: return hipErrorInvalidValue;
     }
 }

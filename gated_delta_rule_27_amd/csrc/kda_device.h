@@ -61,6 +61,18 @@ __device__ __forceinline__ floatx4 mma_f32_k16(floatx4 a, floatx4 b, floatx4 c) 
     return c;
 }
 
+// A k = 16 bf16 product issued as the k = 32 instruction with the upper half
+// of k zero.  Used where the accumulator comes straight from a chain of
+// 16x16x32 products: an accumulator chain then stays on one MFMA opcode,
+// whose back-to-back dependent accumulation the hardware forwards, instead
+// of mixing opcodes on one accumulator, which needs software wait states
+// between the two MFMAs.
+__device__ __forceinline__ floatx4 mma_bf16_k16_as_k32(bf16x4 a, bf16x4 b, floatx4 c) {
+    const bf16 z = (bf16)0.f;
+    return mma_bf16_k32(bf16x8{a[0], a[1], a[2], a[3], z, z, z, z},
+                        bf16x8{b[0], b[1], b[2], b[3], z, z, z, z}, c);
+}
+
 // ---- fragments -------------------------------------------------------------
 
 // bf16 operand over k-block [kb, kb+32) from an LDS row (k contiguous).

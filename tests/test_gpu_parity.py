@@ -51,6 +51,32 @@ def test_small_parity(dtype, lengths, H, h0_std, chunk, split):
     check("h_T", np_(hT), rh, TOL[dtype])
 
 
+PER_CHUNK = [
+    # dtype, chunk, split: every kernel variant of the prefill path
+    ("bf16", 16, 1), ("bf16", 16, 2), ("bf16", 32, 1), ("bf16", 32, 4),
+    ("f32", 16, 1), ("f32", 16, 2), ("f32", 32, 4),
+]
+
+
+@pytest.mark.parametrize("dtype,chunk,split", PER_CHUNK)
+def test_every_chunk_output_under_slow_decay(dtype, chunk, split):
+    """Each chunk's output separately, with slow decay (log alpha near 0) so
+    that the incoming state carries into every chunk, and a non-zero h0:
+    a wrong output in any one chunk (for instance in one unrolled copy of a
+    pipelined loop) fails here even when the whole-tensor norm would hide it."""
+    kda = need_gpu()
+    T, H = 160, 2
+    case(f"per-chunk dtype={dtype} T={T} H={H} chunk={chunk} split={split} decay_mu=-6")
+    d = kda_inputs.prefill_inputs(T, H, dtype=dtype, device="cuda", seed=4242, h0_std=0.1,
+                                  decay_mu=-6.0)
+    o, hT = gpu_prefill(kda, d, chunk, split)
+    ro, rh = oracle_prefill(d)
+    got = np_(o)
+    for c in range(T // 16):
+        check(f"o[chunk {c}]", got[16 * c:16 * c + 16], ro[16 * c:16 * c + 16], TOL[dtype])
+    check("h_T", np_(hT), rh, TOL[dtype])
+
+
 def test_all_empty_sequences_return_h0():
     kda = need_gpu()
     case("T_total = 0 with three empty documents")
