@@ -9,7 +9,9 @@ resident in HBM before timing; two input sets alternate so that consecutive
 steps do not hit in the 256 MiB Infinity Cache.  The decode half of the
 metric (decode state GB/s) is measured in the same run on the batched
 decode workload (256 sequences x 96 heads, one token each, state updated in
-place) and reported under "decode".
+place) and reported under "decode".  The 16-document varlen prefill is timed
+too (under "other_workloads"; `--long` adds the 1M-token sequence), and a
+1 GiB device copy gives the measured streaming ceiling beside the 8 TB/s peak.
 
 Prints ONE JSON line.  `--gpus N` with N > 1 exits: this build is single-GPU.
 """
@@ -94,19 +96,99 @@ def time_launches(fn, steps, warmup, stream):
     return wall, [a.elapsed_time(b) for a, b in ev]
 
 
+def host_info():
+    """CPU model and host memory, for the record."""
+    model, mem_gib = None, None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemTotal"):
+                    mem_gib = round(int(line.split()[1]) / 2**20, 1)
+                    break
+    except OSError:
+        pass
+    return model, mem_gib
+
+
 def cpu_baseline(T, H):
-    """The fp32 CPU oracle on the whole prefill workload, on this host."""
+    """The CPU oracle on the whole prefill workload, on this host: fp32, the
+    median of three runs (the reported value), and one fp64 run."""
     import kda_inputs
     import oracle
     d = kda_inputs.prefill_inputs(T, H, dtype="bf16", device="cpu", seed=1001)
     args = [kda_inputs.to_numpy(d[k]) for k in ("q", "k", "v", "log_alpha", "beta")]
     threads = oracle.default_threads()
+    runs = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        oracle.fwd(*args, precision="f32", nthreads=threads)
+        runs.append(time.perf_counter() - t0)
+    dt = sorted(runs)[1]
     t0 = time.perf_counter()
-    oracle.fwd(*args, precision="f32", nthreads=threads)
-    dt = time.perf_counter() - t0
+    oracle.fwd(*args, precision="f64", nthreads=threads)
+    dt64 = time.perf_counter() - t0
+    model, mem_gib = host_info()
     return {"value": round(T / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"whole prefill workload (T={T}, H={H}, d=128), fp32 oracle, "
-                      f"{dt:.2f} s wall"}
+            "sample": f"whole prefill workload (T={T}, H={H}, d=128), fp32 oracle, median of "
+                      f"3 runs {dt:.2f} s wall",
+            "fp64_tokens_per_s": round(T / dt64, 1), "cpu_model": model, "host_mem_gib": mem_gib}
+
+
+def median(xs):
+    ys = sorted(xs)
+    n = len(ys)
+    return ys[n // 2] if n % 2 else 0.5 * (ys[n // 2 - 1] + ys[n // 2])
+
+
+def copy_bandwidth(torch, dev, stream):
+    """A plain device copy of 1 GiB (read + write), timed with HIP events:
+    the practical streaming ceiling of this GPU, beside the 8 TB/s peak."""
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    gbps = 5 * 2 * src.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    return round(gbps, 1)
+
+
+def extra_prefill(torch, kda, kda_inputs, dev, stream, cfg_id, steps, warmup):
+    """Timing line of another prefill workload (same kernel path, its default
+    configuration): tokens/s, HBM fraction and %MFMA at F(64)."""
+    d = kda_inputs.config_inputs(cfg_id, device=dev)
+    T, H = d["q"].shape[0], d["q"].shape[1]
+    N = 1 if d["cu_seqlens"] is None else d["cu_seqlens"].numel() - 1
+    o = torch.empty_like(d["v"])
+    hT = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
+
+    def step(i):
+        kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], h0=d["h0"],
+                          cu_seqlens=d["cu_seqlens"], o=o, h_T=hT)
+
+    wall, ms = time_launches(step, steps, warmup, stream)
+    avg = sum(ms) / len(ms)
+    nbytes = prefill_bytes(T, H, N, h0=d["h0"] is not None)
+    flops = T * H * flops_per_head_token(64)
+    out = {"workload": kda_inputs.CONFIGS[cfg_id]["name"], "T": T, "H": H, "sequences": N,
+           "tokens_per_s": round(T * steps / wall, 1), "kernel_ms": round(avg, 4),
+           "kernel_ms_median": round(median(ms), 4),
+           "hbm_frac": round(nbytes / (avg * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+           "mfma_frac_F64": round(flops / (avg * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4),
+           "algorithmic_bytes": nbytes}
+    del d, o, hT
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -121,6 +203,10 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy three times, as the "
                          "reference kernel for scaling HBM byte counters")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the 16-document varlen prefill line")
+    ap.add_argument("--long", action="store_true",
+                    help="also time the 1M-token single-sequence prefill (129 GB of HBM)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
@@ -183,7 +269,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "kda::chunk_ws_kernel",
-                     "kernel_ms": round(avg_ms, 5), "algorithmic_bytes": nbytes},
+                     "kernel_ms": round(avg_ms, 5), "kernel_ms_median": round(median(ms), 5),
+                     "algorithmic_bytes": nbytes},
         "mfma": {"flops_per_step": flops, "counted_at_chunk": 64,
                  "frac_of_bf16_peak": round(mfma_frac, 4)},
         "kernel_source_hash": src_hash,
@@ -215,10 +302,27 @@ def main():
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(total_bytes / (davg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                          "traffic": read_traffic("decode_B256_H96_bf16", src_hash),
-                         "kernel": "kda::decode_kernel"},
+                         "kernel": "kda::decode_kernel",
+                         "kernel_ms_median": round(median(dms), 5)},
         }
         del dd
         torch.cuda.empty_cache()
+
+    # measured streaming ceiling: fractions against it beside the 8 TB/s peak
+    cbw = copy_bandwidth(torch, dev, stream)
+    out["copy_GBps"] = cbw
+    out["roofline"]["frac_of_copy"] = round(achieved / cbw, 4)
+    if "decode" in out:
+        out["decode"]["roofline"]["frac_of_copy"] = round(
+            out["decode"]["roofline"]["achieved"] / cbw, 4)
+
+    extra = []
+    if not args.no_extra:
+        extra.append(extra_prefill(torch, kda, kda_inputs, dev, stream, 3, args.steps, args.warmup))
+    if args.long:
+        extra.append(extra_prefill(torch, kda, kda_inputs, dev, stream, 4, 3, 1))
+    if extra:
+        out["other_workloads"] = extra
 
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB

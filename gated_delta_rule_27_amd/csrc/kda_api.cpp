@@ -84,7 +84,8 @@ kda_status kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const v
                             size_t workspace_bytes, int32_t chunk, int32_t dv_split,
                             hipStream_t stream) {
     if (!valid_dtype(dt)) return KDA_ERR_BAD_DTYPE;
-    if (N < 1 || T_total < 0 || H < 1 || Dk != kda::kHeadDim || Dv != kda::kHeadDim)
+    if (N < 1 || T_total < 0 || H < 1 || H > KDA_MAX_HEADS || Dk != kda::kHeadDim ||
+        Dv != kda::kHeadDim)
         return KDA_ERR_BAD_SHAPE;
     if (!cu_seqlens && N != 1) return KDA_ERR_BAD_SHAPE;
     const uint64_t row = (uint64_t)H * kda::kHeadDim;

@@ -24,13 +24,13 @@
 //   waves 0..NSW-1 (state): each owns 16 * NCT value columns of the 128 x 128
 //     state in MFMA accumulators for the whole sequence and runs the state
 //     chain of chunk c; its V values arrive by its own register prefetch;
+//     state waves 0 and 1 then form the Gram tiles of chunk c+2 (A and P);
 //   the next 8 waves (prep), lane = (token r, 4 key channels): load q, k, log_alpha
 //     of chunk c+3 straight into the lanes that use them (PD chunks ahead),
 //     take the cumulative log-decay over the chunk's 16 tokens as a DPP scan
 //     across the 16 lanes of a row and write the decay-scaled operands;
-//     prep waves 4 and 5 (of the eight) also form the Gram tiles of chunk c+2
-//     (A and P) and prep waves 0-3 the triangular solve of chunk c+1 (lane =
-//     one element of the 16 x 16 inverse).
+//     prep waves 0-3 also run the triangular solve of chunk c+1 (lane = one
+//     element of the 16 x 16 inverse).
 // Every stage reads only what an earlier iteration wrote, so one barrier per
 // chunk is the only synchronisation.  LDS holds ring buffers indexed by
 // chunk, each as deep as its value lives (77 KB in all).
@@ -127,15 +127,10 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
     const int nch = (int)((seqlen + kWsC - 1) / kWsC);
     const size_t rowstride = (size_t)H * kHeadDim;
     const size_t headoff = (size_t)h * kHeadDim;
-    const size_t cstride = (size_t)kWsC * rowstride;  // elements per chunk of tokens
     const int col0 = slice * DV;
     // pipeline iterations c = -3 .. nit-4: the prep stage of iteration c
     // handles chunk c+3, the Gram stage c+2, the solve c+1, the state c
     const int nit = (nch + 3 + PD - 1) / PD * PD;
-    auto chunk_len = [&](int yc) {
-        const int64_t rem = seqlen - (int64_t)kWsC * yc;
-        return (int)(rem < 0 ? 0 : (rem < kWsC ? rem : kWsC));
-    };
 
     // An empty sequence has no chunks: only h_T = h0 is written, and no
     // input pointer is touched (they may be null when T_total is 0).  The
@@ -159,6 +154,31 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
         return;
     }
 
+    // Gram tiles of chunk zc, on MFMA (transposed products: acc(s, r)):
+    // A[r][s] = beta_r (Ktil_r . Khat_s), strictly lower (Kn = -Ktil), or
+    // P[r][s] = Qtil_r . Khat_s for s <= r.  Formed by state waves 0 (A) and
+    // 1 (P), which have slack after their own chunk.
+    auto gram_tile = [&](bool isP, int zc) {
+        const bf16* arow = kh_s(zc) + l16 * KP;
+        const bf16* brow = (isP ? qs_s(zc) : kn_s(zc)) + l16 * KP;
+        floatx4 acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < kHeadDim; kb += 32)
+            acc = mma_bf16_k32(frag_k32(arow, kb, g), frag_k32(brow, kb, g), acc);
+        if (!isP) {
+            const float br = beta_s(zc)[l16];
+            floatx4 out;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[e] = (4 * g + e >= l16) ? 0.f : -acc[e] * br;
+            *reinterpret_cast<floatx4*>(a_s(zc) + l16 * AP + 4 * g) = out;
+        } else {
+            bf16x4 out;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[e] = (bf16)((4 * g + e > l16) ? 0.f : acc[e]);
+            *reinterpret_cast<bf16x4*>(p_s(zc) + l16 * TP + 4 * g) = out;
+        }
+    };
+
     if (wave < K::NSW) {
         // ======================= state waves =======================
         floatx4 S[NCT][8];
@@ -174,40 +194,39 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
                         S[ct][it][e] = src ? src[(16 * it + 4 * g + e) * kHeadDim + j] : 0.f;
             }
         }
-        // V of a chunk: rows 4g..4g+3 of this lane's columns, two chunks in
-        // flight (clamped addresses past the end: those rows never reach an
-        // output, since their beta is zero)
-        bf16 vr[2][NCT][4];
-        auto load_v = [&](auto slot_c, int yc) {
+        // V of a chunk: rows 4g..4g+3 of this lane's columns, four chunks in
+        // flight, through a buffer resource over the chunk's rows inside the
+        // sequence: rows past its end read 0 (they never reach an output,
+        // since their beta is zero) and output stores there are dropped, so
+        // every chunk issues the same loads and stores without branches.  The
+        // prefetch distance keeps the memory-counter wait for a chunk's V
+        // clear of the output stores of the iterations just before it.
+        const uint32_t vo_lane = (uint32_t)(
+            ((size_t)(4 * g) * rowstride + headoff + col0 + 16 * NCT * wave + l16) * 2);
+        const uint32_t vo_row = (uint32_t)(rowstride * 2);
+        auto rows_rsrc = [&](const bf16* base, int y) {
+            const int64_t rows = (y >= 0 && y < nch) ? seqlen - (int64_t)kWsC * y : 0;
+            return make_rsrc(base + (size_t)(bos + (int64_t)kWsC * (y < 0 ? 0 : y)) * rowstride,
+                             rows * (int64_t)rowstride * 2);
+        };
+        bf16 vr[4][NCT][4];
+        auto load_v = [&](auto slot_c, int y) {
             constexpr int sv = decltype(slot_c)::value;
+            const rsrc_t rv = rows_rsrc(v, y);
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                const int j = col0 + 16 * (NCT * wave + ct) + l16;
+            for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    // yc is -1 in the first pipeline iteration: rows before the
-                    // sequence start are clamped like rows past its end
-                    const int64_t r = (int64_t)kWsC * yc + 4 * g + e;
-                    const size_t off =
-                        (r >= 0 && r < seqlen) ? (size_t)(bos + r) * rowstride + headoff + j : 0;
-                    vr[sv][ct][e] = v[off];
-                }
-            }
+                for (int e = 0; e < 4; ++e)
+                    vr[sv][ct][e] = buf_load_bf16(rv, vo_lane + e * vo_row + 32 * ct);
         };
         load_v(std::integral_constant<int, 0>{}, 0);
-        load_v(std::integral_constant<int, 1>{}, 1);
-        // this lane's output column at row 4g of chunk 0; rows and chunks
-        // are uniform offsets from it
-        bf16* const o_lane = o + (size_t)(bos + 4 * g) * rowstride + headoff + col0 +
-                             16 * NCT * wave + l16;
 
         auto state_iter = [&](auto slot_c, int c) {
-            constexpr int sv = decltype(slot_c)::value;  // == c & 1
+            constexpr int sv = decltype(slot_c)::value;  // == c & 3
             if (c >= 0 && c < nch) {
                 const bf16* Kn = kn_s(c) + l16 * KP;
                 const bf16* Qs = qs_s(c) + l16 * KP;
                 const float* Gm = gam_s(c);
-                const int len = chunk_len(c);
                 floatx4 X[NCT], Ov[NCT], U[NCT];
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) {
@@ -237,14 +256,12 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
                     ub[ct] = acc_frag_k16(U[ct]);
                     Ov[ct] = mma_bf16_k16_as_k32(ap, ub[ct], Ov[ct]);  // same opcode as Qtil S
                 }
-                bf16* const oc = o_lane + (size_t)c * cstride;
+                const rsrc_t ro = rows_rsrc(o, c);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if (4 * g + e < len) {
+                for (int e = 0; e < 4; ++e)
 #pragma unroll
-                        for (int ct = 0; ct < NCT; ++ct) oc[e * rowstride + 16 * ct] = (bf16)Ov[ct][e];
-                    }
-                }
+                    for (int ct = 0; ct < NCT; ++ct)
+                        buf_store_bf16((bf16)Ov[ct][e], ro, vo_lane + e * vo_row + 32 * ct);
                 // S <- Diag(Gamma) S + Kvec^T U
                 const bf16* KvT = kvt_s(c);
 #pragma unroll
@@ -256,15 +273,23 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
                         S[ct][it] = mma_bf16_k16(a, ub[ct], S[ct][it] * gm);
                 }
             }
-            // refill this V slot with chunk c+2, unconditionally, so the memory
-            // counter stays exact
-            load_v(slot_c, c + 2);
+            // the Gram tiles of chunk c+2 (read by the solve and by this
+            // stage two iterations later)
+            if (wave < 2) {
+                const int zc = c + 2;
+                if (zc >= 0 && zc < nch) gram_tile(wave == 1, zc);
+            }
+            // refill this V slot with chunk c+4 on the one path every
+            // iteration takes, so its registers and memory count are fixed
+            load_v(slot_c, c + 4);
             __syncthreads();
         };
-        for (int c = -3; c < nit - 3; c += 2) {
-            // -3 is odd: keep the V slot equal to c & 1
+        for (int c = -3; c < nit - 3; c += 4) {
+            // -3 = 1 mod 4: V slots 1, 2, 3, 0
             state_iter(std::integral_constant<int, 1>{}, c);
-            state_iter(std::integral_constant<int, 0>{}, c + 1);
+            state_iter(std::integral_constant<int, 2>{}, c + 1);
+            state_iter(std::integral_constant<int, 3>{}, c + 2);
+            state_iter(std::integral_constant<int, 0>{}, c + 3);
         }
         if (h_T) {
             float* dst = h_T + ((size_t)n * (size_t)H + h) * (kHeadDim * kHeadDim);
@@ -285,24 +310,22 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
     const int pw = wave - K::NSW;   // 0..7
     const int r = l16;              // token of the chunk
     const int ch0 = 16 * pw + 4 * g;  // first of this lane's 4 key channels
-    // register slots of in-flight loads: chunk y lives in slot y % PD.  All
-    // lanes issue the same loads for every chunk, from clamped (valid)
-    // addresses, so the memory counter stays exact; rows past the end of the
-    // sequence are zeroed when used.
+    // register slots of in-flight loads: chunk y lives in slot y % PD.  The
+    // loads go through buffer resources over the chunk's rows inside the
+    // sequence, so rows past its end read 0: they neither decay nor write.
     bf16x4 rq[PD], rk[PD], rg[PD];
     bf16 rb[PD];
-    const size_t oq0 = (size_t)(bos + r) * rowstride + headoff + ch0;
-    const size_t ob0 = (size_t)(bos + r) * H + h;
+    const uint32_t qo_lane = (uint32_t)(((size_t)r * rowstride + headoff + ch0) * 2);
+    const uint32_t bo_lane = (uint32_t)(((size_t)r * H + h) * 2);
     auto load_chunk = [&](auto slot_c, int yc) {
         constexpr int s = decltype(slot_c)::value;
-        const int64_t row = (int64_t)kWsC * yc + r;
-        const bool ok = row >= 0 && row < seqlen;
-        const size_t oq = ok ? oq0 + (size_t)yc * cstride : 0;
-        const size_t ob = ok ? ob0 + (size_t)yc * kWsC * H : 0;
-        rq[s] = *reinterpret_cast<const bf16x4*>(q + oq);
-        rk[s] = *reinterpret_cast<const bf16x4*>(k + oq);
-        rg[s] = *reinterpret_cast<const bf16x4*>(log_alpha + oq);
-        rb[s] = beta[ob];
+        const int64_t rows = yc < nch ? seqlen - (int64_t)kWsC * yc : 0;
+        const size_t t0 = (size_t)(bos + (int64_t)kWsC * yc);
+        const int64_t tok_bytes = rows * (int64_t)rowstride * 2;
+        rq[s] = buf_load_bf16x4(make_rsrc(q + t0 * rowstride, tok_bytes), qo_lane);
+        rk[s] = buf_load_bf16x4(make_rsrc(k + t0 * rowstride, tok_bytes), qo_lane);
+        rg[s] = buf_load_bf16x4(make_rsrc(log_alpha + t0 * rowstride, tok_bytes), qo_lane);
+        rb[s] = buf_load_bf16(make_rsrc(beta + t0 * H, rows * (int64_t)H * 2), bo_lane);
     };
     load_chunk(std::integral_constant<int, 0>{}, 0);
     if constexpr (PD > 1) load_chunk(std::integral_constant<int, 1 % PD>{}, 1);
@@ -314,24 +337,13 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
         // (1) decay factors and scaled operands of chunk c+3
         const int yc = c + 3;
         if (yc < nch) {
-            const int len = chunk_len(yc);
             float kf[4], qf[4], lg[4];
-            float bt = (float)rb[s];
+            const float bt = (float)rb[s];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 kf[e] = (float)rk[s][e];
                 qf[e] = (float)rq[s][e];
                 lg[e] = (float)rg[s][e] * kLog2e;
-            }
-            if (len < kWsC) {  // uniform: only the last chunk has rows past the end
-                const bool dead = r >= len;  // such rows neither decay nor write
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    kf[e] = dead ? 0.f : kf[e];
-                    qf[e] = dead ? 0.f : qf[e];
-                    lg[e] = dead ? 0.f : lg[e];
-                }
-                bt = dead ? 0.f : bt;
             }
             bf16x4 kn, qs, kh;
             floatx4 gam;
@@ -355,30 +367,6 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
             if (pw == 0 && g == 0) beta_s(yc)[r] = bt;
         }
         load_chunk(slot_c, yc + PD);
-        // (2) Gram tiles of chunk c+2 (transposed products: acc(s, r))
-        const int zc = c + 2;
-        if (zc >= 0 && zc < nch && (pw == 4 || pw == 5)) {
-            const bf16* arow = kh_s(zc) + l16 * KP;
-            const bool isP = pw == 5;
-            const bf16* brow = (isP ? qs_s(zc) : kn_s(zc)) + l16 * KP;
-            floatx4 acc = zero4();
-#pragma unroll
-            for (int kb = 0; kb < kHeadDim; kb += 32)
-                acc = mma_bf16_k32(frag_k32(arow, kb, g), frag_k32(brow, kb, g), acc);
-            if (!isP) {
-                // A[r][s] = beta_r (Ktil_r . Khat_s), strictly lower (Kn = -Ktil)
-                const float br = beta_s(zc)[l16];
-                floatx4 out;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) out[e] = (4 * g + e >= l16) ? 0.f : -acc[e] * br;
-                *reinterpret_cast<floatx4*>(a_s(zc) + l16 * AP + 4 * g) = out;
-            } else {
-                bf16x4 out;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) out[e] = (bf16)((4 * g + e > l16) ? 0.f : acc[e]);
-                *reinterpret_cast<bf16x4*>(p_s(zc) + l16 * TP + 4 * g) = out;
-            }
-        }
         // (3) UT transform of chunk c+1 on prep waves 0-3: lane = (row
         // l16, column 4 * pw + g) of X = (I + A)^{-1}; forward elimination
         // down the columns of A, the pivot X[sc][c] broadcast along the row

@@ -182,6 +182,32 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
+// ---- buffer resources ---------------------------------------------------------
+// A raw buffer resource (stride 0) covers `bytes` bytes from `base`; loads at
+// byte offsets at or past the end return 0 and stores there are dropped by
+// the hardware.  The chunk kernels use one per chunk of tokens, sized to the
+// rows of that chunk inside its sequence, so partial and out-of-range chunks
+// need neither branches nor 64-bit address arithmetic per element.
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// word 3 of a gfx9-family raw buffer descriptor: 32-bit data format, no swizzle
+constexpr int kBufWord3 = 0x00020000;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    const uint32_t n = bytes <= 0 ? 0u : (bytes >= 0xFFFFFFFFll ? 0xFFFFFFFFu : (uint32_t)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)n, kBufWord3);
+}
+__device__ __forceinline__ bf16 buf_load_bf16(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(bf16, (short)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ bf16x4 buf_load_bf16x4(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ void buf_store_bf16(bf16 x, rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(short, x), r, (int)off, 0, 0);
+}
+
 // ---- vector global loads of 4 or 8 elements ----------------------------------
 
 template <typename T>

@@ -36,7 +36,9 @@
  *     nothing is launched and the outputs are untouched.  KDA_ERR_DEVICE
  *     reports a launch failure (the outputs are then unspecified).
  *   - d_k = d_v = 128 (the K3 head shape, "An infra-oriented diagram of
- *     Kimi K3", KDA card).  Other sizes return KDA_ERR_BAD_SHAPE.
+ *     Kimi K3", KDA card).  Other sizes return KDA_ERR_BAD_SHAPE.  The
+ *     number of heads H is at most KDA_MAX_HEADS (the kernels address a
+ *     16-token chunk of one tensor with 32-bit offsets).
  *   - Input contract (not checked, never clamped): log_alpha in [-5, 0]
  *     (the K3 lower-bounded log-decay, "From GPT-2 to Kimi K3", ch. 5
  *     "K3's lower-bounded decay"), beta in [0, 1].  Inside the contract the
@@ -57,12 +59,15 @@ extern "C" {
 
 #define KDA_ABI_VERSION 1
 
+#define KDA_MAX_HEADS 65536
+
 typedef enum {
     KDA_OK = 0,
     KDA_ERR_NULL_ARG = 1,   /* a required pointer is NULL                    */
     KDA_ERR_BAD_SHAPE = 2,  /* a size <= 0 (or < 0 where 0 is allowed),
-                               d_k or d_v != 128, N != 1 without cu_seqlens,
-                               or an unsupported chunk / split override      */
+                               d_k or d_v != 128, H > KDA_MAX_HEADS, N != 1
+                               without cu_seqlens, or an unsupported chunk /
+                               split override                                */
     KDA_ERR_BAD_DTYPE = 3,  /* dtype is not a kda_dtype                      */
     KDA_ERR_MISALIGNED = 4, /* a pointer breaks the alignment rules above    */
     KDA_ERR_ALIAS = 5,      /* an output overlaps an input or another output */
@@ -114,8 +119,8 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
 
 /*
  * kda_chunk_fwd with explicit tuning choices.  chunk = tokens per chunk
- * (16, 32 or 64; 0 = library choice); dv_split = number of workgroups that
- * share one head's value columns (1, 2, 4 or 8; 0 = library choice).  The
+ * (16 or 32; 0 = library choice); dv_split = number of workgroups that
+ * share one head's value columns (1, 2 or 4; 0 = library choice).  The
  * chunk length is a tuning parameter, not a property of the recurrence
  * ("From GPT-2 to Kimi K3", ch. 6 "Chunkwise execution"): every choice
  * computes the same function up to rounding.  Unsupported combinations

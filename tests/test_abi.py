@@ -92,6 +92,7 @@ def decode(L, **kw):
     (dict(chunk=8), BAD_SHAPE),
     (dict(split=3), BAD_SHAPE),
     (dict(split=8), BAD_SHAPE),
+    (dict(H=65537), BAD_SHAPE),       # above KDA_MAX_HEADS
     (dict(q=None), NULL_ARG),
     (dict(k=None), NULL_ARG),
     (dict(v=None), NULL_ARG),
