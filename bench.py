@@ -191,6 +191,44 @@ def extra_prefill(torch, kda, kda_inputs, dev, stream, cfg_id, steps, warmup):
     return out
 
 
+def verify_replay(torch, kda, kda_inputs, dev, stream, steps, warmup):
+    """Batched speculative decoding on the chunk path: 256 requests x 96
+    heads, each with its cached fp32 state; a 7-token draft is verified in
+    one call (outputs only), then the 4 accepted tokens are replayed from the
+    same states in a second call that writes the new states.  Compared with
+    7 single-token decode steps, which read and write every state 7 times."""
+    B, H, draft, acc = 256, 96, 7, 4
+    d = kda_inputs.prefill_inputs(B * draft, H, dtype="bf16", device=dev, seed=1005,
+                                  lengths=[draft] * B, h0_std=0.02)
+    # the accepted tokens: the first `acc` of every request's draft
+    dr = {x: d[x].view(B, draft, *d[x].shape[1:])[:, :acc].reshape(B * acc, *d[x].shape[1:])
+          .contiguous() for x in ("q", "k", "v", "log_alpha", "beta")}
+    dr["cu_seqlens"] = torch.arange(0, B * acc + 1, acc, dtype=torch.int32, device=dev)
+    o = torch.empty_like(d["v"])
+    o_r = torch.empty_like(dr["v"])
+    h_new = torch.empty_like(d["h0"])
+
+    def vstep(i):
+        kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], h0=d["h0"],
+                          cu_seqlens=d["cu_seqlens"], o=o, store_state=False)
+
+    def rstep(i):
+        kda.kda_chunk_fwd(dr["q"], dr["k"], dr["v"], dr["log_alpha"], dr["beta"], h0=d["h0"],
+                          cu_seqlens=dr["cu_seqlens"], o=o_r, h_T=h_new)
+
+    _, vms = time_launches(vstep, steps, warmup, stream)
+    _, rms = time_launches(rstep, steps, warmup, stream)
+    v_ms, r_ms = sum(vms) / len(vms), sum(rms) / len(rms)
+    state = B * H * D * D * 4
+    out = {"requests": B, "H": H, "draft_tokens": draft, "accepted": acc,
+           "verify_ms": round(v_ms, 4), "replay_ms": round(r_ms, 4),
+           "verify_state_read_GBps": round(state / (v_ms * 1e-3) / 1e9, 1),
+           "replay_state_GBps": round(2 * state / (r_ms * 1e-3) / 1e9, 1)}
+    del d, dr, o, o_r, h_new
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -275,8 +313,32 @@ def main():
                  "frac_of_bf16_peak": round(mfma_frac, 4)},
         "kernel_source_hash": src_hash,
     }
+    # ---------------- prefix snapshots every 512 tokens (same workload) ----------------
+    if not args.no_extra:
+        snap_cu, n_snap = kda.snapshot_index(None, T, 512)
+        snap = torch.empty((n_snap, H, D, D), dtype=torch.float32, device=dev)
+
+        def sstep(i):
+            d = sets[i % 2]
+            kda.kda_chunk_fwd_snap(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"],
+                                   interval=512, o=o, h_T=hT, snap=snap, snap_cu=snap_cu,
+                                   n_snap=n_snap)
+
+        _, sms = time_launches(sstep, args.steps, args.warmup, stream)
+        savg = sum(sms) / len(sms)
+        sbytes = nbytes + n_snap * H * D * D * 4
+        out["snapshots"] = {"interval": 512, "entries": n_snap, "kernel_ms": round(savg, 5),
+                            "overhead_vs_plain": round(savg / avg_ms - 1.0, 4),
+                            "algorithmic_bytes": sbytes,
+                            "hbm_frac": round(sbytes / (savg * 1e-3) / (HBM_PEAK_GBS * 1e9), 4)}
+        del snap
     del sets
     torch.cuda.empty_cache()
+
+    # ---------------- speculative verify + replay, 256 requests ----------------
+    if not args.no_extra and not args.no_decode:
+        out["verify_replay"] = verify_replay(torch, kda, kda_inputs, dev, stream, args.steps,
+                                             args.warmup)
 
     # ---------------- decode: 256 x 96 states, one token ----------------
     if not args.no_decode:
@@ -307,6 +369,11 @@ def main():
         }
         del dd
         torch.cuda.empty_cache()
+
+    if "verify_replay" in out and "decode" in out:
+        vr = out["verify_replay"]
+        vr["vs_7_decode_steps"] = round(
+            7 * out["decode"]["ms_per_step"] / (vr["verify_ms"] + vr["replay_ms"]), 2)
 
     # measured streaming ceiling: fractions against it beside the 8 TB/s peak
     cbw = copy_bandwidth(torch, dev, stream)

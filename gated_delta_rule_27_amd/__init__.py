@@ -9,6 +9,9 @@ Functions (same names as the C entry points):
 
 * ``kda_chunk_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, ...)``
   -> ``(o, h_T)``  chunkwise prefill over packed sequences;
+* ``kda_chunk_fwd_snap(..., interval=512)`` -> ``(o, h_T, snap, snap_cu)``
+  the same, plus prefix snapshots of the state (``snapshot_index`` gives
+  their layout);
 * ``kda_decode_step(q, k, v, log_alpha, beta, S)`` -> ``o``  one recurrent
   step, ``S`` updated in place;
 * ``kda_chunk_fwd_workspace_size``, ``kda_status_str``, ``kda_abi_version``.
@@ -55,6 +58,9 @@ def lib():
         L.kda_chunk_fwd_ex.restype = ctypes.c_int
         L.kda_chunk_fwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
                                        ctypes.c_int, vp, vp, vp, sz, i32, i32, vp]
+        L.kda_chunk_fwd_snap.restype = ctypes.c_int
+        L.kda_chunk_fwd_snap.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
+                                         ctypes.c_int, vp, vp, i32, vp, i64, vp, vp, sz, vp]
         L.kda_decode_step.restype = ctypes.c_int
         L.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                       ctypes.c_int, vp, vp]
@@ -165,6 +171,72 @@ def kda_chunk_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, chunk=0
     return o, h_T
 
 
+def snapshot_index(cu_seqlens, T_total, interval):
+    """Layout of the prefix snapshots of kda_chunk_fwd_snap: returns
+    (snap_cu, n_snap).  snap_cu is the int32 device tensor [N+1] with
+    snap_cu[n] = sum over m < n of floor(len_m / interval) (None for one
+    sequence, whose entries start at 0); sequence n's snapshot after
+    j * interval tokens is entry snap_cu[n] + j - 1.  n_snap needs one
+    device-to-host read when cu_seqlens is given."""
+    torch = _torch()
+    interval = int(interval)
+    if interval <= 0:
+        raise ValueError("interval must be positive")
+    if cu_seqlens is None:
+        return None, int(T_total) // interval
+    cu = cu_seqlens.to(torch.int64)
+    counts = (cu[1:] - cu[:-1]) // interval
+    snap_cu = torch.zeros(cu.numel(), dtype=torch.int64, device=cu.device)
+    snap_cu[1:] = torch.cumsum(counts, 0)
+    return snap_cu.to(torch.int32), int(snap_cu[-1].item())
+
+
+def kda_chunk_fwd_snap(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, interval,
+                       o=None, h_T=None, snap=None, snap_cu=None, n_snap=None,
+                       store_state=True):
+    """kda_chunk_fwd that also writes the state of every sequence after each
+    multiple of `interval` tokens (a multiple of 16) to `snap`
+    [n_snap, H, 128, 128] fp32, laid out as snapshot_index describes.
+    Returns (o, h_T, snap, snap_cu)."""
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("beta", beta)):
+        _dev(t, name, q.dtype)
+    dt = _dtype_code(q)
+    T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if k.shape != q.shape or log_alpha.shape != q.shape or v.shape[:2] != (T, H) \
+            or tuple(beta.shape) != (T, H):
+        raise ValueError("inconsistent shapes")
+    N = 1
+    if cu_seqlens is not None:
+        _dev(cu_seqlens, "cu_seqlens", torch.int32)
+        N = cu_seqlens.numel() - 1
+    _dev(h0, "h0", torch.float32)
+    if h0 is not None and tuple(h0.shape) != (N, H, Dk, Dv):
+        raise ValueError("h0 must be [N, H, Dk, Dv]")
+    if n_snap is None:
+        snap_cu, n_snap = snapshot_index(cu_seqlens, T, interval)
+    _dev(snap_cu, "snap_cu", torch.int32)
+    if snap is None:
+        snap = torch.empty((n_snap, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    _dev(snap, "snap", torch.float32)
+    if o is None:
+        o = torch.empty((T, H, Dv), dtype=q.dtype, device=q.device)
+    _dev(o, "o", q.dtype)
+    if store_state and h_T is None:
+        h_T = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    if not store_state:
+        h_T = None
+    _dev(h_T, "h_T", torch.float32)
+    ws_bytes = kda_chunk_fwd_workspace_size(T, N, H, Dk, Dv, dt)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    _check(lib().kda_chunk_fwd_snap(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0), _ptr(cu_seqlens),
+        N, T, H, Dk, Dv, dt, _ptr(o), _ptr(h_T), int(interval), _ptr(snap_cu), int(n_snap),
+        _ptr(snap), _ptr(ws), ws_bytes, _stream(q.device)))
+    return o, h_T, snap, snap_cu
+
+
 def kda_decode_step(q, k, v, log_alpha, beta, S, *, o=None):
     """One recurrent KDA step for B sequences; S [B, H, 128, 128] fp32 is
     updated in place.  q, k, log_alpha, v: [B, H, 128]; beta: [B, H].
@@ -188,5 +260,6 @@ def kda_decode_step(q, k, v, log_alpha, beta, S, *, o=None):
     return o
 
 
-__all__ = ["kda_chunk_fwd", "kda_decode_step", "kda_chunk_fwd_workspace_size",
-           "kda_status_str", "kda_abi_version", "KDAError", "lib", "LIB_PATH"]
+__all__ = ["kda_chunk_fwd", "kda_chunk_fwd_snap", "snapshot_index", "kda_decode_step",
+           "kda_chunk_fwd_workspace_size", "kda_status_str", "kda_abi_version", "KDAError",
+           "lib", "LIB_PATH"]

@@ -77,12 +77,22 @@ size_t kda_chunk_fwd_workspace_size(int64_t T_total, int32_t N, int32_t H, int32
     return 0;  // the fused chunk kernel keeps every intermediate on chip
 }
 
-kda_status kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* log_alpha,
-                            const void* beta, const float* h0, const int32_t* cu_seqlens,
-                            int32_t N, int64_t T_total, int32_t H, int32_t Dk, int32_t Dv,
-                            kda_dtype dt, void* o, float* h_T, void* workspace,
-                            size_t workspace_bytes, int32_t chunk, int32_t dv_split,
-                            hipStream_t stream) {
+namespace {
+
+// Prefix snapshots requested by kda_chunk_fwd_snap (interval 0 = none).
+struct SnapReq {
+    int32_t interval = 0;
+    const int32_t* snap_cu = nullptr;
+    int64_t n_snap = 0;
+    float* snap = nullptr;
+};
+
+kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const void* log_alpha,
+                          const void* beta, const float* h0, const int32_t* cu_seqlens,
+                          int32_t N, int64_t T_total, int32_t H, int32_t Dk, int32_t Dv,
+                          kda_dtype dt, void* o, float* h_T, void* workspace,
+                          size_t workspace_bytes, int32_t chunk, int32_t dv_split,
+                          const SnapReq& sr, hipStream_t stream) {
     if (!valid_dtype(dt)) return KDA_ERR_BAD_DTYPE;
     if (N < 1 || T_total < 0 || H < 1 || H > KDA_MAX_HEADS || Dk != kda::kHeadDim ||
         Dv != kda::kHeadDim)
@@ -94,8 +104,17 @@ kda_status kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const v
         return KDA_ERR_BAD_SHAPE;
     if (chunk != 0 && chunk != 16 && chunk != 32) return KDA_ERR_BAD_SHAPE;
     if (dv_split != 0 && dv_split != 1 && dv_split != 2 && dv_split != 4) return KDA_ERR_BAD_SHAPE;
+    if (sr.interval != 0) {
+        if (sr.interval < 0 || sr.interval % kda::kSnapUnit != 0 || sr.n_snap < 0)
+            return KDA_ERR_BAD_SHAPE;
+        const uint64_t per = (uint64_t)H * kda::kHeadDim * kda::kHeadDim;
+        if ((uint64_t)sr.n_snap > kMaxElems / per) return KDA_ERR_BAD_SHAPE;
+    }
 
     if (T_total > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERR_NULL_ARG;
+    if (sr.n_snap > 0 && (!sr.snap || (N > 1 && !sr.snap_cu))) return KDA_ERR_NULL_ARG;
+    if (sr.snap && !aligned(sr.snap, 16)) return KDA_ERR_MISALIGNED;
+    if (sr.snap_cu && !aligned(sr.snap_cu, 4)) return KDA_ERR_MISALIGNED;
 
     for (const void* p : {q, k, v, log_alpha, (const void*)h0, (const void*)o,
                           (const void*)h_T, (const void*)workspace})
@@ -113,8 +132,12 @@ kda_status kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const v
                scu = span(cu_seqlens, cu_seqlens ? (uint64_t)(N + 1) * 4 : 0),
                so = span(o, nTok * es), shT = span(h_T, h_T ? nState * 4 : 0),
                sws = span(workspace, workspace_bytes);
-    if (overlaps_any(so, {sq, sk, sv, sg, sb, sh0, scu, sws})) return KDA_ERR_ALIAS;
-    if (overlaps_any(shT, {sq, sk, sv, sg, sb, sh0, scu, so, sws})) return KDA_ERR_ALIAS;
+    const Span ssn = span(sr.snap, sr.snap ? (uint64_t)sr.n_snap * (nState / N) * 4 : 0),
+               sscu = span(sr.snap_cu, sr.snap_cu ? (uint64_t)(N + 1) * 4 : 0);
+    if (overlaps_any(so, {sq, sk, sv, sg, sb, sh0, scu, sws, sscu})) return KDA_ERR_ALIAS;
+    if (overlaps_any(shT, {sq, sk, sv, sg, sb, sh0, scu, so, sws, sscu})) return KDA_ERR_ALIAS;
+    if (overlaps_any(ssn, {sq, sk, sv, sg, sb, sh0, scu, so, shT, sws, sscu}))
+        return KDA_ERR_ALIAS;
 
     const size_t need = kda_chunk_fwd_workspace_size(T_total, N, H, Dk, Dv, dt);
     if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
@@ -124,6 +147,7 @@ kda_status kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const v
     if (chunk) c = chunk;
     if (dv_split) s = dv_split;
     if (!kda::chunk_config_supported((int)dt, c, s)) return KDA_ERR_BAD_SHAPE;
+    if (sr.interval != 0 && sr.interval % c != 0) return KDA_ERR_BAD_SHAPE;
 
     kda::ChunkArgs a;
     a.q = q;
@@ -138,8 +162,42 @@ kda_status kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const v
     a.H = H;
     a.o = o;
     a.h_T = h_T;
+    a.snap.snap = sr.n_snap > 0 ? sr.snap : nullptr;
+    a.snap.snap_cu = sr.snap_cu;
+    a.snap.n_snap = sr.n_snap;
+    a.snap.every_chunks = sr.interval > 0 ? sr.interval / kda::kSnapUnit : 1;
     if (kda::launch_chunk(a, (int)dt, c, s, stream) != hipSuccess) return KDA_ERR_DEVICE;
     return KDA_OK;
+}
+
+}  // namespace
+
+kda_status kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* log_alpha,
+                            const void* beta, const float* h0, const int32_t* cu_seqlens,
+                            int32_t N, int64_t T_total, int32_t H, int32_t Dk, int32_t Dv,
+                            kda_dtype dt, void* o, float* h_T, void* workspace,
+                            size_t workspace_bytes, int32_t chunk, int32_t dv_split,
+                            hipStream_t stream) {
+    return chunk_fwd_impl(q, k, v, log_alpha, beta, h0, cu_seqlens, N, T_total, H, Dk, Dv, dt,
+                          o, h_T, workspace, workspace_bytes, chunk, dv_split, SnapReq{},
+                          stream);
+}
+
+kda_status kda_chunk_fwd_snap(const void* q, const void* k, const void* v,
+                              const void* log_alpha, const void* beta, const float* h0,
+                              const int32_t* cu_seqlens, int32_t N, int64_t T_total, int32_t H,
+                              int32_t Dk, int32_t Dv, kda_dtype dt, void* o, float* h_T,
+                              int32_t interval, const int32_t* snap_cu, int64_t n_snap,
+                              float* snap, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+    if (interval <= 0) return KDA_ERR_BAD_SHAPE;
+    SnapReq sr;
+    sr.interval = interval;
+    sr.snap_cu = snap_cu;
+    sr.n_snap = n_snap;
+    sr.snap = snap;
+    return chunk_fwd_impl(q, k, v, log_alpha, beta, h0, cu_seqlens, N, T_total, H, Dk, Dv, dt,
+                          o, h_T, workspace, workspace_bytes, 0, 0, sr, stream);
 }
 
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* log_alpha,

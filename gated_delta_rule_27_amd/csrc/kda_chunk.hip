@@ -108,7 +108,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(
     const TIn* __restrict__ log_alpha, const TIn* __restrict__ beta,
     const float* __restrict__ h0, const int32_t* __restrict__ cu_seqlens,
     int64_t T_total, int32_t H, int32_t split, TIn* __restrict__ o,
-    float* __restrict__ h_T) {
+    float* __restrict__ h_T, SnapArgs snap) {
     typedef ChunkCfg<TIn, C, NW, NCT> K;
     typedef typename K::TOp TOp;
     constexpr bool kBF16 = sizeof(TOp) == 2;
@@ -508,6 +508,27 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(
                 }
             }
         }
+        // prefix snapshot after this chunk (uniform branch; rare).  C divides
+        // kSnapUnit * every_chunks (checked by the caller).
+        if (snap.snap && len == C) {
+            const int64_t done = t0 + C - bos;  // tokens of the sequence consumed
+            const int64_t every = (int64_t)kSnapUnit * snap.every_chunks;
+            if (done % every == 0) {
+                const int64_t idx = (snap.snap_cu ? (int64_t)snap.snap_cu[n] : 0) + done / every - 1;
+                if (idx < snap.n_snap) {
+                    float* dst = snap.snap + ((size_t)idx * (size_t)H + h) * (kHeadDim * kHeadDim);
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct) {
+                        const int j = col0 + 16 * (NCT * wave + ct) + l16;
+#pragma unroll
+                        for (int it = 0; it < 8; ++it)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                dst[(16 * it + 4 * g + e) * kHeadDim + j] = S[ct][it][e];
+                    }
+                }
+            }
+        }
         __syncthreads();
     }
 
@@ -536,7 +557,8 @@ hipError_t launch(const ChunkArgs& a, hipStream_t stream) {
     if (nwg == 0) return hipSuccess;
     kern<<<dim3((unsigned)nwg), dim3(K::NT), K::bytes, stream>>>(
         (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, (const TIn*)a.log_alpha,
-        (const TIn*)a.beta, a.h0, a.cu_seqlens, a.T_total, a.H, split, (TIn*)a.o, a.h_T);
+        (const TIn*)a.beta, a.h0, a.cu_seqlens, a.T_total, a.H, split, (TIn*)a.o, a.h_T,
+        a.snap);
     return hipGetLastError();
 }
 

@@ -82,6 +82,7 @@ struct WsCfg {
     static constexpr size_t bytes = T0 + 2 * szTile;
 
     static_assert(bytes <= 160 * 1024, "LDS budget");
+    static_assert(kWsC == kSnapUnit, "snapshots fall on chunk ends");
 };
 
 template <int NCT, int NSW, int PD>
@@ -89,7 +90,8 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ log_alpha, const bf16* __restrict__ beta,
     const float* __restrict__ h0, const int32_t* __restrict__ cu_seqlens, int64_t T_total,
-    int32_t H, int32_t split, int32_t units, bf16* __restrict__ o, float* __restrict__ h_T) {
+    int32_t H, int32_t split, int32_t units, bf16* __restrict__ o, float* __restrict__ h_T,
+    SnapArgs snap) {
     typedef WsCfg<NCT, NSW, PD> K;
     constexpr int KP = K::KP, TP = K::TP, AP = K::AP, DV = K::DV;
 
@@ -201,8 +203,9 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
         // every chunk issues the same loads and stores without branches.  The
         // prefetch distance keeps the memory-counter wait for a chunk's V
         // clear of the output stores of the iterations just before it.
-        const uint32_t vo_lane = (uint32_t)(
-            ((size_t)(4 * g) * rowstride + headoff + col0 + 16 * NCT * wave + l16) * 2);
+        const int colw0 = col0 + 16 * NCT * wave + l16;  // this lane's first column
+        const int64_t snap_base = snap.snap_cu ? (int64_t)snap.snap_cu[n] : 0;
+        const uint32_t vo_lane = (uint32_t)(((size_t)(4 * g) * rowstride + headoff + colw0) * 2);
         const uint32_t vo_row = (uint32_t)(rowstride * 2);
         auto rows_rsrc = [&](const bf16* base, int y) {
             const int64_t rows = (y >= 0 && y < nch) ? seqlen - (int64_t)kWsC * y : 0;
@@ -271,6 +274,22 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
 #pragma unroll
                     for (int ct = 0; ct < NCT; ++ct)
                         S[ct][it] = mma_bf16_k16(a, ub[ct], S[ct][it] * gm);
+                }
+                // prefix snapshot after chunk c (uniform branch; rare)
+                if (snap.snap && (c + 1) % snap.every_chunks == 0 &&
+                    (int64_t)kWsC * (c + 1) <= seqlen) {
+                    const int64_t idx = snap_base + (c + 1) / snap.every_chunks - 1;
+                    if (idx < snap.n_snap) {
+                        float* dst = snap.snap + ((size_t)idx * (size_t)H + h) * (kHeadDim * kHeadDim);
+#pragma unroll
+                        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                            for (int it = 0; it < 8; ++it)
+#pragma unroll
+                                for (int e = 0; e < 4; ++e)
+                                    dst[(16 * it + 4 * g + e) * kHeadDim + colw0 + 16 * ct] =
+                                        S[ct][it][e];
+                    }
                 }
             }
             // the Gram tiles of chunk c+2 (read by the solve and by this
@@ -427,7 +446,7 @@ hipError_t launch_ws_t(const ChunkArgs& a, hipStream_t stream) {
     kern<<<dim3((unsigned)nwg), dim3(K::NT), K::bytes, stream>>>(
         (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.log_alpha,
         (const bf16*)a.beta, a.h0, a.cu_seqlens, a.T_total, a.H, split, (int32_t)units,
-        (bf16*)a.o, a.h_T);
+        (bf16*)a.o, a.h_T, a.snap);
     return hipGetLastError();
 }
 

@@ -9,6 +9,18 @@
 namespace kda {
 
 constexpr int kHeadDim = 128;  // d_k = d_v of the K3 KDA head
+constexpr int kSnapUnit = 16;  // prefix-snapshot intervals are multiples of this
+
+// Prefix snapshots: the state after every `every_chunks` units of kSnapUnit
+// tokens of a sequence, i.e. after j * kSnapUnit * every_chunks tokens (j = 1, 2, ...), goes to
+// snap[(base_n + j - 1), h] with base_n = snap_cu[n] (0 without snap_cu);
+// indices at or past n_snap are not written.  snap == nullptr disables them.
+struct SnapArgs {
+    float* snap;              // [n_snap, H, 128, 128] fp32
+    const int32_t* snap_cu;   // device [N + 1], may be null (one sequence)
+    int64_t n_snap;
+    int32_t every_chunks;     // >= 1
+};
 
 struct ChunkArgs {
     const void* q;
@@ -23,6 +35,7 @@ struct ChunkArgs {
     int32_t H;
     void* o;
     float* h_T;               // may be null
+    SnapArgs snap;            // snap.snap == nullptr: no snapshots
 };
 
 struct DecodeArgs {

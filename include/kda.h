@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 #define KDA_MAX_HEADS 65536
 
@@ -134,6 +134,40 @@ kda_status kda_chunk_fwd_ex(const void* q, const void* k, const void* v,
                             void* workspace, size_t workspace_bytes,
                             int32_t chunk, int32_t dv_split,
                             hipStream_t stream);
+
+/*
+ * kda_chunk_fwd that also writes prefix snapshots of the state, for a prefix
+ * cache: sparse KDA snapshots stored only at token boundaries on a fixed
+ * grid (512-token hash boundaries on the pages, "From GPT-2 to Kimi K3",
+ * "Serving a hybrid cache").
+ *
+ *   interval : a positive multiple of 16 tokens (KDA_ERR_BAD_SHAPE otherwise)
+ *   snap_cu  : [N + 1] int32 device, snap_cu[n] = sum over m < n of
+ *              floor(len_m / interval) with len_m = cu_seqlens[m+1] -
+ *              cu_seqlens[m]; may be NULL only for N == 1 (base 0)
+ *   n_snap   : entries of snap (snap_cu[N] when it is consistent)
+ *   snap     : [n_snap, H, Dk, Dv] fp32, 16-byte aligned, written: entry
+ *              snap_cu[n] + j - 1 = the state of sequence n after its first
+ *              j * interval tokens, j = 1 .. floor(len_n / interval)
+ *
+ * Entries at or past n_snap are never written, whatever snap_cu holds.  A
+ * snapshot is meant to be read-only: restoring one (h0 = a snapshot entry in
+ * kda_chunk_fwd, or a copy as the in-place S of kda_decode_step) resumes the
+ * recurrence from that boundary, and replaying only the accepted prefix of a
+ * speculative draft from the pre-draft state is the same call with T = the
+ * accepted tokens ("Speculative decoding cannot naively roll KDA back").
+ * Errors as kda_chunk_fwd, plus: n_snap > 0 with snap NULL, or with N > 1
+ * and snap_cu NULL, is KDA_ERR_NULL_ARG; snap overlapping any other buffer
+ * is KDA_ERR_ALIAS.
+ */
+kda_status kda_chunk_fwd_snap(const void* q, const void* k, const void* v,
+                              const void* log_alpha, const void* beta,
+                              const float* h0, const int32_t* cu_seqlens,
+                              int32_t N, int64_t T_total, int32_t H, int32_t Dk,
+                              int32_t Dv, kda_dtype dt, void* o, float* h_T,
+                              int32_t interval, const int32_t* snap_cu,
+                              int64_t n_snap, float* snap, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
 
 /*
  * One recurrent step for B independent sequences (single-token cached

@@ -38,13 +38,14 @@ def declared_functions():
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert {"kda_chunk_fwd", "kda_chunk_fwd_ex", "kda_decode_step",
-            "kda_chunk_fwd_workspace_size", "kda_status_str", "kda_abi_version"} <= set(names)
+            "kda_chunk_fwd_workspace_size", "kda_status_str", "kda_abi_version",
+            "kda_chunk_fwd_snap"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_version_and_status_strings(L):
-    assert kda.kda_abi_version() == 1
+    assert kda.kda_abi_version() == 2
     for code in range(8):
         s = kda.kda_status_str(code)
         assert s.startswith("KDA_")
@@ -69,6 +70,49 @@ def chunk(L, **kw):
     return L.kda_chunk_fwd_ex(a["q"], a["k"], a["v"], a["g"], a["b"], a["h0"], a["cu"],
                               a["N"], a["T"], a["H"], a["Dk"], a["Dv"], a["dt"], a["o"],
                               a["hT"], a["ws"], a["wsb"], a["chunk"], a["split"], a["stream"])
+
+
+def chunk_snap(L, **kw):
+    """kda_chunk_fwd_snap with fake pointers; every case below fails validation,
+    so nothing is launched."""
+    a = dict(q=P(0), k=P(1), v=P(2), g=P(3), b=P(4), h0=P(5), cu=P(6), N=1, T=64, H=2,
+             Dk=D, Dv=D, dt=BF16, o=P(7), hT=P(8), interval=512, scu=P(9), n_snap=4,
+             snap=P(10), ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return L.kda_chunk_fwd_snap(a["q"], a["k"], a["v"], a["g"], a["b"], a["h0"], a["cu"],
+                                a["N"], a["T"], a["H"], a["Dk"], a["Dv"], a["dt"], a["o"],
+                                a["hT"], a["interval"], a["scu"], a["n_snap"], a["snap"],
+                                a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(interval=0), BAD_SHAPE),
+    (dict(interval=-16), BAD_SHAPE),
+    (dict(interval=100), BAD_SHAPE),          # not a multiple of 16
+    (dict(n_snap=-1), BAD_SHAPE),
+    (dict(Dk=64), BAD_SHAPE),                 # the chunk checks still apply
+    (dict(snap=None), NULL_ARG),              # n_snap > 0 needs the buffer
+    (dict(N=2, scu=None), NULL_ARG),          # several sequences need snap_cu
+    (dict(snap=P(10, 4)), MISALIGNED),
+    (dict(scu=P(9, 2)), MISALIGNED),
+    (dict(snap=P(0)), ALIAS),                 # snapshots on q
+    (dict(snap=P(8)), ALIAS),                 # snapshots on h_T
+    (dict(snap=P(5)), ALIAS),                 # snapshots on h0
+    (dict(o=P(9)), ALIAS),                    # o on snap_cu
+    (dict(snap=P(9)), ALIAS),                 # snapshots on snap_cu
+])
+def test_snapshot_argument_errors(L, kw, code):
+    assert chunk_snap(L, **kw) == code
+
+
+def test_snapshot_layout_helper():
+    import torch
+    cu = torch.tensor([0, 100, 1100, 1137, 1649, 3185], dtype=torch.int32)
+    snap_cu, n = kda.snapshot_index(cu, 3185, 512)
+    assert snap_cu.tolist() == [0, 0, 1, 1, 2, 5] and n == 5
+    assert kda.snapshot_index(None, 1100, 512) == (None, 2)
+    with pytest.raises(ValueError):
+        kda.snapshot_index(None, 10, 0)
 
 
 def decode(L, **kw):
