@@ -192,39 +192,57 @@ def extra_prefill(torch, kda, kda_inputs, dev, stream, cfg_id, steps, warmup):
 
 
 def verify_replay(torch, kda, kda_inputs, dev, stream, steps, warmup):
-    """Batched speculative decoding on the chunk path: 256 requests x 96
-    heads, each with its cached fp32 state; a 7-token draft is verified in
-    one call (outputs only), then the 4 accepted tokens are replayed from the
-    same states in a second call that writes the new states.  Compared with
-    7 single-token decode steps, which read and write every state 7 times."""
+    """Batched speculative decoding: 256 requests x 96 heads, each with its
+    cached fp32 state; a 7-token draft is verified (outputs only, state
+    untouched), then the 4 accepted tokens are replayed from the same states
+    (new states written).  Measured with the multi-token recurrent kernel
+    (kda_decode_multi) and, for comparison, with the chunk path; 7
+    single-token decode steps would read and write every state 7 times."""
     B, H, draft, acc = 256, 96, 7, 4
     d = kda_inputs.prefill_inputs(B * draft, H, dtype="bf16", device=dev, seed=1005,
                                   lengths=[draft] * B, h0_std=0.02)
-    # the accepted tokens: the first `acc` of every request's draft
-    dr = {x: d[x].view(B, draft, *d[x].shape[1:])[:, :acc].reshape(B * acc, *d[x].shape[1:])
-          .contiguous() for x in ("q", "k", "v", "log_alpha", "beta")}
+    names = ("q", "k", "v", "log_alpha", "beta")
+    w = {x: d[x].view(B, draft, *d[x].shape[1:]) for x in names}
+    n_acc = torch.full((B,), acc, dtype=torch.int32, device=dev)
+    S_new = d["h0"].clone()
+    o = torch.empty((B, draft, H, D), dtype=torch.bfloat16, device=dev)
+
+    def mverify(i):
+        kda.kda_decode_multi(*[w[x] for x in names], d["h0"], update_state=False, o=o)
+
+    def mreplay(i):
+        # each timed replay updates S_new again: the same work every time
+        kda.kda_decode_multi(*[w[x] for x in names], S_new, n_acc, update_state=True, o=o)
+
+    # chunk path: accepted tokens packed as sequences of `acc`
+    dr = {x: w[x][:, :acc].reshape(B * acc, *d[x].shape[1:]).contiguous() for x in names}
     dr["cu_seqlens"] = torch.arange(0, B * acc + 1, acc, dtype=torch.int32, device=dev)
-    o = torch.empty_like(d["v"])
-    o_r = torch.empty_like(dr["v"])
+    oc = torch.empty_like(d["v"])
+    oc_r = torch.empty_like(dr["v"])
     h_new = torch.empty_like(d["h0"])
 
-    def vstep(i):
-        kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], h0=d["h0"],
-                          cu_seqlens=d["cu_seqlens"], o=o, store_state=False)
+    def cverify(i):
+        kda.kda_chunk_fwd(*[d[x] for x in names], h0=d["h0"], cu_seqlens=d["cu_seqlens"],
+                          o=oc, store_state=False)
 
-    def rstep(i):
-        kda.kda_chunk_fwd(dr["q"], dr["k"], dr["v"], dr["log_alpha"], dr["beta"], h0=d["h0"],
-                          cu_seqlens=dr["cu_seqlens"], o=o_r, h_T=h_new)
+    def creplay(i):
+        kda.kda_chunk_fwd(*[dr[x] for x in names], h0=d["h0"], cu_seqlens=dr["cu_seqlens"],
+                          o=oc_r, h_T=h_new)
 
-    _, vms = time_launches(vstep, steps, warmup, stream)
-    _, rms = time_launches(rstep, steps, warmup, stream)
-    v_ms, r_ms = sum(vms) / len(vms), sum(rms) / len(rms)
+    res = {}
+    for name, fn in (("multi_verify", mverify), ("multi_replay", mreplay),
+                     ("chunk_verify", cverify), ("chunk_replay", creplay)):
+        _, ms = time_launches(fn, steps, warmup, stream)
+        res[name] = sum(ms) / len(ms)
     state = B * H * D * D * 4
     out = {"requests": B, "H": H, "draft_tokens": draft, "accepted": acc,
-           "verify_ms": round(v_ms, 4), "replay_ms": round(r_ms, 4),
-           "verify_state_read_GBps": round(state / (v_ms * 1e-3) / 1e9, 1),
-           "replay_state_GBps": round(2 * state / (r_ms * 1e-3) / 1e9, 1)}
-    del d, dr, o, o_r, h_new
+           "kernel": "kda::decode_multi_kernel",
+           "verify_ms": round(res["multi_verify"], 4), "replay_ms": round(res["multi_replay"], 4),
+           "verify_state_read_GBps": round(state / (res["multi_verify"] * 1e-3) / 1e9, 1),
+           "replay_state_GBps": round(2 * state / (res["multi_replay"] * 1e-3) / 1e9, 1),
+           "chunk_path_verify_ms": round(res["chunk_verify"], 4),
+           "chunk_path_replay_ms": round(res["chunk_replay"], 4)}
+    del d, w, dr, o, oc, oc_r, h_new, S_new
     torch.cuda.empty_cache()
     return out
 

@@ -14,6 +14,9 @@ Functions (same names as the C entry points):
   their layout);
 * ``kda_decode_step(q, k, v, log_alpha, beta, S)`` -> ``o``  one recurrent
   step, ``S`` updated in place;
+* ``kda_decode_multi(q, k, v, log_alpha, beta, S, n_tok)`` -> ``o``  up to K
+  steps per sequence in one pass over the states (speculative verify /
+  replay);
 * ``kda_chunk_fwd_workspace_size``, ``kda_status_str``, ``kda_abi_version``.
 """
 import ctypes
@@ -64,6 +67,9 @@ def lib():
         L.kda_decode_step.restype = ctypes.c_int
         L.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                       ctypes.c_int, vp, vp]
+        L.kda_decode_multi.restype = ctypes.c_int
+        L.kda_decode_multi.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                       ctypes.c_int, i32, vp, vp]
         _lib = L
     return _lib
 
@@ -260,6 +266,37 @@ def kda_decode_step(q, k, v, log_alpha, beta, S, *, o=None):
     return o
 
 
+def kda_decode_multi(q, k, v, log_alpha, beta, S, n_tok=None, *, update_state=True, o=None):
+    """Up to K recurrent KDA steps for B sequences in one pass over their
+    states.  q, k, log_alpha, v: [B, K, H, 128]; beta: [B, K, H]; S
+    [B, H, 128, 128] fp32, written back in place iff update_state; n_tok:
+    int32 [B] device (tokens applied per sequence, clamped to [0, K]) or
+    None (all K).  Returns o [B, K, H, 128] (rows past n_tok[b] untouched)."""
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("beta", beta)):
+        _dev(t, name, q.dtype)
+    _dev(S, "S", torch.float32)
+    _dev(n_tok, "n_tok", torch.int32)
+    dt = _dtype_code(q)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, K, H, D]")
+    B, K, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if k.shape != q.shape or log_alpha.shape != q.shape or v.shape[:3] != (B, K, H) \
+            or tuple(beta.shape) != (B, K, H) or tuple(S.shape) != (B, H, Dk, Dv):
+        raise ValueError("inconsistent shapes")
+    if n_tok is not None and tuple(n_tok.shape) != (B,):
+        raise ValueError("n_tok must be [B]")
+    if o is None:
+        o = torch.empty((B, K, H, Dv), dtype=q.dtype, device=q.device)
+    _dev(o, "o", q.dtype)
+    _check(lib().kda_decode_multi(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S), _ptr(n_tok),
+        B, K, H, Dk, Dv, dt, 1 if update_state else 0, _ptr(o), _stream(q.device)))
+    return o
+
+
 __all__ = ["kda_chunk_fwd", "kda_chunk_fwd_snap", "snapshot_index", "kda_decode_step",
+           "kda_decode_multi",
            "kda_chunk_fwd_workspace_size", "kda_status_str", "kda_abi_version", "KDAError",
            "lib", "LIB_PATH"]

@@ -244,4 +244,50 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const vo
     return KDA_OK;
 }
 
+kda_status kda_decode_multi(const void* q, const void* k, const void* v, const void* log_alpha,
+                            const void* beta, float* S, const int32_t* n_tok, int32_t B,
+                            int32_t K, int32_t H, int32_t Dk, int32_t Dv, kda_dtype dt,
+                            int32_t update_state, void* o, hipStream_t stream) {
+    if (!valid_dtype(dt)) return KDA_ERR_BAD_DTYPE;
+    if (B < 0 || K < 1 || H < 1 || H > KDA_MAX_HEADS || Dk != kda::kHeadDim ||
+        Dv != kda::kHeadDim)
+        return KDA_ERR_BAD_SHAPE;
+    if ((uint64_t)B * (uint64_t)H > (uint64_t)std::numeric_limits<int32_t>::max())
+        return KDA_ERR_BAD_SHAPE;
+    if ((uint64_t)B * (uint64_t)K * (uint64_t)H > kMaxElems / kda::kHeadDim)
+        return KDA_ERR_BAD_SHAPE;
+    if (B > 0 && (!q || !k || !v || !log_alpha || !beta || !S || !o)) return KDA_ERR_NULL_ARG;
+    for (const void* p : {q, k, v, log_alpha, (const void*)S, (const void*)o})
+        if (p && !aligned(p, 16)) return KDA_ERR_MISALIGNED;
+    if (beta && !aligned(beta, esize(dt))) return KDA_ERR_MISALIGNED;
+    if (n_tok && !aligned(n_tok, 4)) return KDA_ERR_MISALIGNED;
+
+    const uint64_t es = esize(dt);
+    const uint64_t nVec = (uint64_t)B * K * H * kda::kHeadDim;
+    const uint64_t nState = (uint64_t)B * H * kda::kHeadDim * kda::kHeadDim;
+    const Span sq = span(q, nVec * es), sk = span(k, nVec * es), sv = span(v, nVec * es),
+               sg = span(log_alpha, nVec * es), sb = span(beta, (uint64_t)B * K * H * es),
+               sS = span(S, nState * 4), so = span(o, nVec * es),
+               sn = span(n_tok, n_tok ? (uint64_t)B * 4 : 0);
+    if (overlaps_any(so, {sq, sk, sv, sg, sb, sS, sn})) return KDA_ERR_ALIAS;
+    if (overlaps_any(sS, {sq, sk, sv, sg, sb, sn})) return KDA_ERR_ALIAS;
+    if (B == 0) return KDA_OK;
+
+    kda::DecodeMultiArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.log_alpha = log_alpha;
+    a.beta = beta;
+    a.S = S;
+    a.n_tok = n_tok;
+    a.B = B;
+    a.K = K;
+    a.H = H;
+    a.update_state = update_state ? 1 : 0;
+    a.o = o;
+    if (kda::launch_decode_multi(a, (int)dt, stream) != hipSuccess) return KDA_ERR_DEVICE;
+    return KDA_OK;
+}
+
 }  // extern "C"

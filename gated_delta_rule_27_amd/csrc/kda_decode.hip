@@ -156,6 +156,180 @@ __global__ __launch_bounds__(256 * NS) void decode_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Up to K recurrent steps per sequence in one pass over its state: the state
+// is read once, stays in registers across the tokens, and is written back
+// only when update_state is set (a speculative draft is verified without
+// touching the cached state, and the accepted prefix replayed on chip:
+// "From GPT-2 to Kimi K3", "Speculative decoding cannot naively roll KDA
+// back").  Same thread mapping as decode_kernel; per token the small vectors
+// go to an LDS buffer chosen by the token's parity, so one token's reads and
+// the next token's writes never meet, and three barriers order each step.
+// Token t of sequence b is applied only for t < n_b (n_tok[b] clamped to
+// [0, K]); later tokens become exact no-ops (alpha = 1, beta = 0, k = 0) and
+// write no output.
+template <typename TIn, int NS>
+__global__ __launch_bounds__(256 * NS) void decode_multi_kernel(
+    const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
+    const TIn* __restrict__ log_alpha, const TIn* __restrict__ beta,
+    float* __restrict__ S, const int32_t* __restrict__ n_tok, TIn* __restrict__ o,
+    int32_t units, int32_t H, int32_t K, int32_t update_state) {
+    constexpr int kWaves = 4 * NS;
+    constexpr int kRowStep = 8 * NS;
+    constexpr int kLoadsPerState = kStateLoads / NS;
+    static_assert(kRowStep * kLoadsPerState == kHeadDim, "a state is 128 rows");
+
+    const int t = threadIdx.x;
+    const int cg = t & 31;
+    const int rg = t >> 5;
+    const int first = NS * blockIdx.x;
+    const int nvalid = min(NS, units - first);
+
+    __shared__ float sk[2][NS][kHeadDim], sq[2][NS][kHeadDim], sa[2][NS][kHeadDim],
+        sv[2][NS][kHeadDim];
+    __shared__ float skq[2][NS][2];
+    __shared__ float su[NS][kHeadDim];
+    __shared__ floatx4 sred[kWaves][NS][2][kHeadDim / 4];
+
+    // tokens to apply for each state of the block (uniform)
+    int nt[NS];
+    int tmax = 0;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        int c = 0;
+        if (s < nvalid) {
+            const int b = (first + s) / H;
+            c = n_tok ? n_tok[b] : K;
+            c = c < 0 ? 0 : (c > K ? K : c);
+        }
+        nt[s] = __builtin_amdgcn_readfirstlane(c);
+        tmax = max(tmax, nt[s]);
+    }
+
+    // thread t serves the per-token vectors of state t / 256 (as in decode)
+    const int ms = t >> 8;
+    const int j = t & 255;
+    const int jc = j & (kHeadDim - 1);
+    const bool kside = j < kHeadDim;
+    const int unit_v = first + min(ms, nvalid - 1);
+    const size_t bv = (size_t)(unit_v / H) * K;   // first token row of the sequence
+    const size_t hv = (size_t)(unit_v % H);
+    auto tok_off = [&](int tt) { return ((bv + tt) * (size_t)H + hv) * kHeadDim; };
+    auto tok_beta = [&](int tt) { return (bv + tt) * (size_t)H + hv; };
+    int nt_ms = nt[0];
+#pragma unroll
+    for (int s = 1; s < NS; ++s) nt_ms = ms == s ? nt[s] : nt_ms;
+
+    // token 0's vectors first, then the state (its wait does not hold them back)
+    TIn r0, r1, r2, rb;
+    auto load_tok = [&](int tt) {
+        const int tc = tt < K ? tt : K - 1;   // always a valid token row
+        const size_t off = tok_off(tc);
+        r0 = (kside ? k : v)[off + jc];
+        r1 = q[off + jc];
+        r2 = log_alpha[off + jc];
+        rb = beta[tok_beta(tc)];
+    };
+    load_tok(0);
+
+    float* Sb = S + (size_t)first * (kHeadDim * kHeadDim);
+    floatx4 st[kStateLoads];
+#pragma unroll
+    for (int m = 0; m < kStateLoads; ++m) {
+        const int s = m / kLoadsPerState;
+        const int row = rg + kRowStep * m;
+        const int src = s < nvalid ? row : (row & (kHeadDim - 1));
+        st[m] = __builtin_nontemporal_load(
+            reinterpret_cast<const floatx4*>(Sb + src * kHeadDim + 4 * cg));
+    }
+
+    const int pr = (t >> 7) & 1;
+    const int col = t & (kHeadDim - 1);
+    const float* red = reinterpret_cast<const float*>(&sred[0][0][0][0]);
+
+    for (int tt = 0; tt < tmax; ++tt) {
+        const int par = tt & 1;
+        // this token's vectors to LDS; a token past the sequence's count is
+        // an exact no-op: alpha = 1, beta = 0, k = 0
+        const bool live = tt < nt_ms;
+        const float x0 = live ? to_f32(r0) : (kside ? 0.f : to_f32(r0));
+        const float x1 = to_f32(r1);
+        const float x2 = live ? to_f32(r2) : 0.f;
+        const float bcur = live ? to_f32(rb) : 0.f;
+        (kside ? sk[par][ms] : sv[par][ms])[jc] = x0;
+        sq[par][ms][jc] = x1;
+        sa[par][ms][jc] = expf(x2);
+        const float kq_part = wave_sum(x0 * x1);
+        if (kside && (j & 63) == 0) skq[par][ms][j >> 6] = kq_part;
+        // the next token's vectors are in flight during this token's work
+        load_tok(tt + 1);
+        __syncthreads();
+
+        // retain, partial recall p = S'^T k and read r = S'^T q
+        floatx4 p[NS], r[NS];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) p[s] = r[s] = zero4();
+#pragma unroll
+        for (int m = 0; m < kStateLoads; ++m) {
+            const int s = m / kLoadsPerState;
+            const int i = (rg + kRowStep * m) & (kHeadDim - 1);
+            st[m] *= sa[par][s][i];
+            p[s] += sk[par][s][i] * st[m];
+            r[s] += sq[par][s][i] * st[m];
+        }
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                p[s][c] += __shfl_xor(p[s][c], 32, 64);
+                r[s][c] += __shfl_xor(r[s][c], 32, 64);
+            }
+        }
+        if ((t & 32) == 0) {
+            const int w = t >> 6;
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                sred[w][s][0][cg] = p[s];
+                sred[w][s][1][cg] = r[s];
+            }
+        }
+        __syncthreads();
+
+        // column sums; the recall sums give u = beta (v - p)
+        float acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) acc += red[((w * NS + ms) * 2 + pr) * kHeadDim + col];
+        if (pr == 0) su[ms][col] = bcur * (sv[par][ms][col] - acc);
+        __syncthreads();
+
+        // read-out o = r + u (k . q)
+        if (pr == 1 && ms < nvalid && live) {
+            const float kq = skq[par][ms][0] + skq[par][ms][1];
+            o[tok_off(tt) + col] = from_f32<TIn>(acc + su[ms][col] * kq);
+        }
+        // erase + write: S = S' + k u^T
+        floatx4 uu[NS];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) uu[s] = *reinterpret_cast<const floatx4*>(&su[s][4 * cg]);
+#pragma unroll
+        for (int m = 0; m < kStateLoads; ++m) {
+            const int s = m / kLoadsPerState;
+            const int i = (rg + kRowStep * m) & (kHeadDim - 1);
+            st[m] += sk[par][s][i] * uu[s];
+        }
+    }
+
+    if (update_state) {
+#pragma unroll
+        for (int m = 0; m < kStateLoads; ++m) {
+            const int s = m / kLoadsPerState;
+            const int row = rg + kRowStep * m;
+            if (s < nvalid)
+                __builtin_nontemporal_store(st[m], reinterpret_cast<floatx4*>(Sb + row * kHeadDim + 4 * cg));
+        }
+    }
+}
+
 template <int NS>
 void launch_decode_ns(const DecodeArgs& a, int dtype, int32_t units, hipStream_t stream) {
     const dim3 grid((unsigned)((units + NS - 1) / NS)), block(256 * NS);
@@ -171,6 +345,25 @@ void launch_decode_ns(const DecodeArgs& a, int dtype, int32_t units, hipStream_t
 }
 
 }  // namespace
+
+hipError_t launch_decode_multi(const DecodeMultiArgs& a, int dtype, hipStream_t stream) {
+    const int64_t units = (int64_t)a.B * a.H;
+    if (units == 0) return hipSuccess;
+    constexpr int NS = kDecodeStates;
+    const dim3 grid((unsigned)((units + NS - 1) / NS)), block(256 * NS);
+    if (dtype == 0) {
+        decode_multi_kernel<float, NS><<<grid, block, 0, stream>>>(
+            (const float*)a.q, (const float*)a.k, (const float*)a.v, (const float*)a.log_alpha,
+            (const float*)a.beta, a.S, a.n_tok, (float*)a.o, (int32_t)units, a.H, a.K,
+            a.update_state);
+    } else {
+        decode_multi_kernel<bf16, NS><<<grid, block, 0, stream>>>(
+            (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.log_alpha,
+            (const bf16*)a.beta, a.S, a.n_tok, (bf16*)a.o, (int32_t)units, a.H, a.K,
+            a.update_state);
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream) {
     const int64_t units = (int64_t)a.B * a.H;

@@ -50,6 +50,21 @@ struct DecodeArgs {
     void* o;
 };
 
+struct DecodeMultiArgs {
+    const void* q;            // [B, K, H, 128]
+    const void* k;
+    const void* v;
+    const void* log_alpha;
+    const void* beta;         // [B, K, H]
+    float* S;                 // [B, H, 128, 128]
+    const int32_t* n_tok;     // device [B] or null (K for every sequence)
+    int32_t B;
+    int32_t K;
+    int32_t H;
+    int32_t update_state;
+    void* o;                  // [B, K, H, 128]
+};
+
 // dtype: 0 = fp32, 1 = bf16 (kda_dtype values).
 // chunk in {16, 32}; split = workgroups per head (value-column slices).
 // bf16 with chunk 16 and split 1 or 2 runs the wave-specialised pipelined
@@ -63,5 +78,6 @@ hipError_t launch_chunk(const ChunkArgs& a, int dtype, int chunk, int split,
                         hipStream_t stream);
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_decode_multi(const DecodeMultiArgs& a, int dtype, hipStream_t stream);
 
 }  // namespace kda

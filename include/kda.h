@@ -185,6 +185,35 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v,
                            int32_t B, int32_t H, int32_t Dk, int32_t Dv,
                            kda_dtype dt, void* o, hipStream_t stream);
 
+/*
+ * Up to K recurrent steps for each of B sequences in one pass over their
+ * states: a short window of tokens per cached sequence, such as a
+ * speculative draft.  Verifying a draft must not move the cached state, and
+ * after acceptance only the accepted updates are replayed, on chip, from
+ * the pre-draft state ("From GPT-2 to Kimi K3", "Speculative decoding
+ * cannot naively roll KDA back"); with update_state = 0 this call is the
+ * verify pass (outputs only), with update_state = 1 and n_tok = the accepted
+ * counts it is the replay.  Token t of sequence b gives exactly what t + 1
+ * calls of kda_decode_step would.
+ *
+ *   q, k, log_alpha : [B, K, H, Dk]  dt   (sequence-major, then token)
+ *   v               : [B, K, H, Dv]  dt
+ *   beta            : [B, K, H]      dt
+ *   S               : [B, H, Dk, Dv] fp32, read; written back (in place)
+ *                     iff update_state != 0
+ *   n_tok           : [B] int32 device, tokens to apply per sequence, clamped
+ *                     to [0, K] by the kernel; NULL = K for every sequence
+ *   o               : [B, K, H, Dv]  dt; rows t >= n_tok[b] are not written
+ * B == 0 is allowed (nothing is launched); K >= 1.  Alignment and errors as
+ * kda_decode_step (n_tok: 4-byte aligned; o overlapping S, n_tok or an
+ * input, or S overlapping an input or n_tok, is KDA_ERR_ALIAS).
+ */
+kda_status kda_decode_multi(const void* q, const void* k, const void* v,
+                            const void* log_alpha, const void* beta, float* S,
+                            const int32_t* n_tok, int32_t B, int32_t K, int32_t H,
+                            int32_t Dk, int32_t Dv, kda_dtype dt,
+                            int32_t update_state, void* o, hipStream_t stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* kda_status_str(kda_status s);
 

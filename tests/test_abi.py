@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert {"kda_chunk_fwd", "kda_chunk_fwd_ex", "kda_decode_step",
             "kda_chunk_fwd_workspace_size", "kda_status_str", "kda_abi_version",
-            "kda_chunk_fwd_snap"} <= set(names)
+            "kda_chunk_fwd_snap", "kda_decode_multi"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -113,6 +113,40 @@ def test_snapshot_layout_helper():
     assert kda.snapshot_index(None, 1100, 512) == (None, 2)
     with pytest.raises(ValueError):
         kda.snapshot_index(None, 10, 0)
+
+
+def decode_multi(L, **kw):
+    a = dict(q=P(0), k=P(1), v=P(2), g=P(3), b=P(4), S=P(5), n=P(6), B=4, K=7, H=2, Dk=D,
+             Dv=D, dt=BF16, upd=1, o=P(7), stream=None)
+    a.update(kw)
+    return L.kda_decode_multi(a["q"], a["k"], a["v"], a["g"], a["b"], a["S"], a["n"], a["B"],
+                              a["K"], a["H"], a["Dk"], a["Dv"], a["dt"], a["upd"], a["o"],
+                              a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=7), BAD_DTYPE),
+    (dict(K=0), BAD_SHAPE),
+    (dict(B=-1), BAD_SHAPE),
+    (dict(H=0), BAD_SHAPE),
+    (dict(Dv=64), BAD_SHAPE),
+    (dict(q=None), NULL_ARG),
+    (dict(S=None), NULL_ARG),
+    (dict(o=None), NULL_ARG),
+    (dict(q=P(0, 8)), MISALIGNED),
+    (dict(S=P(5, 4)), MISALIGNED),
+    (dict(n=P(6, 2)), MISALIGNED),
+    (dict(o=P(5)), ALIAS),              # o on S
+    (dict(o=P(6)), ALIAS),              # o on n_tok
+    (dict(S=P(0)), ALIAS),              # S on q
+    (dict(S=P(6)), ALIAS),              # S on n_tok
+])
+def test_decode_multi_argument_errors(L, kw, code):
+    assert decode_multi(L, **kw) == code
+
+
+def test_decode_multi_empty_batch_launches_nothing(L):
+    assert decode_multi(L, B=0, q=None, k=None, v=None, g=None, b=None, S=None, o=None) == OK
 
 
 def decode(L, **kw):
