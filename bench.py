@@ -247,6 +247,67 @@ def verify_replay(torch, kda, kda_inputs, dev, stream, steps, warmup):
     return out
 
 
+def context_parallel(torch, kda, kda_inputs, dev, stream, steps, warmup):
+    """One rank's share of KDA context parallelism for a 1M-token sequence
+    over 8 ranks: 131072 tokens x 96 heads, bf16.  The rank summarises its
+    segment (M and B: two prefill passes without outputs), the scan over the
+    8 summaries gives its incoming state (here the local summary stands in
+    for the 7 others, which would arrive by an all-gather), and a second
+    prefill pass from that state gives its outputs.  Timed beside one plain
+    prefill pass over the same share."""
+    T, H, R = 131072, 96, 8
+    d = kda_inputs.prefill_inputs(T, H, dtype="bf16", device=dev, seed=1006)
+    args = [d[x] for x in ("q", "k", "v", "log_alpha", "beta")]
+    o = torch.empty_like(d["v"])
+    hT = torch.empty((1, H, D, D), dtype=torch.float32, device=dev)
+    M, B = kda.kda_segment_summary(*args)
+    Mr = M.expand(R, H, D, D).contiguous()
+    Br = B.expand(R, H, D, D).contiguous()
+    S_in, S_fin = kda.kda_segment_scan(Mr, Br)
+    h_in = S_in[R - 1:R].contiguous()
+
+    def summary_B(i):
+        kda.kda_segment_summary(*args, want_M=False)
+
+    def summary_M(i):
+        kda.kda_segment_summary(*args, want_B=False)
+
+    def scan(i):
+        kda.kda_segment_scan(Mr, Br)
+
+    def pass2(i):
+        kda.kda_chunk_fwd(*args, h0=h_in, o=o, h_T=hT)
+
+    def plain(i):
+        kda.kda_chunk_fwd(*args, o=o, h_T=hT)
+
+    res = {}
+    for name, fn in (("summary_B", summary_B), ("summary_M", summary_M), ("scan", scan),
+                     ("pass2", pass2), ("plain", plain)):
+        _, ms = time_launches(fn, steps, warmup, stream)
+        res[name] = sum(ms) / len(ms)
+    tok = T * H * 2
+    state = H * D * D * 4
+    total = res["summary_B"] + res["summary_M"] + res["scan"] + res["pass2"]
+    out = {"workload": "kda_cp_rank_share_T131072_of_1M_8ranks_H96_bf16", "T": T, "H": H,
+           "segments_scanned": R,
+           "summary_B_ms": round(res["summary_B"], 4), "summary_M_ms": round(res["summary_M"], 4),
+           "scan_ms": round(res["scan"], 4), "pass2_ms": round(res["pass2"], 4),
+           "plain_prefill_ms": round(res["plain"], 4),
+           "rank_total_ms": round(total, 4),
+           "rank_tokens_per_s": round(T / (total * 1e-3), 1),
+           "vs_plain_prefill": round(total / res["plain"], 3),
+           # k, v, log_alpha, beta read; B written | k, log_alpha, beta read; M written
+           "summary_B_hbm_frac": round((tok * (3 * D + 1) + state) / (res["summary_B"] * 1e-3)
+                                       / (HBM_PEAK_GBS * 1e9), 4),
+           "summary_M_hbm_frac": round((tok * (2 * D + 1) + state) / (res["summary_M"] * 1e-3)
+                                       / (HBM_PEAK_GBS * 1e9), 4),
+           "scan_GBps": round(R * 3 * state / (res["scan"] * 1e-3) / 1e9, 1)}
+    del d, args, o, hT, M, B, Mr, Br, S_in, S_fin, h_in
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -406,6 +467,9 @@ def main():
         extra.append(extra_prefill(torch, kda, kda_inputs, dev, stream, 3, args.steps, args.warmup))
     if args.long:
         extra.append(extra_prefill(torch, kda, kda_inputs, dev, stream, 4, 3, 1))
+    if not args.no_extra:
+        out["context_parallel"] = context_parallel(torch, kda, kda_inputs, dev, stream,
+                                                   min(args.steps, 5), 1)
     if extra:
         out["other_workloads"] = extra
 

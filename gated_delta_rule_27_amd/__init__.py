@@ -17,6 +17,9 @@ Functions (same names as the C entry points):
 * ``kda_decode_multi(q, k, v, log_alpha, beta, S, n_tok)`` -> ``o``  up to K
   steps per sequence in one pass over the states (speculative verify /
   replay);
+* ``kda_segment_summary`` -> ``(M, B)`` and ``kda_segment_scan`` -> ``(S_in,
+  S_final)``  the affine summaries of sequence segments and the scan that
+  chains them (context parallelism);
 * ``kda_chunk_fwd_workspace_size``, ``kda_status_str``, ``kda_abi_version``.
 """
 import ctypes
@@ -70,6 +73,11 @@ def lib():
         L.kda_decode_multi.restype = ctypes.c_int
         L.kda_decode_multi.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                        ctypes.c_int, i32, vp, vp]
+        L.kda_segment_summary.restype = ctypes.c_int
+        L.kda_segment_summary.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
+                                          ctypes.c_int, vp, vp, vp, sz, vp]
+        L.kda_segment_scan.restype = ctypes.c_int
+        L.kda_segment_scan.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -266,6 +274,53 @@ def kda_decode_step(q, k, v, log_alpha, beta, S, *, o=None):
     return o
 
 
+def kda_segment_summary(q, k, v, log_alpha, beta, cu_seqlens=None, *, want_M=True,
+                        want_B=True):
+    """Affine summaries S_out = M S_in + B of the segments given by
+    cu_seqlens (packed as for kda_chunk_fwd).  Returns (M, B), each
+    [N, H, 128, 128] fp32 or None when not asked for."""
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("log_alpha", log_alpha), ("beta", beta)):
+        _dev(t, name, q.dtype)
+    if want_B:
+        _dev(v, "v", q.dtype)
+    dt = _dtype_code(q)
+    T, H, Dk = q.shape
+    N = 1
+    if cu_seqlens is not None:
+        _dev(cu_seqlens, "cu_seqlens", torch.int32)
+        N = cu_seqlens.numel() - 1
+    M = torch.empty((N, H, Dk, Dk), dtype=torch.float32, device=q.device) if want_M else None
+    B = torch.empty((N, H, Dk, Dk), dtype=torch.float32, device=q.device) if want_B else None
+    ws_bytes = kda_chunk_fwd_workspace_size(T, N, H, Dk, Dk, dt)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    _check(lib().kda_segment_summary(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(cu_seqlens), N, T, H,
+        Dk, Dk, dt, _ptr(M), _ptr(B), _ptr(ws), ws_bytes, _stream(q.device)))
+    return M, B
+
+
+def kda_segment_scan(M, B, h0=None):
+    """States entering R consecutive segments: S_in[0] = h0 (None = 0),
+    S_in[r+1] = M[r] S_in[r] + B[r].  M, B: [R, H, 128, 128] fp32; h0:
+    [H, 128, 128] or [1, H, 128, 128].  Returns (S_in [R, H, 128, 128],
+    S_final [H, 128, 128])."""
+    torch = _torch()
+    _dev(M, "M", torch.float32)
+    _dev(B, "B", torch.float32)
+    R, H, Dk, Dv = M.shape
+    if tuple(B.shape) != (R, H, Dk, Dv):
+        raise ValueError("M and B must have the same shape")
+    if h0 is not None:
+        h0 = h0.reshape(H, Dk, Dv)
+    _dev(h0, "h0", torch.float32)
+    S_in = torch.empty_like(M)
+    S_final = torch.empty((H, Dk, Dv), dtype=torch.float32, device=M.device)
+    _check(lib().kda_segment_scan(_ptr(M), _ptr(B), _ptr(h0), R, H, Dk, Dv, _ptr(S_in),
+                                  _ptr(S_final), _stream(M.device)))
+    return S_in, S_final
+
+
 def kda_decode_multi(q, k, v, log_alpha, beta, S, n_tok=None, *, update_state=True, o=None):
     """Up to K recurrent KDA steps for B sequences in one pass over their
     states.  q, k, log_alpha, v: [B, K, H, 128]; beta: [B, K, H]; S
@@ -297,6 +352,6 @@ def kda_decode_multi(q, k, v, log_alpha, beta, S, n_tok=None, *, update_state=Tr
 
 
 __all__ = ["kda_chunk_fwd", "kda_chunk_fwd_snap", "snapshot_index", "kda_decode_step",
-           "kda_decode_multi",
+           "kda_decode_multi", "kda_segment_summary", "kda_segment_scan",
            "kda_chunk_fwd_workspace_size", "kda_status_str", "kda_abi_version", "KDAError",
            "lib", "LIB_PATH"]

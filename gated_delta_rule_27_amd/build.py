@@ -16,7 +16,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libkda.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["kda_api.cpp", "kda_chunk.hip", "kda_chunk_ws.hip", "kda_decode.hip"]
+SOURCES = ["kda_api.cpp", "kda_chunk.hip", "kda_chunk_ws.hip", "kda_decode.hip",
+           "kda_segment.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -47,6 +48,33 @@ def build(verbose=False):
     subprocess.run(cmd, check=True, capture_output=not verbose)
     os.replace(tmp, LIB)
     return LIB
+
+
+def resource_usage(src):
+    """Per-kernel register and scratch use of one HIP source, from the
+    compiler's resource-usage remarks: {kernel symbol: {"vgpr", "agpr",
+    "scratch", "occupancy"}} (scratch in bytes per lane; non-zero means
+    spills or a stack)."""
+    import re
+    cmd = [HIPCC] + COMMON + ["-x", "hip", "--cuda-device-only", "-c", os.path.join(CSRC, src),
+                              "-o", os.devnull, "-Rpass-analysis=kernel-resource-usage"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise subprocess.CalledProcessError(r.returncode, cmd)
+    out, cur = {}, None
+    keys = {"VGPRs": "vgpr", "AGPRs": "agpr", "ScratchSize [bytes/lane]": "scratch",
+            "Occupancy [waves/SIMD]": "occupancy"}
+    for line in r.stderr.splitlines():
+        m = re.search(r"remark:\s+(.*?): (\S+) \[-Rpass-analysis", line)
+        if not m:
+            continue
+        key, val = m.group(1).strip(), m.group(2)
+        if key == "Function Name":
+            cur = out.setdefault(val, {})
+        elif cur is not None and key in keys:
+            cur[keys[key]] = int(val)
+    return out
 
 
 if __name__ == "__main__":

@@ -92,7 +92,8 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
                           int32_t N, int64_t T_total, int32_t H, int32_t Dk, int32_t Dv,
                           kda_dtype dt, void* o, float* h_T, void* workspace,
                           size_t workspace_bytes, int32_t chunk, int32_t dv_split,
-                          const SnapReq& sr, hipStream_t stream) {
+                          const SnapReq& sr, int32_t flags, hipStream_t stream,
+                          bool check_only = false) {
     if (!valid_dtype(dt)) return KDA_ERR_BAD_DTYPE;
     if (N < 1 || T_total < 0 || H < 1 || H > KDA_MAX_HEADS || Dk != kda::kHeadDim ||
         Dv != kda::kHeadDim)
@@ -111,7 +112,9 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
         if ((uint64_t)sr.n_snap > kMaxElems / per) return KDA_ERR_BAD_SHAPE;
     }
 
-    if (T_total > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERR_NULL_ARG;
+    const bool need_v = !(flags & kda::kChunkVZero), need_o = !(flags & kda::kChunkNoOutput);
+    if (T_total > 0 && (!k || !log_alpha || !beta || (need_v && !v) || (need_o && (!q || !o))))
+        return KDA_ERR_NULL_ARG;
     if (sr.n_snap > 0 && (!sr.snap || (N > 1 && !sr.snap_cu))) return KDA_ERR_NULL_ARG;
     if (sr.snap && !aligned(sr.snap, 16)) return KDA_ERR_MISALIGNED;
     if (sr.snap_cu && !aligned(sr.snap_cu, 4)) return KDA_ERR_MISALIGNED;
@@ -148,6 +151,7 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
     if (dv_split) s = dv_split;
     if (!kda::chunk_config_supported((int)dt, c, s)) return KDA_ERR_BAD_SHAPE;
     if (sr.interval != 0 && sr.interval % c != 0) return KDA_ERR_BAD_SHAPE;
+    if (check_only) return KDA_OK;
 
     kda::ChunkArgs a;
     a.q = q;
@@ -166,6 +170,7 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
     a.snap.snap_cu = sr.snap_cu;
     a.snap.n_snap = sr.n_snap;
     a.snap.every_chunks = sr.interval > 0 ? sr.interval / kda::kSnapUnit : 1;
+    a.flags = flags;
     if (kda::launch_chunk(a, (int)dt, c, s, stream) != hipSuccess) return KDA_ERR_DEVICE;
     return KDA_OK;
 }
@@ -179,7 +184,7 @@ kda_status kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const v
                             size_t workspace_bytes, int32_t chunk, int32_t dv_split,
                             hipStream_t stream) {
     return chunk_fwd_impl(q, k, v, log_alpha, beta, h0, cu_seqlens, N, T_total, H, Dk, Dv, dt,
-                          o, h_T, workspace, workspace_bytes, chunk, dv_split, SnapReq{},
+                          o, h_T, workspace, workspace_bytes, chunk, dv_split, SnapReq{}, 0,
                           stream);
 }
 
@@ -197,7 +202,7 @@ kda_status kda_chunk_fwd_snap(const void* q, const void* k, const void* v,
     sr.n_snap = n_snap;
     sr.snap = snap;
     return chunk_fwd_impl(q, k, v, log_alpha, beta, h0, cu_seqlens, N, T_total, H, Dk, Dv, dt,
-                          o, h_T, workspace, workspace_bytes, 0, 0, sr, stream);
+                          o, h_T, workspace, workspace_bytes, 0, 0, sr, 0, stream);
 }
 
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* log_alpha,
@@ -241,6 +246,59 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const vo
     a.H = H;
     a.o = o;
     if (kda::launch_decode(a, (int)dt, stream) != hipSuccess) return KDA_ERR_DEVICE;
+    return KDA_OK;
+}
+
+kda_status kda_segment_summary(const void* q, const void* k, const void* v,
+                               const void* log_alpha, const void* beta,
+                               const int32_t* cu_seqlens, int32_t N, int64_t T_total, int32_t H,
+                               int32_t Dk, int32_t Dv, kda_dtype dt, float* M, float* B,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!M && !B) return KDA_ERR_NULL_ARG;
+    if (N >= 1 && H >= 1) {
+        const uint64_t n = (uint64_t)N * H * kda::kHeadDim * kda::kHeadDim * 4;
+        if (M && B && overlaps(span(M, n), span(B, n))) return KDA_ERR_ALIAS;
+    }
+    // B: the state reached from a zero start.  M: the transition, i.e. the
+    // state reached from the identity with V = 0 (v is passed along only so
+    // that M is checked against it; that pass never reads it).  Both passes
+    // are validated before either is launched.
+    const int32_t fB = kda::kChunkNoOutput;
+    const int32_t fM = kda::kChunkNoOutput | kda::kChunkVZero | kda::kChunkH0Identity;
+    for (int launch = 0; launch < 2; ++launch) {
+        kda_status st = KDA_OK;
+        if (B)
+            st = chunk_fwd_impl(q, k, v, log_alpha, beta, nullptr, cu_seqlens, N, T_total, H, Dk,
+                                Dv, dt, nullptr, B, workspace, workspace_bytes, 0, 0, SnapReq{},
+                                fB, stream, !launch);
+        if (st == KDA_OK && M)
+            st = chunk_fwd_impl(q, k, v, log_alpha, beta, nullptr, cu_seqlens, N, T_total, H, Dk,
+                                Dv, dt, nullptr, M, workspace, workspace_bytes, 0, 0, SnapReq{},
+                                fM, stream, !launch);
+        if (st != KDA_OK) return st;
+    }
+    return KDA_OK;
+}
+
+kda_status kda_segment_scan(const float* M, const float* B, const float* h0, int32_t R,
+                            int32_t H, int32_t Dk, int32_t Dv, float* S_in, float* S_final,
+                            hipStream_t stream) {
+    if (R < 0 || H < 1 || H > KDA_MAX_HEADS || Dk != kda::kHeadDim || Dv != kda::kHeadDim)
+        return KDA_ERR_BAD_SHAPE;
+    const uint64_t per = (uint64_t)H * kda::kHeadDim * kda::kHeadDim;
+    if ((uint64_t)R > kMaxElems / per) return KDA_ERR_BAD_SHAPE;
+    if (R > 0 && (!M || !B || !S_in)) return KDA_ERR_NULL_ARG;
+    for (const void* p : {(const void*)M, (const void*)B, (const void*)h0, (const void*)S_in,
+                          (const void*)S_final})
+        if (p && !aligned(p, 16)) return KDA_ERR_MISALIGNED;
+    const Span sM = span(M, M ? (uint64_t)R * per * 4 : 0), sB = span(B, B ? (uint64_t)R * per * 4 : 0),
+               sh0 = span(h0, h0 ? per * 4 : 0), sS = span(S_in, S_in ? (uint64_t)R * per * 4 : 0),
+               sF = span(S_final, S_final ? per * 4 : 0);
+    if (overlaps_any(sS, {sM, sB, sh0, sF})) return KDA_ERR_ALIAS;
+    if (overlaps_any(sF, {sM, sB, sh0})) return KDA_ERR_ALIAS;
+    if (R == 0 && !S_final) return KDA_OK;
+    if (kda::launch_segment_scan(M, B, h0, R, H, S_in, S_final, stream) != hipSuccess)
+        return KDA_ERR_DEVICE;
     return KDA_OK;
 }
 

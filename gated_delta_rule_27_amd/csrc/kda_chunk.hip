@@ -108,7 +108,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(
     const TIn* __restrict__ log_alpha, const TIn* __restrict__ beta,
     const float* __restrict__ h0, const int32_t* __restrict__ cu_seqlens,
     int64_t T_total, int32_t H, int32_t split, TIn* __restrict__ o,
-    float* __restrict__ h_T, SnapArgs snap) {
+    float* __restrict__ h_T, SnapArgs snap, int32_t flags) {
     typedef ChunkCfg<TIn, C, NW, NCT> K;
     typedef typename K::TOp TOp;
     constexpr bool kBF16 = sizeof(TOp) == 2;
@@ -166,7 +166,22 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(
                 for (int e = 0; e < 4; ++e)
                     S[ct][it][e] = src ? src[(16 * it + 4 * g + e) * kHeadDim + j] : 0.f;
         }
+        // h0 = I (a separate uniform branch: folded into the loads above, the
+        // selects cost registers across the whole chunk loop)
+        if (!src && (flags & kChunkH0Identity)) {
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                const int j = col0 + 16 * (NCT * wave + ct) + l16;
+#pragma unroll
+                for (int it = 0; it < 8; ++it)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (16 * it + 4 * g + e == j) S[ct][it][e] = 1.f;
+            }
+        }
     }
+    const bool v_zero = flags & kChunkVZero;
+    const bool write_o = !(flags & kChunkNoOutput);
 
     // ---- register prefetch of one chunk's inputs ----
     // channel thread (tid < 128): q, k, log alpha of channel tid for C tokens
@@ -179,7 +194,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(
             for (int r = 0; r < C; ++r) {
                 const bool ok = r < len;
                 const size_t off = (size_t)(t0 + r) * rowstride + headoff + tid;
-                pq[r] = ok ? q[off] : from_f32<TIn>(0.f);
+                pq[r] = ok && write_o ? q[off] : from_f32<TIn>(0.f);  // q feeds o only
                 pk[r] = ok ? k[off] : from_f32<TIn>(0.f);
                 pg[r] = ok ? log_alpha[off] : from_f32<TIn>(0.f);
             }
@@ -189,7 +204,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(
             const int idx = tid + u * K::NT;
             const int r = idx / K::VROW, cv = idx % K::VROW;
             typename Vec16<TIn>::type x = {};
-            if (idx < C * K::VROW && r < len)
+            if (idx < C * K::VROW && r < len && !v_zero)
                 x = *reinterpret_cast<const typename Vec16<TIn>::type*>(
                     v + (size_t)(t0 + r) * rowstride + headoff + col0 + cv * K::VEC);
             pv[u] = x;
@@ -473,7 +488,8 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 16 * mt + 4 * g + e;
-                    if (r < len) o[(size_t)(t0 + r) * rowstride + headoff + j] = from_f32<TIn>(O[ct][mt][e]);
+                    if (r < len && write_o)
+                        o[(size_t)(t0 + r) * rowstride + headoff + j] = from_f32<TIn>(O[ct][mt][e]);
                 }
             }
         // S <- Diag(Gamma_C) S + Kvec^T U
@@ -516,16 +532,21 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(
             if (done % every == 0) {
                 const int64_t idx = (snap.snap_cu ? (int64_t)snap.snap_cu[n] : 0) + done / every - 1;
                 if (idx < snap.n_snap) {
-                    float* dst = snap.snap + ((size_t)idx * (size_t)H + h) * (kHeadDim * kHeadDim);
+                    // buffer stores: one lane offset, the rest in the scalar
+                    // offset, so no per-element addresses stay live
+                    const rsrc_t rs = make_rsrc(
+                        snap.snap + ((size_t)idx * (size_t)H + h) * (kHeadDim * kHeadDim),
+                        kHeadDim * kHeadDim * 4);
+                    const uint32_t lane =
+                        (uint32_t)((4 * g * kHeadDim + col0 + 16 * NCT * wave + l16) * 4);
 #pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct) {
-                        const int j = col0 + 16 * (NCT * wave + ct) + l16;
+                    for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
                         for (int it = 0; it < 8; ++it)
 #pragma unroll
                             for (int e = 0; e < 4; ++e)
-                                dst[(16 * it + 4 * g + e) * kHeadDim + j] = S[ct][it][e];
-                    }
+                                buf_store_f32(S[ct][it][e], rs, lane,
+                                              ((16 * it + e) * kHeadDim + 16 * ct) * 4);
                 }
             }
         }
@@ -558,7 +579,7 @@ hipError_t launch(const ChunkArgs& a, hipStream_t stream) {
     kern<<<dim3((unsigned)nwg), dim3(K::NT), K::bytes, stream>>>(
         (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, (const TIn*)a.log_alpha,
         (const TIn*)a.beta, a.h0, a.cu_seqlens, a.T_total, a.H, split, (TIn*)a.o, a.h_T,
-        a.snap);
+        a.snap, a.flags);
     return hipGetLastError();
 }
 

@@ -91,7 +91,7 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
     const bf16* __restrict__ log_alpha, const bf16* __restrict__ beta,
     const float* __restrict__ h0, const int32_t* __restrict__ cu_seqlens, int64_t T_total,
     int32_t H, int32_t split, int32_t units, bf16* __restrict__ o, float* __restrict__ h_T,
-    SnapArgs snap) {
+    SnapArgs snap, int32_t flags) {
     typedef WsCfg<NCT, NSW, PD> K;
     constexpr int KP = K::KP, TP = K::TP, AP = K::AP, DV = K::DV;
 
@@ -148,8 +148,10 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
                 for (int it = 0; it < 8; ++it)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const int idx = (16 * it + 4 * g + e) * kHeadDim + j;
-                        dst[idx] = src ? src[idx] : 0.f;
+                        const int row = 16 * it + 4 * g + e;
+                        const int idx = row * kHeadDim + j;
+                        dst[idx] = src ? src[idx]
+                                       : ((flags & kChunkH0Identity) && row == j ? 1.f : 0.f);
                     }
             }
         }
@@ -195,6 +197,19 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
                     for (int e = 0; e < 4; ++e)
                         S[ct][it][e] = src ? src[(16 * it + 4 * g + e) * kHeadDim + j] : 0.f;
             }
+            // h0 = I (a separate uniform branch: folded into the loads above,
+            // the selects cost registers across the whole chunk loop)
+            if (!src && (flags & kChunkH0Identity)) {
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) {
+                    const int j = col0 + 16 * (NCT * wave + ct) + l16;
+#pragma unroll
+                    for (int it = 0; it < 8; ++it)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (16 * it + 4 * g + e == j) S[ct][it][e] = 1.f;
+                }
+            }
         }
         // V of a chunk: rows 4g..4g+3 of this lane's columns, four chunks in
         // flight, through a buffer resource over the chunk's rows inside the
@@ -207,15 +222,17 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
         const int64_t snap_base = snap.snap_cu ? (int64_t)snap.snap_cu[n] : 0;
         const uint32_t vo_lane = (uint32_t)(((size_t)(4 * g) * rowstride + headoff + colw0) * 2);
         const uint32_t vo_row = (uint32_t)(rowstride * 2);
-        auto rows_rsrc = [&](const bf16* base, int y) {
-            const int64_t rows = (y >= 0 && y < nch) ? seqlen - (int64_t)kWsC * y : 0;
+        const uint32_t snap_lane = (uint32_t)((4 * g * kHeadDim + colw0) * 4);
+        // (an empty resource when the pass takes V as zero / writes no output)
+        auto rows_rsrc = [&](const bf16* base, int y, bool none) {
+            const int64_t rows = (!none && y >= 0 && y < nch) ? seqlen - (int64_t)kWsC * y : 0;
             return make_rsrc(base + (size_t)(bos + (int64_t)kWsC * (y < 0 ? 0 : y)) * rowstride,
                              rows * (int64_t)rowstride * 2);
         };
         bf16 vr[4][NCT][4];
         auto load_v = [&](auto slot_c, int y) {
             constexpr int sv = decltype(slot_c)::value;
-            const rsrc_t rv = rows_rsrc(v, y);
+            const rsrc_t rv = rows_rsrc(v, y, flags & kChunkVZero);
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
@@ -259,7 +276,7 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
                     ub[ct] = acc_frag_k16(U[ct]);
                     Ov[ct] = mma_bf16_k16_as_k32(ap, ub[ct], Ov[ct]);  // same opcode as Qtil S
                 }
-                const rsrc_t ro = rows_rsrc(o, c);
+                const rsrc_t ro = rows_rsrc(o, c, flags & kChunkNoOutput);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
 #pragma unroll
@@ -280,15 +297,17 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
                     (int64_t)kWsC * (c + 1) <= seqlen) {
                     const int64_t idx = snap_base + (c + 1) / snap.every_chunks - 1;
                     if (idx < snap.n_snap) {
-                        float* dst = snap.snap + ((size_t)idx * (size_t)H + h) * (kHeadDim * kHeadDim);
+                        const rsrc_t rs = make_rsrc(
+                            snap.snap + ((size_t)idx * (size_t)H + h) * (kHeadDim * kHeadDim),
+                            kHeadDim * kHeadDim * 4);
 #pragma unroll
                         for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
                             for (int it = 0; it < 8; ++it)
 #pragma unroll
                                 for (int e = 0; e < 4; ++e)
-                                    dst[(16 * it + 4 * g + e) * kHeadDim + colw0 + 16 * ct] =
-                                        S[ct][it][e];
+                                    buf_store_f32(S[ct][it][e], rs, snap_lane,
+                                                  ((16 * it + e) * kHeadDim + 16 * ct) * 4);
                     }
                 }
             }
@@ -336,12 +355,15 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
     bf16 rb[PD];
     const uint32_t qo_lane = (uint32_t)(((size_t)r * rowstride + headoff + ch0) * 2);
     const uint32_t bo_lane = (uint32_t)(((size_t)r * H + h) * 2);
+    const bool q_none = flags & kChunkNoOutput;
+    auto q_bytes = [&](int64_t b) { return q_none ? (int64_t)0 : b; };
     auto load_chunk = [&](auto slot_c, int yc) {
         constexpr int s = decltype(slot_c)::value;
         const int64_t rows = yc < nch ? seqlen - (int64_t)kWsC * yc : 0;
         const size_t t0 = (size_t)(bos + (int64_t)kWsC * yc);
         const int64_t tok_bytes = rows * (int64_t)rowstride * 2;
-        rq[s] = buf_load_bf16x4(make_rsrc(q + t0 * rowstride, tok_bytes), qo_lane);
+        // q feeds the outputs only: a pass without them reads none (zeros)
+        rq[s] = buf_load_bf16x4(make_rsrc(q + t0 * rowstride, q_bytes(tok_bytes)), qo_lane);
         rk[s] = buf_load_bf16x4(make_rsrc(k + t0 * rowstride, tok_bytes), qo_lane);
         rg[s] = buf_load_bf16x4(make_rsrc(log_alpha + t0 * rowstride, tok_bytes), qo_lane);
         rb[s] = buf_load_bf16(make_rsrc(beta + t0 * H, rows * (int64_t)H * 2), bo_lane);
@@ -446,7 +468,7 @@ hipError_t launch_ws_t(const ChunkArgs& a, hipStream_t stream) {
     kern<<<dim3((unsigned)nwg), dim3(K::NT), K::bytes, stream>>>(
         (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.log_alpha,
         (const bf16*)a.beta, a.h0, a.cu_seqlens, a.T_total, a.H, split, (int32_t)units,
-        (bf16*)a.o, a.h_T, a.snap);
+        (bf16*)a.o, a.h_T, a.snap, a.flags);
     return hipGetLastError();
 }
 

@@ -22,6 +22,17 @@ struct SnapArgs {
     int32_t every_chunks;     // >= 1
 };
 
+// Variants of a prefill pass used for segment summaries (context
+// parallelism): the affine map S_out = M S_in + B of a segment is B = the
+// final state from a zero start, and M = the final state when V is zero and
+// the initial state is the identity (the recurrence acts on each value
+// column separately, so columns of the identity evolve into columns of M).
+enum ChunkFlags : int32_t {
+    kChunkNoOutput = 1,     // o is not written (may be null)
+    kChunkVZero = 2,        // V is taken as zero (v may be null)
+    kChunkH0Identity = 4,   // the initial state of every sequence is I
+};
+
 struct ChunkArgs {
     const void* q;
     const void* k;
@@ -36,6 +47,7 @@ struct ChunkArgs {
     void* o;
     float* h_T;               // may be null
     SnapArgs snap;            // snap.snap == nullptr: no snapshots
+    int32_t flags;            // ChunkFlags
 };
 
 struct DecodeArgs {
@@ -79,5 +91,7 @@ hipError_t launch_chunk(const ChunkArgs& a, int dtype, int chunk, int split,
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_decode_multi(const DecodeMultiArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_segment_scan(const float* M, const float* B, const float* h0, int32_t R,
+                               int32_t H, float* S_in, float* S_final, hipStream_t stream);
 
 }  // namespace kda

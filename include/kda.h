@@ -186,6 +186,43 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v,
                            kda_dtype dt, void* o, hipStream_t stream);
 
 /*
+ * Segment summaries for KDA context parallelism ("An infra-oriented diagram
+ * of Kimi K3", "KDA Context Parallelism"; "From GPT-2 to Kimi K3", ch. 6):
+ * a segment maps the state entering it affinely, S_out = M S_in + B.  For
+ * every segment n (the packed sequences of cu_seqlens, as for
+ * kda_chunk_fwd):
+ *   B[n] : [H, Dk, Dv] fp32, the state reached from a zero start;
+ *   M[n] : [H, Dk, Dk] fp32, the product of the segment's per-token
+ *          transitions (I - beta k k^T) Diag(alpha), latest on the left.
+ * Either output may be NULL (not computed), not both.  Each is one prefill
+ * pass (M: V taken as zero from the identity, by column independence).
+ * Neither pass reads q (it feeds only the outputs o = S^T q, which a summary
+ * does not form), so q may be NULL.  Errors as kda_chunk_fwd (o and h0 are
+ * not arguments); v may be NULL when only M is asked for; M overlapping B
+ * is KDA_ERR_ALIAS.  Both passes are validated before either is launched.
+ */
+kda_status kda_segment_summary(const void* q, const void* k, const void* v,
+                               const void* log_alpha, const void* beta,
+                               const int32_t* cu_seqlens, int32_t N,
+                               int64_t T_total, int32_t H, int32_t Dk,
+                               int32_t Dv, kda_dtype dt, float* M, float* B,
+                               void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/*
+ * The exclusive scan over R consecutive segments of one sequence, per head:
+ *   S_in[0] = h0 (NULL = 0),  S_in[r + 1] = M[r] S_in[r] + B[r],
+ * with M, B, S_in : [R, H, 128, 128] fp32 and S_final = M[R-1] S_in[R-1] +
+ * B[R-1] : [H, 128, 128] (may be NULL).  Resuming each segment from
+ * S_in[r] (kda_chunk_fwd with h0 = S_in) reproduces the uninterrupted run.
+ * R == 0 writes S_final = h0.  All buffers 16-byte aligned; S_in or
+ * S_final overlapping an input is KDA_ERR_ALIAS.
+ */
+kda_status kda_segment_scan(const float* M, const float* B, const float* h0,
+                            int32_t R, int32_t H, int32_t Dk, int32_t Dv,
+                            float* S_in, float* S_final, hipStream_t stream);
+
+/*
  * Up to K recurrent steps for each of B sequences in one pass over their
  * states: a short window of tokens per cached sequence, such as a
  * speculative draft.  Verifying a draft must not move the cached state, and

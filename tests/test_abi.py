@@ -39,7 +39,8 @@ def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert {"kda_chunk_fwd", "kda_chunk_fwd_ex", "kda_decode_step",
             "kda_chunk_fwd_workspace_size", "kda_status_str", "kda_abi_version",
-            "kda_chunk_fwd_snap", "kda_decode_multi"} <= set(names)
+            "kda_chunk_fwd_snap", "kda_decode_multi", "kda_segment_summary",
+            "kda_segment_scan"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -147,6 +148,57 @@ def test_decode_multi_argument_errors(L, kw, code):
 
 def test_decode_multi_empty_batch_launches_nothing(L):
     assert decode_multi(L, B=0, q=None, k=None, v=None, g=None, b=None, S=None, o=None) == OK
+
+
+def seg_summary(L, **kw):
+    a = dict(q=P(0), k=P(1), v=P(2), g=P(3), b=P(4), cu=P(6), N=3, T=600, H=2, Dk=D, Dv=D,
+             dt=BF16, M=P(7), B=P(8), ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return L.kda_segment_summary(a["q"], a["k"], a["v"], a["g"], a["b"], a["cu"], a["N"],
+                                 a["T"], a["H"], a["Dk"], a["Dv"], a["dt"], a["M"], a["B"],
+                                 a["ws"], a["wsb"], a["stream"])
+
+
+def seg_scan(L, **kw):
+    a = dict(M=P(0), B=P(1), h0=P(2), R=4, H=2, Dk=D, Dv=D, S=P(3), F=P(4), stream=None)
+    a.update(kw)
+    return L.kda_segment_scan(a["M"], a["B"], a["h0"], a["R"], a["H"], a["Dk"], a["Dv"],
+                              a["S"], a["F"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=None, B=None), NULL_ARG),
+    (dict(k=None), NULL_ARG),
+    (dict(v=None), NULL_ARG),             # B needs V
+    (dict(Dk=64), BAD_SHAPE),
+    (dict(N=3, cu=None), BAD_SHAPE),
+    (dict(M=P(8)), ALIAS),                # M on B
+    (dict(B=P(0)), ALIAS),                # B on q
+    (dict(M=P(7, 4)), MISALIGNED),
+])
+def test_segment_summary_argument_errors(L, kw, code):
+    assert seg_summary(L, **kw) == code
+
+
+def test_segment_summary_without_q_or_v_passes_validation(L):
+    # q is never read; v only for B.  With no device the launch is what fails.
+    assert seg_summary(L, q=None) == DEVICE
+    assert seg_summary(L, q=None, v=None, B=None) == DEVICE
+    assert seg_summary(L, T=0, q=None, v=None, k=None, g=None, b=None) == DEVICE
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(R=-1), BAD_SHAPE),
+    (dict(H=0), BAD_SHAPE),
+    (dict(Dv=64), BAD_SHAPE),
+    (dict(M=None), NULL_ARG),
+    (dict(S=None), NULL_ARG),
+    (dict(S=P(3, 8)), MISALIGNED),
+    (dict(S=P(0)), ALIAS),                # S_in on M
+    (dict(F=P(2)), ALIAS),                # S_final on h0
+])
+def test_segment_scan_argument_errors(L, kw, code):
+    assert seg_scan(L, **kw) == code
 
 
 def decode(L, **kw):

@@ -1,0 +1,42 @@
+"""Register and scratch budgets of the HIP kernels, from the compiler's
+resource-usage remarks (a CPU test: hipcc cross-compiles for gfx950).
+
+The chunk kernels keep the 128 x 128 state of a head in registers for the
+whole sequence; a spill to scratch puts per-lane memory traffic into the
+chunk loop and slows prefill by a third, so every kernel must compile with
+no scratch, and the 1024-thread prefill variant must fit 128 VGPRs (four
+waves per SIMD).
+"""
+import pytest
+
+from gated_delta_rule_27_amd import build
+
+SOURCES = [s for s in build.SOURCES if s.endswith(".hip")]
+
+
+@pytest.fixture(scope="module")
+def usage():
+    out = {}
+    for src in SOURCES:
+        out.update(build.resource_usage(src))
+    return out
+
+
+def test_every_kernel_is_reported(usage):
+    names = " ".join(usage)
+    for k in ("chunk_ws_kernel", "chunk_kernel", "decode_kernel", "decode_multi_kernel",
+              "segment_scan_kernel"):
+        assert k in names, k
+
+
+def test_no_kernel_spills_to_scratch(usage):
+    bad = {k: v for k, v in usage.items() if v.get("scratch", 0) != 0}
+    assert not bad, f"kernels with scratch: {bad}"
+
+
+def test_whole_head_prefill_fits_four_waves_per_simd(usage):
+    ws = {k: v for k, v in usage.items() if "chunk_ws_kernelILi1ELi8E" in k}
+    assert ws, "16-wave prefill variant missing"
+    for k, v in ws.items():
+        assert v["vgpr"] + v.get("agpr", 0) <= 128, (k, v)
+        assert v["occupancy"] >= 4, (k, v)
