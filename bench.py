@@ -308,6 +308,47 @@ def context_parallel(torch, kda, kda_inputs, dev, stream, steps, warmup):
     return out
 
 
+def layer_elementwise(torch, kda, kda_inputs, dev, stream, steps, warmup, chunk_ms, decode_ms):
+    """The prologue (short conv + Swish + L2 norm, decay and write gates) and
+    the epilogue (head RMSNorm x output gate) around the core, on the
+    4096-token prefill workload and on a 256-request decode step (with the
+    convolution history read and written).  HBM fractions count the
+    algorithmic bytes: every input read once, every output written once."""
+    out = {}
+    for name, T, H, lengths in (("prefill_T4096_H96_bf16", 4096, 96, None),
+                                ("decode_B256_H96_bf16", 256, 96, [1] * 256)):
+        d = kda_inputs.layer_inputs(T, H, dtype="bf16", device=dev, seed=1007, lengths=lengths,
+                                    conv_state=lengths is not None)
+        so = torch.empty_like(d["conv_state"]) if d["conv_state"] is not None else None
+        y = torch.empty_like(d["o"])
+
+        def pro(i):
+            kda.kda_prologue(d["xq"], d["xk"], d["xv"], d["a_raw"], d["b_raw"], d["conv_w"],
+                             d["a_bias"], cu_seqlens=d["cu_seqlens"], conv_state=d["conv_state"],
+                             store_state=so is not None, state_out=so)
+
+        def epi(i):
+            kda.kda_epilogue(d["o"], d["g"], d["norm_w"], y=y)
+
+        _, pms = time_launches(pro, steps, warmup, stream)
+        _, ems = time_launches(epi, steps, warmup, stream)
+        pavg, eavg = sum(pms) / len(pms), sum(ems) / len(ems)
+        row = H * D * 2
+        hist = 0 if so is None else 2 * d["N"] * 9 * row      # history read + written
+        pbytes = T * (8 * row + 4 * H) + hist + (3 * 4 + 1) * H * D * 4
+        ebytes = T * 3 * row + H * D * 4
+        core = chunk_ms if lengths is None else decode_ms
+        out[name] = {"prologue_ms": round(pavg, 5), "epilogue_ms": round(eavg, 5),
+                     "prologue_hbm_frac": round(pbytes / (pavg * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+                     "epilogue_hbm_frac": round(ebytes / (eavg * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+                     "prologue_bytes": pbytes, "epilogue_bytes": ebytes,
+                     "core_ms": round(core, 5) if core else None,
+                     "layer_ms": round(pavg + eavg + core, 5) if core else None}
+        del d, so, y
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -448,6 +489,11 @@ def main():
         }
         del dd
         torch.cuda.empty_cache()
+
+    if not args.no_extra:
+        out["layer_elementwise"] = layer_elementwise(
+            torch, kda, kda_inputs, dev, stream, args.steps, args.warmup, avg_ms,
+            out["decode"]["ms_per_step"] if "decode" in out else None)
 
     if "verify_replay" in out and "decode" in out:
         vr = out["verify_replay"]

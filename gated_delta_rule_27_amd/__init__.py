@@ -20,6 +20,8 @@ Functions (same names as the C entry points):
 * ``kda_segment_summary`` -> ``(M, B)`` and ``kda_segment_scan`` -> ``(S_in,
   S_final)``  the affine summaries of sequence segments and the scan that
   chains them (context parallelism);
+* ``kda_prologue`` and ``kda_epilogue``  the elementwise work of a KDA layer
+  around the core (short convolution, Swish, norms, gates);
 * ``kda_chunk_fwd_workspace_size``, ``kda_status_str``, ``kda_abi_version``.
 """
 import ctypes
@@ -78,6 +80,13 @@ def lib():
                                           ctypes.c_int, vp, vp, vp, sz, vp]
         L.kda_segment_scan.restype = ctypes.c_int
         L.kda_segment_scan.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]
+        L.kda_prologue.restype = ctypes.c_int
+        L.kda_prologue.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32,
+                                   ctypes.c_int, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp,
+                                   vp]
+        L.kda_epilogue.restype = ctypes.c_int
+        L.kda_epilogue.argtypes = [vp, vp, vp, i64, i32, i32, ctypes.c_int, ctypes.c_float,
+                                   vp, vp]
         _lib = L
     return _lib
 
@@ -321,6 +330,59 @@ def kda_segment_scan(M, B, h0=None):
     return S_in, S_final
 
 
+def kda_prologue(xq, xk, xv, a_raw, b_raw, conv_w, a_bias, cu_seqlens=None, conv_state=None,
+                 *, l2_eps=1e-6, store_state=True, state_out=None):
+    """Prologue of a KDA layer: Swish(short conv) for q, k, v (q, k then
+    L2-normalised per head), log_alpha = -5 sigmoid(a_raw + a_bias), beta =
+    sigmoid(b_raw), and the new convolution history.
+
+    xq, xk, xv, a_raw: [T, H, 128]; b_raw: [T, H] (bf16 or fp32, one dtype);
+    conv_w: [3, H, 128, 4] fp32; a_bias: [H, 128] fp32; conv_state:
+    [N, 3, 3, H, 128] in the input dtype or None (zero history).  Returns
+    (q, k, v, log_alpha, beta, conv_state_out or None)."""
+    torch = _torch()
+    dt_t = xq.dtype
+    for name, t in (("xq", xq), ("xk", xk), ("xv", xv), ("a_raw", a_raw), ("b_raw", b_raw)):
+        _dev(t, name, dt_t)
+    _dev(conv_w, "conv_w", torch.float32)
+    _dev(a_bias, "a_bias", torch.float32)
+    dt = _dtype_code(xq)
+    T, H, D = xq.shape
+    N = 1
+    if cu_seqlens is not None:
+        _dev(cu_seqlens, "cu_seqlens", torch.int32)
+        N = cu_seqlens.numel() - 1
+    _dev(conv_state, "conv_state", dt_t)
+    q, k, v, la = (torch.empty_like(xq) for _ in range(4))
+    beta = torch.empty_like(b_raw)
+    so = None
+    if store_state:
+        so = state_out if state_out is not None else torch.empty(
+            (N, 3, 3, H, D), dtype=dt_t, device=xq.device)
+        _dev(so, "state_out", dt_t)
+    _check(lib().kda_prologue(
+        _ptr(xq), _ptr(xk), _ptr(xv), _ptr(a_raw), _ptr(b_raw), _ptr(conv_w), _ptr(a_bias),
+        _ptr(cu_seqlens), N, T, H, D, dt, _ptr(conv_state), _ptr(so), float(l2_eps), _ptr(q),
+        _ptr(k), _ptr(v), _ptr(la), _ptr(beta), _stream(xq.device)))
+    return q, k, v, la, beta, so
+
+
+def kda_epilogue(o, g, norm_w, *, eps=1e-5, y=None):
+    """y = RMSNorm_head(o) * norm_w * sigmoid(g).  o, g: [T, H, 128]
+    (bf16 or fp32); norm_w: [H, 128] fp32.  y may be o or g (in place)."""
+    torch = _torch()
+    _dev(o, "o", o.dtype)
+    _dev(g, "g", o.dtype)
+    _dev(norm_w, "norm_w", torch.float32)
+    T, H, D = o.shape
+    if y is None:
+        y = torch.empty_like(o)
+    _dev(y, "y", o.dtype)
+    _check(lib().kda_epilogue(_ptr(o), _ptr(g), _ptr(norm_w), T, H, D, _dtype_code(o),
+                              float(eps), _ptr(y), _stream(o.device)))
+    return y
+
+
 def kda_decode_multi(q, k, v, log_alpha, beta, S, n_tok=None, *, update_state=True, o=None):
     """Up to K recurrent KDA steps for B sequences in one pass over their
     states.  q, k, log_alpha, v: [B, K, H, 128]; beta: [B, K, H]; S
@@ -352,6 +414,7 @@ def kda_decode_multi(q, k, v, log_alpha, beta, S, n_tok=None, *, update_state=Tr
 
 
 __all__ = ["kda_chunk_fwd", "kda_chunk_fwd_snap", "snapshot_index", "kda_decode_step",
-           "kda_decode_multi", "kda_segment_summary", "kda_segment_scan",
+           "kda_decode_multi", "kda_segment_summary", "kda_segment_scan", "kda_prologue",
+           "kda_epilogue",
            "kda_chunk_fwd_workspace_size", "kda_status_str", "kda_abi_version", "KDAError",
            "lib", "LIB_PATH"]

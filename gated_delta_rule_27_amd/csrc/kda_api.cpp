@@ -348,4 +348,111 @@ kda_status kda_decode_multi(const void* q, const void* k, const void* v, const v
     return KDA_OK;
 }
 
+kda_status kda_prologue(const void* xq, const void* xk, const void* xv, const void* a_raw,
+                        const void* b_raw, const float* conv_w, const float* a_bias,
+                        const int32_t* cu_seqlens, int32_t N, int64_t T_total, int32_t H,
+                        int32_t D, kda_dtype dt, const void* conv_state_in,
+                        void* conv_state_out, float l2_eps, void* q, void* k, void* v,
+                        void* log_alpha, void* beta, hipStream_t stream) {
+    if (!valid_dtype(dt)) return KDA_ERR_BAD_DTYPE;
+    if (N < 1 || T_total < 0 || H < 1 || H > KDA_MAX_HEADS || D != kda::kHeadDim)
+        return KDA_ERR_BAD_SHAPE;
+    if (!cu_seqlens && N != 1) return KDA_ERR_BAD_SHAPE;
+    if (!(l2_eps >= 0.f) || l2_eps > std::numeric_limits<float>::max()) return KDA_ERR_BAD_SHAPE;
+    const uint64_t row = (uint64_t)H * kda::kHeadDim;
+    if ((uint64_t)T_total > kMaxElems / row) return KDA_ERR_BAD_SHAPE;
+    if ((uint64_t)N * 9u * row > kMaxElems) return KDA_ERR_BAD_SHAPE;
+    if (T_total > 0 && (!xq || !xk || !xv || !a_raw || !b_raw || !conv_w || !a_bias || !q ||
+                        !k || !v || !log_alpha || !beta))
+        return KDA_ERR_NULL_ARG;
+    for (const void* p : {xq, xk, xv, a_raw, (const void*)conv_w, (const void*)a_bias,
+                          conv_state_in, (const void*)conv_state_out, (const void*)q,
+                          (const void*)k, (const void*)v, (const void*)log_alpha})
+        if (p && !aligned(p, 16)) return KDA_ERR_MISALIGNED;
+    if ((b_raw && !aligned(b_raw, esize(dt))) || (beta && !aligned(beta, esize(dt))))
+        return KDA_ERR_MISALIGNED;
+    if (cu_seqlens && !aligned(cu_seqlens, 4)) return KDA_ERR_MISALIGNED;
+
+    const uint64_t es = esize(dt);
+    const uint64_t nTok = (uint64_t)T_total * row * es, nB = (uint64_t)T_total * H * es;
+    const uint64_t nState = (uint64_t)N * 9u * row * es;
+    const Span sxq = span(xq, nTok), sxk = span(xk, nTok), sxv = span(xv, nTok),
+               sa = span(a_raw, nTok), sbr = span(b_raw, nB),
+               sw = span(conv_w, T_total > 0 ? 3 * row * 4 * 4 : 0),
+               sbias = span(a_bias, T_total > 0 ? row * 4 : 0),
+               scu = span(cu_seqlens, cu_seqlens ? (uint64_t)(N + 1) * 4 : 0),
+               ssi = span(conv_state_in, conv_state_in ? nState : 0),
+               sso = span(conv_state_out, conv_state_out ? nState : 0), sq = span(q, nTok),
+               sk = span(k, nTok), sv = span(v, nTok), sla = span(log_alpha, nTok),
+               sbeta = span(beta, nB);
+    for (const Span& o : {sq, sk, sv, sla, sbeta, sso})
+        if (overlaps_any(o, {sxq, sxk, sxv, sa, sbr, sw, sbias, scu, ssi})) return KDA_ERR_ALIAS;
+    const Span outs[] = {sq, sk, sv, sla, sbeta, sso};
+    for (int i = 0; i < 6; ++i)
+        for (int j = i + 1; j < 6; ++j)
+            if (overlaps(outs[i], outs[j])) return KDA_ERR_ALIAS;
+
+    kda::PrologueArgs a;
+    a.x[0] = xq;
+    a.x[1] = xk;
+    a.x[2] = xv;
+    a.x[3] = a_raw;
+    a.b_raw = b_raw;
+    a.conv_w = conv_w;
+    a.a_bias = a_bias;
+    a.cu_seqlens = cu_seqlens;
+    a.N = N;
+    a.T_total = T_total;
+    a.H = H;
+    a.state_in = conv_state_in;
+    a.state_out = conv_state_out;
+    a.l2_eps = l2_eps;
+    a.out[0] = q;
+    a.out[1] = k;
+    a.out[2] = v;
+    a.out[3] = log_alpha;
+    a.beta = beta;
+    a.tb = kda::prologue_tokens_per_wave(T_total, H);
+    a.n_tblocks = (int32_t)((T_total + a.tb - 1) / a.tb);
+    if ((uint64_t)a.n_tblocks * (uint64_t)((H + 3) / 4) * 4u + (uint64_t)N >
+        (uint64_t)std::numeric_limits<int32_t>::max() * 4u)
+        return KDA_ERR_BAD_SHAPE;
+    if (T_total == 0 && !conv_state_out) return KDA_OK;
+    if (kda::launch_prologue(a, (int)dt, stream) != hipSuccess) return KDA_ERR_DEVICE;
+    return KDA_OK;
+}
+
+kda_status kda_epilogue(const void* o, const void* g, const float* norm_w, int64_t T_total,
+                        int32_t H, int32_t D, kda_dtype dt, float eps, void* y,
+                        hipStream_t stream) {
+    if (!valid_dtype(dt)) return KDA_ERR_BAD_DTYPE;
+    if (T_total < 0 || H < 1 || H > KDA_MAX_HEADS || D != kda::kHeadDim) return KDA_ERR_BAD_SHAPE;
+    if (!(eps >= 0.f) || eps > std::numeric_limits<float>::max()) return KDA_ERR_BAD_SHAPE;
+    const uint64_t row = (uint64_t)H * kda::kHeadDim;
+    if ((uint64_t)T_total > kMaxElems / row) return KDA_ERR_BAD_SHAPE;
+    if ((uint64_t)T_total * H > (uint64_t)std::numeric_limits<int32_t>::max() * 64u)
+        return KDA_ERR_BAD_SHAPE;
+    if (T_total > 0 && (!o || !g || !norm_w || !y)) return KDA_ERR_NULL_ARG;
+    for (const void* p : {o, g, (const void*)norm_w, (const void*)y})
+        if (p && !aligned(p, 16)) return KDA_ERR_MISALIGNED;
+    const uint64_t n = (uint64_t)T_total * row * esize(dt);
+    const Span so = span(o, n), sg = span(g, n), sy = span(y, n),
+               sw = span(norm_w, T_total > 0 ? row * 4 : 0);
+    // in place over o or g is allowed (each element is read before it is written,
+    // by the same lane); any other overlap is not
+    if ((y != o && overlaps(sy, so)) || (y != g && overlaps(sy, sg)) || overlaps(sy, sw))
+        return KDA_ERR_ALIAS;
+    if (T_total == 0) return KDA_OK;
+    kda::EpilogueArgs a;
+    a.o = o;
+    a.g = g;
+    a.norm_w = norm_w;
+    a.T_total = T_total;
+    a.H = H;
+    a.eps = eps;
+    a.y = y;
+    if (kda::launch_epilogue(a, (int)dt, stream) != hipSuccess) return KDA_ERR_DEVICE;
+    return KDA_OK;
+}
+
 }  // extern "C"

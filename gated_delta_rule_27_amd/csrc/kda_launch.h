@@ -94,4 +94,38 @@ hipError_t launch_decode_multi(const DecodeMultiArgs& a, int dtype, hipStream_t 
 hipError_t launch_segment_scan(const float* M, const float* B, const float* h0, int32_t R,
                                int32_t H, float* S_in, float* S_final, hipStream_t stream);
 
+// Prologue of a KDA layer: projections in, core inputs out (kda_layer.hip).
+struct PrologueArgs {
+    const void* x[4];          // x_q, x_k, x_v, decay logits a: [T, H, 128]
+    const void* b_raw;         // [T, H]
+    const float* conv_w;       // [3 (q, k, v), H, 128, 4]
+    const float* a_bias;       // [H, 128]
+    const int32_t* cu_seqlens; // device, may be null (one sequence)
+    int32_t N;
+    int64_t T_total;
+    int32_t H;
+    const void* state_in;      // [N, 3, 3, H, 128] or null (zero history)
+    void* state_out;           // same layout or null
+    float l2_eps;
+    void* out[4];              // q, k, v, log_alpha: [T, H, 128]
+    void* beta;                // [T, H]
+    int32_t tb;                // tokens per wave (prologue_tokens_per_wave)
+    int32_t n_tblocks;         // ceil(T / tb)
+};
+
+// Epilogue: y = RMSNorm_head(o) * w * sigmoid(g).
+struct EpilogueArgs {
+    const void* o;             // [T, H, 128]
+    const void* g;             // [T, H, 128]
+    const float* norm_w;       // [H, 128]
+    int64_t T_total;
+    int32_t H;
+    float eps;
+    void* y;                   // [T, H, 128]
+};
+
+int32_t prologue_tokens_per_wave(int64_t T_total, int32_t H);
+hipError_t launch_prologue(const PrologueArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_epilogue(const EpilogueArgs& a, int dtype, hipStream_t stream);
+
 }  // namespace kda

@@ -223,6 +223,60 @@ kda_status kda_segment_scan(const float* M, const float* B, const float* h0,
                             float* S_in, float* S_final, hipStream_t stream);
 
 /*
+ * Prologue of a KDA layer: from the outputs of its input projections to the
+ * inputs of kda_chunk_fwd / kda_decode_step ("From GPT-2 to Kimi K3", ch. 6,
+ * "Where q, k, v, alpha, and beta come from"; "An infra-oriented diagram of
+ * Kimi K3", Kimi Delta Attention card; "Kimi K3 Architecture Explained",
+ * "Inside a KDA Layer").  Per packed sequence n of cu_seqlens (as for
+ * kda_chunk_fwd; N = 1 and cu_seqlens NULL for one sequence) and head:
+ *   q, k, v    = Swish(conv(x_q | x_k | x_v)), q and k then divided by
+ *                sqrt(sum over the head's 128 channels of x^2 + l2_eps);
+ *   log_alpha  = -5 sigmoid(a_raw + a_bias), in (-5, 0);
+ *   beta       = sigmoid(b_raw).
+ * conv is depthwise and causal over the tokens of a sequence, width 4:
+ * y_t[c] = sum_{j=0..3} w[c][j] x_{t-3+j}[c] (w[c][3] on the current token),
+ * no bias; inputs before the sequence start come from conv_state_in (the
+ * last three inputs of the previous segment, oldest first) or are zero when
+ * it is NULL.  conv_state_out, when not NULL, receives the last three inputs
+ * of every sequence (an empty sequence carries its history over), ready as
+ * conv_state_in of the next segment or decode step.
+ *
+ *   xq, xk, xv, a_raw, q, k, v, log_alpha : [T_total, H, D]  dt
+ *   b_raw, beta                           : [T_total, H]     dt
+ *   conv_w   : [3 (q, k, v), H, D, 4] fp32
+ *   a_bias   : [H, D] fp32
+ *   conv_state_in / conv_state_out : [N, 3 (q, k, v), 3 (tokens), H, D] dt
+ * D must be 128.  l2_eps must be finite and >= 0 (KDA_ERR_BAD_SHAPE).
+ * No output may overlap an input or another output (KDA_ERR_ALIAS; a
+ * decode loop alternates two history buffers).  Pointers 16-byte aligned,
+ * b_raw / beta element aligned.  Math in fp32, outputs rounded to dt.
+ */
+kda_status kda_prologue(const void* xq, const void* xk, const void* xv,
+                        const void* a_raw, const void* b_raw,
+                        const float* conv_w, const float* a_bias,
+                        const int32_t* cu_seqlens, int32_t N, int64_t T_total,
+                        int32_t H, int32_t D, kda_dtype dt,
+                        const void* conv_state_in, void* conv_state_out,
+                        float l2_eps, void* q, void* k, void* v,
+                        void* log_alpha, void* beta, hipStream_t stream);
+
+/*
+ * Epilogue of a KDA layer ("From GPT-2 to Kimi K3", ch. 6, "A third gate:
+ * control what leaves the module"): head-wise RMSNorm and the full-rank
+ * output gate,
+ *   y = o / sqrt(mean over the head's 128 channels of o^2 + eps)
+ *       * norm_w[h] * sigmoid(g),
+ * where g is the output of the gate projection.
+ *
+ *   o, g, y : [T_total, H, D] dt;  norm_w : [H, D] fp32;  D must be 128.
+ * y may be o or g itself (in place); any other overlap is KDA_ERR_ALIAS.
+ * eps must be finite and >= 0.  Pointers 16-byte aligned.
+ */
+kda_status kda_epilogue(const void* o, const void* g, const float* norm_w,
+                        int64_t T_total, int32_t H, int32_t D, kda_dtype dt,
+                        float eps, void* y, hipStream_t stream);
+
+/*
  * Up to K recurrent steps for each of B sequences in one pass over their
  * states: a short window of tokens per cached sequence, such as a
  * speculative draft.  Verifying a draft must not move the cached state, and

@@ -21,6 +21,13 @@ ch. 5, "K3's lower-bounded decay"):
 * h0 (per-document initial state) and the decode state S ~ N(0, 0.02) fp32
   (0.02 is the standard deviation).
 
+Inputs of the layer prologue / epilogue (the outputs of the layer's
+projections, which are plain GEMMs outside this path): x_q, x_k, x_v, the
+decay logits a and the write logits b ~ N(0, 1); the width-4 convolution
+taps ~ N(0, 0.5^2) (so a tap sum of unit inputs has unit variance); the
+decay bias ~ N(0, 1); a cached convolution history ~ N(0, 1); the core's
+read-out o and the gate logits g ~ N(0, 1); the RMSNorm weight 1 + N(0, 0.1^2).
+
 Every tensor has its own generator, seeded from (seed, tensor id), so the
 shapes of one tensor never shift the stream of another.  Large tensors are
 drawn in slabs of tokens to bound temporary memory; the slab order is fixed,
@@ -32,7 +39,9 @@ import torch
 DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 # Tensor ids for the per-tensor generators.
-_TID = {"q": 1, "k": 2, "v": 3, "log_alpha": 4, "beta": 5, "h0": 6, "S": 7}
+_TID = {"q": 1, "k": 2, "v": 3, "log_alpha": 4, "beta": 5, "h0": 6, "S": 7,
+        "xq": 11, "xk": 12, "xv": 13, "a_raw": 14, "b_raw": 15, "conv_w": 16, "a_bias": 17,
+        "conv_state": 18, "o": 19, "g": 20, "norm_w": 21}
 
 # The five workloads.  "chunk" is the chunk length fixed by a workload (only
 # the tiny one fixes it).
@@ -159,6 +168,38 @@ def decode_inputs(B, H, Dk=128, Dv=128, dtype="bf16", device="cpu", seed=0,
         S[b0:b1].copy_(_normal((b1 - b0, H, Dk, Dv), gen, dev, std=state_std))
     return dict(q=d["q"], k=d["k"], v=d["v"], log_alpha=d["log_alpha"],
                 beta=d["beta"], S=S)
+
+
+def layer_inputs(T, H, D=128, dtype="bf16", device="cpu", seed=0, lengths=None,
+                 conv_state=False):
+    """Inputs of the prologue and epilogue of a KDA layer.
+
+    Returns a dict: xq, xk, xv, a_raw [T, H, D] and b_raw [T, H] (dtype);
+    conv_w [3, H, D, 4] and a_bias [H, D] (fp32); conv_state
+    [N, 3, 3, H, D] (dtype) or None; cu_seqlens int32 [N + 1] or None; o and
+    g [T, H, D] (dtype); norm_w [H, D] (fp32); N."""
+    dt = DTYPES[dtype] if isinstance(dtype, str) else dtype
+    dev = torch.device(device)
+    if lengths is not None:
+        cu = cu_from_lengths(lengths)
+        if int(cu[-1]) != T:
+            raise ValueError("lengths must sum to T")
+        N = len(lengths)
+    else:
+        cu, N = None, 1
+    out = {"N": N, "cu_seqlens": (torch.as_tensor(cu, dtype=torch.int32, device=dev)
+                                  if cu is not None else None)}
+    for name in ("xq", "xk", "xv", "a_raw", "o", "g"):
+        t = torch.empty((T, H, D), dtype=dt, device=dev)
+        out[name] = _fill_tokens(t, _gen(dev, seed, name), dev, "normal")
+    b = torch.empty((T, H), dtype=dt, device=dev)
+    out["b_raw"] = _fill_tokens(b, _gen(dev, seed, "b_raw"), dev, "normal")
+    out["conv_w"] = _normal((3, H, D, 4), _gen(dev, seed, "conv_w"), dev, std=0.5)
+    out["a_bias"] = _normal((H, D), _gen(dev, seed, "a_bias"), dev)
+    out["norm_w"] = _normal((H, D), _gen(dev, seed, "norm_w"), dev, mean=1.0, std=0.1)
+    out["conv_state"] = (_normal((N, 3, 3, H, D), _gen(dev, seed, "conv_state"), dev).to(dt)
+                         if conv_state else None)
+    return out
 
 
 def config_inputs(cfg_id, device="cpu", seed=None):

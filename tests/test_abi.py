@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(L):
     assert {"kda_chunk_fwd", "kda_chunk_fwd_ex", "kda_decode_step",
             "kda_chunk_fwd_workspace_size", "kda_status_str", "kda_abi_version",
             "kda_chunk_fwd_snap", "kda_decode_multi", "kda_segment_summary",
-            "kda_segment_scan"} <= set(names)
+            "kda_segment_scan", "kda_prologue", "kda_epilogue"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -199,6 +199,75 @@ def test_segment_summary_without_q_or_v_passes_validation(L):
 ])
 def test_segment_scan_argument_errors(L, kw, code):
     assert seg_scan(L, **kw) == code
+
+
+def prologue(L, **kw):
+    a = dict(xq=P(0), xk=P(1), xv=P(2), a=P(3), b=P(4), w=P(5), bias=P(6), cu=P(7), N=2,
+             T=100, H=3, D=D, dt=BF16, si=P(8), so=P(9), eps=1e-6, q=P(10), k=P(11), v=P(12),
+             la=P(13), beta=P(14), stream=None)
+    a.update(kw)
+    return L.kda_prologue(a["xq"], a["xk"], a["xv"], a["a"], a["b"], a["w"], a["bias"],
+                          a["cu"], a["N"], a["T"], a["H"], a["D"], a["dt"], a["si"], a["so"],
+                          a["eps"], a["q"], a["k"], a["v"], a["la"], a["beta"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=7), BAD_DTYPE),
+    (dict(D=64), BAD_SHAPE),
+    (dict(N=0), BAD_SHAPE),
+    (dict(T=-1), BAD_SHAPE),
+    (dict(cu=None), BAD_SHAPE),           # N = 2 needs offsets
+    (dict(eps=-1.0), BAD_SHAPE),
+    (dict(eps=float("nan")), BAD_SHAPE),
+    (dict(xk=None), NULL_ARG),
+    (dict(w=None), NULL_ARG),
+    (dict(beta=None), NULL_ARG),
+    (dict(q=P(10, 8)), MISALIGNED),
+    (dict(w=P(5, 4)), MISALIGNED),
+    (dict(b=P(4, 1)), MISALIGNED),
+    (dict(q=P(0)), ALIAS),                # output on an input
+    (dict(so=P(8)), ALIAS),               # history out on history in
+    (dict(k=P(10)), ALIAS),               # two outputs
+    (dict(beta=P(7)), ALIAS),             # beta on the offsets
+])
+def test_prologue_argument_errors(L, kw, code):
+    assert prologue(L, **kw) == code
+
+
+def test_prologue_optional_history_and_empty(L):
+    assert prologue(L, si=None, so=None) == DEVICE     # valid: the launch is what fails
+    assert prologue(L, T=0, xq=None, xk=None, xv=None, a=None, b=None, w=None, bias=None,
+                    q=None, k=None, v=None, la=None, beta=None, so=None) == OK
+    assert prologue(L, T=0, xq=None, xk=None, xv=None, a=None, b=None, w=None, bias=None,
+                    q=None, k=None, v=None, la=None, beta=None) == DEVICE   # history copy
+
+
+def epilogue(L, **kw):
+    a = dict(o=P(0), g=P(1), w=P(2), T=100, H=3, D=D, dt=BF16, eps=1e-5, y=P(3), stream=None)
+    a.update(kw)
+    return L.kda_epilogue(a["o"], a["g"], a["w"], a["T"], a["H"], a["D"], a["dt"], a["eps"],
+                          a["y"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=5), BAD_DTYPE),
+    (dict(D=256), BAD_SHAPE),
+    (dict(H=0), BAD_SHAPE),
+    (dict(eps=-0.5), BAD_SHAPE),
+    (dict(o=None), NULL_ARG),
+    (dict(w=None), NULL_ARG),
+    (dict(y=P(3, 2)), MISALIGNED),
+    (dict(y=P(0, 256)), ALIAS),           # partial overlap with o
+    (dict(y=P(2)), ALIAS),                # over the weights
+])
+def test_epilogue_argument_errors(L, kw, code):
+    assert epilogue(L, **kw) == code
+
+
+def test_epilogue_in_place_and_empty(L):
+    assert epilogue(L, y=P(0)) == DEVICE    # y == o: allowed
+    assert epilogue(L, y=P(1)) == DEVICE    # y == g: allowed
+    assert epilogue(L, T=0, o=None, g=None, w=None, y=None) == OK
 
 
 def decode(L, **kw):
