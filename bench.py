@@ -349,6 +349,33 @@ def layer_elementwise(torch, kda, kda_inputs, dev, stream, steps, warmup, chunk_
     return out
 
 
+def backward(torch, kda, kda_inputs, dev, stream, steps, warmup, fwd_ms):
+    """Backward pass (kda_chunk_bwd) of the 4096-token, 96-head workload:
+    the forward state recursion again (states after every chunk), the
+    reverse recursion of the state gradient, and every chunk's gradients.
+    Algorithmic bytes: the forward inputs and dout read, the five token
+    gradients written (10 rows of 256 B per token and head, plus beta and
+    dbeta); the per-chunk state tables are extra traffic of this design."""
+    T, H = 4096, 96
+    d = kda_inputs.prefill_inputs(T, H, dtype="bf16", device=dev, seed=1008)
+    do = torch.randn((T, H, D), device=dev).to(torch.bfloat16)
+    ws = torch.empty(kda.kda_chunk_bwd_workspace_size(T, 1, H), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        kda.kda_chunk_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], do, workspace=ws)
+
+    wall, ms = time_launches(step, steps, warmup, stream)
+    avg = sum(ms) / len(ms)
+    alg = T * H * (10 * D * 2 + 4)
+    out = {"workload": "kda_backward_T4096_H96_d128_bf16", "ms_per_step": round(avg, 4),
+           "tokens_per_s": round(T * steps / wall, 1), "vs_forward": round(avg / fwd_ms, 2),
+           "algorithmic_bytes": alg, "state_table_bytes": ws.numel(),
+           "hbm_frac_algorithmic": round(alg / (avg * 1e-3) / (HBM_PEAK_GBS * 1e9), 4)}
+    del d, do, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -491,6 +518,8 @@ def main():
         torch.cuda.empty_cache()
 
     if not args.no_extra:
+        out["backward"] = backward(torch, kda, kda_inputs, dev, stream, args.steps, args.warmup,
+                                   avg_ms)
         out["layer_elementwise"] = layer_elementwise(
             torch, kda, kda_inputs, dev, stream, args.steps, args.warmup, avg_ms,
             out["decode"]["ms_per_step"] if "decode" in out else None)

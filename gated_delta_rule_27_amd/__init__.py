@@ -20,6 +20,8 @@ Functions (same names as the C entry points):
 * ``kda_segment_summary`` -> ``(M, B)`` and ``kda_segment_scan`` -> ``(S_in,
   S_final)``  the affine summaries of sequence segments and the scan that
   chains them (context parallelism);
+* ``kda_chunk_bwd`` -> ``(dq, dk, dv, dlog_alpha, dbeta, dh0)``  the
+  backward (training) pass of the chunkwise forward;
 * ``kda_prologue`` and ``kda_epilogue``  the elementwise work of a KDA layer
   around the core (short convolution, Swish, norms, gates);
 * ``kda_chunk_fwd_workspace_size``, ``kda_status_str``, ``kda_abi_version``.
@@ -87,6 +89,11 @@ def lib():
         L.kda_epilogue.restype = ctypes.c_int
         L.kda_epilogue.argtypes = [vp, vp, vp, i64, i32, i32, ctypes.c_int, ctypes.c_float,
                                    vp, vp]
+        L.kda_chunk_bwd_workspace_size.restype = sz
+        L.kda_chunk_bwd_workspace_size.argtypes = [i64, i32, i32, i32, i32, ctypes.c_int]
+        L.kda_chunk_bwd.restype = ctypes.c_int
+        L.kda_chunk_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
+                                    ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         _lib = L
     return _lib
 
@@ -330,6 +337,44 @@ def kda_segment_scan(M, B, h0=None):
     return S_in, S_final
 
 
+def kda_chunk_bwd_workspace_size(T_total, N, H, Dk=HEAD_DIM, Dv=HEAD_DIM, dtype=KDA_BF16):
+    return lib().kda_chunk_bwd_workspace_size(int(T_total), int(N), int(H), int(Dk), int(Dv),
+                                              int(dtype))
+
+
+def kda_chunk_bwd(q, k, v, log_alpha, beta, do, h0=None, cu_seqlens=None, dhT=None, *,
+                  want_dh0=True, workspace=None):
+    """Backward of kda_chunk_fwd for the loss sum(do * o) + sum(dhT * h_T).
+
+    Inputs as kda_chunk_fwd plus do [T, H, 128] (input dtype) and dhT
+    [N, H, 128, 128] fp32 or None.  Returns (dq, dk, dv, dlog_alpha, dbeta,
+    dh0 or None); token gradients in the input dtype, dh0 fp32."""
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("beta", beta),
+                    ("do", do)):
+        _dev(t, name, q.dtype)
+    dt = _dtype_code(q)
+    T, H, Dk = q.shape
+    Dv = v.shape[2]
+    N = 1
+    if cu_seqlens is not None:
+        _dev(cu_seqlens, "cu_seqlens", torch.int32)
+        N = cu_seqlens.numel() - 1
+    _dev(h0, "h0", torch.float32)
+    _dev(dhT, "dhT", torch.float32)
+    dq, dk, dv, dg = (torch.empty_like(x) for x in (q, k, v, log_alpha))
+    db = torch.empty_like(beta)
+    dh0 = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device) if want_dh0 else None
+    ws_bytes = kda_chunk_bwd_workspace_size(T, N, H, Dk, Dv, dt)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    _check(lib().kda_chunk_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0), _ptr(cu_seqlens), N,
+        T, H, Dk, Dv, dt, _ptr(do), _ptr(dhT), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(db),
+        _ptr(dh0), _ptr(workspace), workspace.numel(), _stream(q.device)))
+    return dq, dk, dv, dg, db, dh0
+
+
 def kda_prologue(xq, xk, xv, a_raw, b_raw, conv_w, a_bias, cu_seqlens=None, conv_state=None,
                  *, l2_eps=1e-6, store_state=True, state_out=None):
     """Prologue of a KDA layer: Swish(short conv) for q, k, v (q, k then
@@ -415,6 +460,6 @@ def kda_decode_multi(q, k, v, log_alpha, beta, S, n_tok=None, *, update_state=Tr
 
 __all__ = ["kda_chunk_fwd", "kda_chunk_fwd_snap", "snapshot_index", "kda_decode_step",
            "kda_decode_multi", "kda_segment_summary", "kda_segment_scan", "kda_prologue",
-           "kda_epilogue",
+           "kda_epilogue", "kda_chunk_bwd", "kda_chunk_bwd_workspace_size",
            "kda_chunk_fwd_workspace_size", "kda_status_str", "kda_abi_version", "KDAError",
            "lib", "LIB_PATH"]

@@ -115,7 +115,9 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
     const bool need_v = !(flags & kda::kChunkVZero), need_o = !(flags & kda::kChunkNoOutput);
     if (T_total > 0 && (!k || !log_alpha || !beta || (need_v && !v) || (need_o && (!q || !o))))
         return KDA_ERR_NULL_ARG;
-    if (sr.n_snap > 0 && (!sr.snap || (N > 1 && !sr.snap_cu))) return KDA_ERR_NULL_ARG;
+    if (sr.n_snap > 0 &&
+        (!sr.snap || (N > 1 && !sr.snap_cu && !(flags & kda::kChunkSnapSlots))))
+        return KDA_ERR_NULL_ARG;
     if (sr.snap && !aligned(sr.snap, 16)) return KDA_ERR_MISALIGNED;
     if (sr.snap_cu && !aligned(sr.snap_cu, 4)) return KDA_ERR_MISALIGNED;
 
@@ -345,6 +347,105 @@ kda_status kda_decode_multi(const void* q, const void* k, const void* v, const v
     a.update_state = update_state ? 1 : 0;
     a.o = o;
     if (kda::launch_decode_multi(a, (int)dt, stream) != hipSuccess) return KDA_ERR_DEVICE;
+    return KDA_OK;
+}
+
+size_t kda_chunk_bwd_workspace_size(int64_t T_total, int32_t N, int32_t H, int32_t Dk,
+                                    int32_t Dv, kda_dtype dt) {
+    (void)dt;
+    if (T_total < 0 || N < 1 || H < 1 || Dk != kda::kHeadDim || Dv != kda::kHeadDim) return 0;
+    // the state after every chunk and its gradient, one table entry per chunk
+    return 2u * (size_t)kda::chunk_slots(T_total, N) * (size_t)H * kda::kHeadDim *
+           kda::kHeadDim * sizeof(float);
+}
+
+kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void* log_alpha,
+                         const void* beta, const float* h0, const int32_t* cu_seqlens,
+                         int32_t N, int64_t T_total, int32_t H, int32_t Dk, int32_t Dv,
+                         kda_dtype dt, const void* dout, const float* dhT, void* dq, void* dk,
+                         void* dv, void* dlog_alpha, void* dbeta, float* dh0, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+    if (!valid_dtype(dt)) return KDA_ERR_BAD_DTYPE;
+    if (N < 1 || T_total < 0 || H < 1 || H > KDA_MAX_HEADS || Dk != kda::kHeadDim ||
+        Dv != kda::kHeadDim)
+        return KDA_ERR_BAD_SHAPE;
+    const uint64_t row = (uint64_t)H * kda::kHeadDim;
+    if ((uint64_t)T_total > kMaxElems / row) return KDA_ERR_BAD_SHAPE;
+    const int64_t n_slots = kda::chunk_slots(T_total, N);
+    const uint64_t per = (uint64_t)H * kda::kHeadDim * kda::kHeadDim;
+    if ((uint64_t)n_slots > kMaxElems / per / 2) return KDA_ERR_BAD_SHAPE;
+    if ((uint64_t)n_slots * (uint64_t)H > (uint64_t)std::numeric_limits<uint32_t>::max())
+        return KDA_ERR_BAD_SHAPE;
+    if (T_total > 0 && (!q || !k || !v || !log_alpha || !beta || !dout || !dq || !dk || !dv ||
+                        !dlog_alpha || !dbeta))
+        return KDA_ERR_NULL_ARG;
+    for (const void* p : {dout, (const void*)dhT, (const void*)dq, (const void*)dk,
+                          (const void*)dv, (const void*)dlog_alpha, (const void*)dh0})
+        if (p && !aligned(p, 16)) return KDA_ERR_MISALIGNED;
+    if (dbeta && !aligned(dbeta, esize(dt))) return KDA_ERR_MISALIGNED;
+    const size_t need = kda_chunk_bwd_workspace_size(T_total, N, H, Dk, Dv, dt);
+    if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE;
+    float* states = static_cast<float*>(workspace);
+    float* dstates = states + (size_t)n_slots * per;
+
+    // the forward pass again, keeping the state after every chunk (validates
+    // the forward arguments and the state table against them)
+    SnapReq sr;
+    sr.interval = kda::kChunk;
+    sr.n_snap = n_slots;
+    sr.snap = states;
+    const int32_t fflags = kda::kChunkNoOutput | kda::kChunkSnapSlots;
+    kda_status st = chunk_fwd_impl(q, k, v, log_alpha, beta, h0, cu_seqlens, N, T_total, H, Dk,
+                                   Dv, dt, nullptr, nullptr, nullptr, 0, kda::kChunk, 0, sr,
+                                   fflags, stream, true);
+    if (st != KDA_OK) return st;
+
+    const uint64_t es = esize(dt);
+    const uint64_t nTok = (uint64_t)T_total * row * es, nB = (uint64_t)T_total * H * es;
+    const uint64_t nState = (uint64_t)N * per * 4;
+    const Span sq = span(q, nTok), sk = span(k, nTok), sv = span(v, nTok),
+               sg = span(log_alpha, nTok), sb = span(beta, nB),
+               sh0 = span(h0, h0 ? nState : 0),
+               scu = span(cu_seqlens, cu_seqlens ? (uint64_t)(N + 1) * 4 : 0),
+               sdo = span(dout, nTok), sdhT = span(dhT, dhT ? nState : 0),
+               sws = span(workspace, need), sdq = span(dq, nTok), sdk = span(dk, nTok),
+               sdv = span(dv, nTok), sdg = span(dlog_alpha, nTok), sdb = span(dbeta, nB),
+               sdh0 = span(dh0, dh0 ? nState : 0);
+    const Span outs[] = {sdq, sdk, sdv, sdg, sdb, sdh0};
+    for (int i = 0; i < 6; ++i) {
+        if (overlaps_any(outs[i], {sq, sk, sv, sg, sb, sh0, scu, sdo, sdhT, sws}))
+            return KDA_ERR_ALIAS;
+        for (int j = i + 1; j < 6; ++j)
+            if (overlaps(outs[i], outs[j])) return KDA_ERR_ALIAS;
+    }
+    if (overlaps_any(sws, {sdo, sdhT})) return KDA_ERR_ALIAS;
+
+    st = chunk_fwd_impl(q, k, v, log_alpha, beta, h0, cu_seqlens, N, T_total, H, Dk, Dv, dt,
+                        nullptr, nullptr, nullptr, 0, kda::kChunk, 0, sr, fflags, stream);
+    if (st != KDA_OK) return st;
+    kda::BwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.log_alpha = log_alpha;
+    a.beta = beta;
+    a.h0 = h0;
+    a.cu_seqlens = cu_seqlens;
+    a.N = N;
+    a.T_total = T_total;
+    a.H = H;
+    a.dout = dout;
+    a.dhT = dhT;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.dlog_alpha = dlog_alpha;
+    a.dbeta = dbeta;
+    a.dh0 = dh0;
+    a.states = states;
+    a.dstates = dstates;
+    a.n_slots = n_slots;
+    if (kda::launch_bwd(a, (int)dt, stream) != hipSuccess) return KDA_ERR_DEVICE;
     return KDA_OK;
 }
 

@@ -1,0 +1,740 @@
+// kda_bwd.hip -- backward pass of chunkwise KDA (training) for gfx950.
+//
+// The pages give the forward recurrence only and say training runs the
+// chunkwise mode ("From GPT-2 to Kimi K3", ch. 6, "Training, prefill, and
+// decode use different paths").  The gradients below are the reverse of
+// the chunk form used by the prefill kernels (kda_chunk.hip, header), for
+// one head, a 16-token chunk with incoming state S (row = key channel) and
+// G_r = sum_{s<=r} log alpha_s, E_r = exp(G_r), Gamma = exp(G_15):
+//
+//   Qt = Q o E, Kt = K o E, Kh = K / E, Kv = K o Gamma / E,
+//   W = Kt Kh^T, A = strict_lower(diag(beta) W), M = (I + A)^{-1},
+//   T = M diag(beta), P = lower_incl(Qt Kh^T),
+//   X = V - Kt S, U = T X, O = Qt S + P U, S' = Diag(Gamma) S + Kv^T U.
+//
+// With D = dLoss/dS' (the state gradient arriving from later chunks) and
+// dO, reverse mode gives
+//   dU  = P^T dO + Kv D,           dX = T^T dU,       dV = dX,
+//   dS  = Diag(Gamma) D + Qt^T dO - Kt^T dX           (passed to the chunk before),
+//   dP  = lower_incl(dO U^T),      dT = dU X^T,
+//   dbeta_c = sum_r M_rc dT_rc + sum_{s<c} dA_cs W_cs,  dA = -M^T (dT diag beta) M^T
+//             (strict lower part),  dW = diag(beta) dA,
+//   dQt = dO S^T + dP Kh,          dKt = -dX S^T + dW Kh,
+//   dKh = dP^T Qt + dW^T Kt,       dKv = U D^T,
+//   dq = dQt o E,   dk = dKt o E + dKh / E + dKv o Gamma / E,
+//   dG_r = dQt o Qt + dKt o Kt - dKh o Kh - dKv o Kv   (+ for r = 15:
+//          Gamma o rowsum(D o S) + sum_r dKv_r o Kv_r),
+//   dlog_alpha_s = sum_{r>=s} dG_r.
+// These are checked against the token-by-token reverse-mode oracle.
+//
+// Three launches (the caller's kda_chunk_bwd):
+//  (F) the forward state recursion again, storing the state after every
+//      chunk (the prefill kernel with per-chunk snapshots, no outputs);
+//  (R) bwd_dh_kernel: the reverse recursion of D, one workgroup per
+//      (sequence, head, value-column slice) walking the chunks backwards;
+//      value columns are independent in it, as in the forward.  It stores
+//      the D entering every chunk and returns dh0;
+//  (G) bwd_grad_kernel: every gradient of every chunk at once, one
+//      workgroup per (chunk, head), given the chunk's state S (from F) and
+//      D (from R): no recursion left, so the whole chip works on it.
+// Products contracting over key channels use the state tiles held in
+// accumulator layout (as in the forward); products contracting over value
+// columns (dO S^T, dX S^T, U D^T) read the state rows straight from global
+// memory as B operands (8 consecutive columns per lane).
+//
+// Precision as the forward: bf16 inputs use bf16 MFMA operands with fp32
+// accumulation, fp32 inputs fp32 MFMA; the chain rule and the 16 x 16
+// algebra run in fp32.
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int C = kChunk;  // 16
+
+// ---- generic MFMA helpers over the operand type ---------------------------
+
+// c += A(16 x 128, rows from LDS, k contiguous) * St (128 x 16, accumulator
+// tiles St[it] = rows 16 it .. 16 it + 15)
+__device__ __forceinline__ floatx4 mm_k128(const bf16* arow, const floatx4 (&St)[8], floatx4 c,
+                                           int g) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+        c = mma_bf16_k32(frag_k32(arow, 32 * b, g), acc_frag_k32(St[2 * b], St[2 * b + 1]), c);
+    return c;
+}
+__device__ __forceinline__ floatx4 mm_k128(const float* arow, const floatx4 (&St)[8], floatx4 c,
+                                           int g) {
+#pragma unroll
+    for (int it = 0; it < 8; ++it) c = mma_f32_k16(frag_k16(arow, 16 * it, g), St[it], c);
+    return c;
+}
+
+// c += A(16 x 16 from an LDS row) * b (16 x 16 accumulator tile)
+__device__ __forceinline__ floatx4 mm_k16(const bf16* arow, floatx4 b, floatx4 c, int g) {
+    return mma_bf16_k16(frag_k16(arow, 0, g), acc_frag_k16(b), c);
+}
+__device__ __forceinline__ floatx4 mm_k16(const float* arow, floatx4 b, floatx4 c, int g) {
+    return mma_f32_k16(frag_k16(arow, 0, g), b, c);
+}
+
+// c += A(16 x 128 from an LDS row, k = value column) * R^T where R is a
+// 16 x 128 block of rows of a global fp32 matrix (this lane's row `brow`):
+// the B operand takes 8 (bf16) or 4 (fp32) consecutive columns per lane.
+__device__ __forceinline__ floatx4 mm_rowB(const bf16* arow, const float* brow, floatx4 c,
+                                           int g) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const floatx4 lo = *reinterpret_cast<const floatx4*>(brow + 32 * b + 4 * g);
+        const floatx4 hi = *reinterpret_cast<const floatx4*>(brow + 32 * b + 16 + 4 * g);
+        c = mma_bf16_k32(frag_k32(arow, 32 * b, g), acc_frag_k32(lo, hi), c);
+    }
+    return c;
+}
+__device__ __forceinline__ floatx4 mm_rowB(const float* arow, const float* brow, floatx4 c,
+                                           int g) {
+#pragma unroll
+    for (int it = 0; it < 8; ++it)
+        c = mma_f32_k16(frag_k16(arow, 16 * it, g),
+                        *reinterpret_cast<const floatx4*>(brow + 16 * it + 4 * g), c);
+    return c;
+}
+
+template <typename TOp>
+struct BwdLds {
+    static constexpr int PAD = 16 / (int)sizeof(TOp);
+    static constexpr int KP = kHeadDim + PAD;  // [token][channel] rows
+    static constexpr int CP = C + PAD;         // [.][token] rows
+    static constexpr int FP = C + 4;           // fp32 16 x 16 rows
+};
+
+// Per-chunk preparation shared by both kernels.  Thread i < 128 owns key
+// channel i: running decay E_r, Gamma, and the scaled operands.  Rows past
+// the sequence end carry q = k = 0 and log alpha = 0, so they decay nothing
+// and contribute nothing.
+template <typename TIn>
+__device__ __forceinline__ void load_chunk_channel(const TIn* q, const TIn* k, const TIn* g,
+                                                   size_t base, size_t rowstride, int len,
+                                                   float (&qv)[C], float (&kv)[C],
+                                                   float (&E)[C]) {
+    float cum = 0.f;
+#pragma unroll
+    for (int r = 0; r < C; ++r) {
+        const bool ok = r < len;
+        const size_t off = base + (size_t)r * rowstride;
+        qv[r] = ok ? to_f32(q[off]) : 0.f;
+        kv[r] = ok ? to_f32(k[off]) : 0.f;
+        cum += ok ? to_f32(g[off]) : 0.f;
+        E[r] = __expf(cum);
+    }
+}
+
+// ============================================================================
+// (R) reverse recursion of the state gradient
+// ============================================================================
+// NW waves x NCT column tiles of 16: DV = 16 NW NCT value columns per
+// workgroup.  The inputs of the chunk before are loaded into registers while
+// the current one is processed.
+template <typename TIn, int NW, int NCT>
+__global__ __launch_bounds__(64 * NW) void bwd_dh_kernel(BwdArgs a, int32_t split) {
+    typedef TIn TOp;
+    typedef BwdLds<TOp> L;
+    constexpr int KP = L::KP, CP = L::CP, FP = L::FP;
+    constexpr int NT = 64 * NW;
+    constexpr int DV = 16 * NW * NCT;
+    static_assert(NT >= kHeadDim, "one thread per key channel");
+
+    __shared__ __attribute__((aligned(16))) TOp sKv[C * KP];          // Kv rows
+    __shared__ __attribute__((aligned(16))) TOp sKt[C * KP];          // Kt rows (Gram)
+    __shared__ __attribute__((aligned(16))) TOp sQt[C * KP];          // Qt rows (Gram)
+    __shared__ __attribute__((aligned(16))) TOp sKh[C * KP];          // Kh rows (Gram)
+    __shared__ __attribute__((aligned(16))) TOp sQtT[kHeadDim * CP];  // Qt^T
+    __shared__ __attribute__((aligned(16))) TOp sKtTn[kHeadDim * CP]; // -Kt^T
+    __shared__ __attribute__((aligned(16))) TOp sPt[C * CP];          // P^T
+    __shared__ __attribute__((aligned(16))) TOp sTt[C * CP];          // T^T
+    __shared__ __attribute__((aligned(16))) float sA[C * FP];         // A (fp32)
+    __shared__ float sGam[kHeadDim];
+    __shared__ float sBeta[C];
+
+    const TIn* q = static_cast<const TIn*>(a.q);
+    const TIn* k = static_cast<const TIn*>(a.k);
+    const TIn* lg = static_cast<const TIn*>(a.log_alpha);
+    const TIn* bt = static_cast<const TIn*>(a.beta);
+    const TIn* dout = static_cast<const TIn*>(a.dout);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, g = lane >> 4;
+    const int wg = blockIdx.x;
+    const int slice = wg % split;
+    const int h = (wg / split) % a.H;
+    const int n = wg / (split * a.H);
+    const int64_t bos = a.cu_seqlens ? (int64_t)a.cu_seqlens[n] : 0;
+    const int64_t eos = a.cu_seqlens ? (int64_t)a.cu_seqlens[n + 1] : a.T_total;
+    const int64_t nch = (eos - bos + C - 1) / C;
+    const size_t rowstride = (size_t)a.H * kHeadDim;
+    const size_t headoff = (size_t)h * kHeadDim;
+    const int col0 = slice * DV;
+    const int64_t slot0 = chunk_slot(bos, n);
+    constexpr size_t kState = (size_t)kHeadDim * kHeadDim;
+
+    // D = dLoss / dh_T (or 0): wave w owns columns col0 + 16 (NCT w + ct) + l16
+    floatx4 D[NCT][8];
+    {
+        const float* src = a.dhT ? a.dhT + ((size_t)n * a.H + h) * kState : nullptr;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            const int j = col0 + 16 * (NCT * wave + ct) + l16;
+#pragma unroll
+            for (int it = 0; it < 8; ++it)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    D[ct][it][e] = src ? src[(16 * it + 4 * g + e) * kHeadDim + j] : 0.f;
+        }
+    }
+    // upper triangles of P^T and T^T stay zero
+    for (int idx = tid; idx < C * CP; idx += NT) {
+        sPt[idx] = from_f32<TOp>(0.f);
+        sTt[idx] = from_f32<TOp>(0.f);
+    }
+    const uint32_t dlane = (uint32_t)((4 * g * kHeadDim + col0 + 16 * NCT * wave + l16) * 4);
+
+    // register prefetch of one chunk: channel thread i < 128 takes q, k,
+    // log alpha of channel i for the chunk's 16 tokens; every lane its dO
+    // rows 4g .. 4g+3 of its columns; threads < 16 beta
+    TIn pq[C], pk[C], pg[C], pb = from_f32<TIn>(0.f);
+    TIn pdo[NCT][4];
+    auto fetch = [&](int64_t cc) {
+        const int64_t t0 = bos + C * cc;
+        const int len = (int)((eos - t0) < C ? (eos - t0) : C);
+        if (tid < kHeadDim) {
+#pragma unroll
+            for (int r = 0; r < C; ++r) {
+                const bool ok = r < len;
+                const size_t off = (size_t)(t0 + r) * rowstride + headoff + tid;
+                pq[r] = ok ? q[off] : from_f32<TIn>(0.f);
+                pk[r] = ok ? k[off] : from_f32<TIn>(0.f);
+                pg[r] = ok ? lg[off] : from_f32<TIn>(0.f);
+            }
+        }
+        if (tid < C) pb = tid < len ? bt[(size_t)(t0 + tid) * a.H + h] : from_f32<TIn>(0.f);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            const int j = col0 + 16 * (NCT * wave + ct) + l16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * g + e;
+                pdo[ct][e] = r < len ? dout[(size_t)(t0 + r) * rowstride + headoff + j]
+                                     : from_f32<TIn>(0.f);
+            }
+        }
+    };
+    if (nch > 0) fetch(nch - 1);
+
+    for (int64_t c = nch - 1; c >= 0; --c) {
+        __syncthreads();  // the previous chunk's readers are done with LDS
+        if (tid < kHeadDim) {
+            const int i = tid;
+            float E[C];
+            float cum = 0.f;
+#pragma unroll
+            for (int r = 0; r < C; ++r) {
+                cum += to_f32(pg[r]);
+                E[r] = __expf(cum);
+            }
+            const float gam = E[C - 1];
+            sGam[i] = gam;
+#pragma unroll
+            for (int r = 0; r < C; ++r) {
+                const float inv = 1.f / E[r];
+                const float kr = to_f32(pk[r]), qr = to_f32(pq[r]);
+                const float kt = kr * E[r], qt = qr * E[r];
+                sKt[r * KP + i] = from_f32<TOp>(kt);
+                sQt[r * KP + i] = from_f32<TOp>(qt);
+                sKh[r * KP + i] = from_f32<TOp>(kr * inv);
+                sKv[r * KP + i] = from_f32<TOp>(kr * gam * inv);
+                sQtT[i * CP + r] = from_f32<TOp>(qt);
+                sKtTn[i * CP + r] = from_f32<TOp>(-kt);
+            }
+        }
+        if (tid < C) sBeta[tid] = to_f32(pb);
+        floatx4 dob[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dob[ct][e] = to_f32(pdo[ct][e]);
+        __syncthreads();
+        if (c > 0) fetch(c - 1);   // in flight during the rest of this chunk
+        // Gram tiles: acc(s, r) = sum_i Kh[s][i] X[r][i], X = Kt (A) or Qt (P)
+        if (wave < 2) {
+            const bool isP = wave == 1;
+            const TOp* arow = sKh + l16 * KP;
+            const TOp* brow = (isP ? sQt : sKt) + l16 * KP;
+            floatx4 acc = zero4();
+#pragma unroll
+            for (int kb = 0; kb < kHeadDim; kb += 16) {
+                if constexpr (sizeof(TOp) == 2) {
+                    if (kb % 32 == 0)
+                        acc = mma_bf16_k32(frag_k32(arow, kb, g), frag_k32(brow, kb, g), acc);
+                } else {
+                    acc = mma_f32_k16(frag_k16(arow, kb, g), frag_k16(brow, kb, g), acc);
+                }
+            }
+            const int r = l16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int s = 4 * g + e;
+                if (!isP) sA[r * FP + s] = (s < r) ? acc[e] * sBeta[r] : 0.f;
+                else sPt[s * CP + r] = from_f32<TOp>((s <= r) ? acc[e] : 0.f);
+            }
+        }
+        __syncthreads();
+        // M = (I + A)^{-1} by forward substitution, column c per lane; T^T
+        if (wave == 0 && lane < C) {
+            const int cc = lane;
+            float x[C];
+#pragma unroll
+            for (int rr = 0; rr < C; ++rr) {
+                float v = (rr == cc) ? 1.f : 0.f;
+#pragma unroll
+                for (int s2 = 0; s2 < rr; ++s2) v -= sA[rr * FP + s2] * x[s2];
+                x[rr] = v;
+            }
+            const float bc = sBeta[cc];
+#pragma unroll
+            for (int rr = 0; rr < C; ++rr) sTt[cc * CP + rr] = from_f32<TOp>(x[rr] * bc);
+        }
+        // this chunk's D goes to the table before the update (buffer stores:
+        // one lane offset, the rest in the scalar offset)
+        {
+            const rsrc_t rs = make_rsrc(a.dstates + ((size_t)(slot0 + c) * a.H + h) * kState,
+                                        (int64_t)kState * 4);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                for (int it = 0; it < 8; ++it)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        buf_store_f32(D[ct][it][e], rs, dlane,
+                                      ((16 * it + e) * kHeadDim + 16 * ct) * 4);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            // dU = Kv D + P^T dO;  dX = T^T dU
+            floatx4 dU = mm_k128(sKv + l16 * KP, D[ct], zero4(), g);
+            dU += mm_k16(sPt + l16 * CP, dob[ct], zero4(), g);
+            const floatx4 dX = mm_k16(sTt + l16 * CP, dU, zero4(), g);
+            // D <- Diag(Gamma) D + Qt^T dO - Kt^T dX
+#pragma unroll
+            for (int it = 0; it < 8; ++it) {
+                floatx4 gm;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) gm[e] = sGam[16 * it + 4 * g + e];
+                floatx4 d = D[ct][it] * gm;
+                d = mm_k16(sQtT + (16 * it + l16) * CP, dob[ct], d, g);
+                d = mm_k16(sKtTn + (16 * it + l16) * CP, dX, d, g);
+                D[ct][it] = d;
+            }
+        }
+    }
+    if (a.dh0) {
+        float* dst = a.dh0 + ((size_t)n * a.H + h) * kState;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            const int j = col0 + 16 * (NCT * wave + ct) + l16;
+#pragma unroll
+            for (int it = 0; it < 8; ++it)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    dst[(16 * it + 4 * g + e) * kHeadDim + j] = D[ct][it][e];
+        }
+    }
+}
+
+// ============================================================================
+// (G) all gradients of one chunk
+// ============================================================================
+template <typename TIn>
+__global__ __launch_bounds__(512) void bwd_grad_kernel(BwdArgs a) {
+    typedef TIn TOp;
+    typedef BwdLds<TOp> L;
+    constexpr int KP = L::KP, CP = L::CP, FP = L::FP;
+    constexpr size_t kState = (size_t)kHeadDim * kHeadDim;
+
+    __shared__ __attribute__((aligned(16))) TOp sQt[C * KP];
+    __shared__ __attribute__((aligned(16))) TOp sKt[C * KP];
+    __shared__ __attribute__((aligned(16))) TOp sKh[C * KP];
+    __shared__ __attribute__((aligned(16))) TOp sKv[C * KP];
+    __shared__ __attribute__((aligned(16))) TOp sdO[C * KP];
+    __shared__ __attribute__((aligned(16))) TOp sX[C * KP];
+    __shared__ __attribute__((aligned(16))) TOp sU[C * KP];
+    __shared__ __attribute__((aligned(16))) TOp sdU[C * KP];
+    __shared__ __attribute__((aligned(16))) TOp sdX[C * KP];
+    __shared__ __attribute__((aligned(16))) float sq[C * kHeadDim];
+    __shared__ __attribute__((aligned(16))) float sk[C * kHeadDim];
+    __shared__ __attribute__((aligned(16))) float sE[C * kHeadDim];
+    __shared__ __attribute__((aligned(16))) float sW[C * FP];    // Kt Kh^T (raw)
+    __shared__ __attribute__((aligned(16))) float sM[C * FP];    // (I + A)^{-1}
+    __shared__ __attribute__((aligned(16))) float sdT[C * FP];
+    __shared__ __attribute__((aligned(16))) float sY[C * FP];    // M^T dT diag(beta)
+    __shared__ __attribute__((aligned(16))) float sAW[C * FP];   // dA o W
+    __shared__ __attribute__((aligned(16))) TOp sT[C * CP];     // T
+    __shared__ __attribute__((aligned(16))) TOp sTt[C * CP];    // T^T
+    __shared__ __attribute__((aligned(16))) TOp sPt[C * CP];    // P^T
+    // dP, dP^T, dW, dW^T stay fp32: their products with the decay-scaled keys
+    // feed the log-decay gradient, the most cancellation-prone output
+    __shared__ __attribute__((aligned(16))) float sdPo[C * FP];
+    __shared__ __attribute__((aligned(16))) float sdPt[C * FP];
+    __shared__ __attribute__((aligned(16))) float sdW[C * FP];
+    __shared__ __attribute__((aligned(16))) float sdWt[C * FP];
+    __shared__ float sGam[kHeadDim];
+    __shared__ float sDG[kHeadDim];   // row sums of D o S
+    __shared__ float sBeta[C];
+
+    const TIn* q = static_cast<const TIn*>(a.q);
+    const TIn* k = static_cast<const TIn*>(a.k);
+    const TIn* v = static_cast<const TIn*>(a.v);
+    const TIn* lg = static_cast<const TIn*>(a.log_alpha);
+    const TIn* bt = static_cast<const TIn*>(a.beta);
+    const TIn* dout = static_cast<const TIn*>(a.dout);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;  // 8 waves
+    const int l16 = lane & 15, g = lane >> 4;
+    const int64_t slot = blockIdx.x / a.H;
+    const int h = blockIdx.x % a.H;
+
+    // the sequence and chunk of this slot (uniform binary search)
+    int64_t n = 0;
+    if (a.cu_seqlens) {
+        int64_t lo = 0, hi = a.N - 1;
+        while (lo < hi) {
+            const int64_t mid = (lo + hi + 1) >> 1;
+            if (chunk_slot(a.cu_seqlens[mid], mid) <= slot) lo = mid;
+            else hi = mid - 1;
+        }
+        n = lo;
+    }
+    const int64_t bos = a.cu_seqlens ? (int64_t)a.cu_seqlens[n] : 0;
+    const int64_t eos = a.cu_seqlens ? (int64_t)a.cu_seqlens[n + 1] : a.T_total;
+    const int64_t c = slot - chunk_slot(bos, n);
+    if (c < 0 || C * c >= eos - bos) return;   // a gap of the slot table
+    const int64_t t0 = bos + C * c;
+    const int len = (int)((eos - t0) < C ? (eos - t0) : C);
+    const size_t rowstride = (size_t)a.H * kHeadDim;
+    const size_t headoff = (size_t)h * kHeadDim;
+
+    // S at the chunk start and D at its end
+    const float* Sc = (c == 0) ? (a.h0 ? a.h0 + ((size_t)n * a.H + h) * kState : nullptr)
+                               : a.states + ((size_t)(slot - 1) * a.H + h) * kState;
+    const float* Dd = a.dstates + ((size_t)slot * a.H + h) * kState;
+
+    // the state tiles of phase 3 are loaded first, so their latency overlaps
+    // phases 1 and 2 (column tile J = 16 wave .. +15, accumulator layout)
+    floatx4 St[8], Dt[8];
+    {
+        const int j = 16 * wave + l16;
+#pragma unroll
+        for (int it = 0; it < 8; ++it)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * it + 4 * g + e;
+                St[it][e] = Sc ? Sc[i * kHeadDim + j] : 0.f;
+                Dt[it][e] = Dd[i * kHeadDim + j];
+            }
+    }
+
+    // ---- phase 1: operands ----
+    if (tid < kHeadDim) {
+        const int i = tid;
+        float qv[C], kv[C], E[C];
+        load_chunk_channel(q, k, lg, (size_t)t0 * rowstride + headoff + i, rowstride, len, qv, kv,
+                           E);
+        const float gam = E[C - 1];
+        sGam[i] = gam;
+        sDG[i] = 0.f;
+#pragma unroll
+        for (int r = 0; r < C; ++r) {
+            const float inv = 1.f / E[r];
+            sq[r * kHeadDim + i] = qv[r];
+            sk[r * kHeadDim + i] = kv[r];
+            sE[r * kHeadDim + i] = E[r];
+            sQt[r * KP + i] = from_f32<TOp>(qv[r] * E[r]);
+            sKt[r * KP + i] = from_f32<TOp>(kv[r] * E[r]);
+            sKh[r * KP + i] = from_f32<TOp>(kv[r] * inv);
+            sKv[r * KP + i] = from_f32<TOp>(kv[r] * gam * inv);
+        }
+    }
+    if (tid < C) sBeta[tid] = tid < len ? to_f32(bt[(size_t)(t0 + tid) * a.H + h]) : 0.f;
+    for (int idx = tid; idx < C * kHeadDim; idx += 512) {
+        const int r = idx / kHeadDim, j = idx % kHeadDim;
+        sdO[r * KP + j] =
+            from_f32<TOp>(r < len ? to_f32(dout[(size_t)(t0 + r) * rowstride + headoff + j]) : 0.f);
+    }
+    for (int idx = tid; idx < C * CP; idx += 512) {
+        sT[idx] = sTt[idx] = sPt[idx] = from_f32<TOp>(0.f);
+    }
+    __syncthreads();
+
+    // ---- phase 2: Gram tiles (waves 0, 1) ----
+    if (wave < 2) {
+        const bool isP = wave == 1;
+        const TOp* arow = sKh + l16 * KP;
+        const TOp* brow = (isP ? sQt : sKt) + l16 * KP;
+        floatx4 acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < kHeadDim; kb += 16) {
+            if constexpr (sizeof(TOp) == 2) {
+                if (kb % 32 == 0)
+                    acc = mma_bf16_k32(frag_k32(arow, kb, g), frag_k32(brow, kb, g), acc);
+            } else {
+                acc = mma_f32_k16(frag_k16(arow, kb, g), frag_k16(brow, kb, g), acc);
+            }
+        }
+        const int r = l16;  // acc(s, r): lane holds rows s = 4g + e of column r
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int s = 4 * g + e;
+            if (!isP) sW[r * FP + s] = (s < r) ? acc[e] : 0.f;
+            else sPt[s * CP + r] = from_f32<TOp>((s <= r) ? acc[e] : 0.f);
+        }
+    }
+    __syncthreads();
+    // ---- M = (I + A)^{-1}, T = M diag(beta) (wave 0, one column per lane) ----
+    if (wave == 0 && lane < C) {
+        const int cc = lane;
+        float x[C];
+#pragma unroll
+        for (int rr = 0; rr < C; ++rr) {
+            float val = (rr == cc) ? 1.f : 0.f;
+#pragma unroll
+            for (int s2 = 0; s2 < rr; ++s2) val -= sBeta[rr] * sW[rr * FP + s2] * x[s2];
+            x[rr] = val;
+        }
+        const float bc = sBeta[cc];
+#pragma unroll
+        for (int rr = 0; rr < C; ++rr) {
+            sM[rr * FP + cc] = x[rr];
+            sT[rr * CP + cc] = from_f32<TOp>(x[rr] * bc);
+            sTt[cc * CP + rr] = from_f32<TOp>(x[rr] * bc);
+        }
+    }
+    __syncthreads();
+
+    // ---- phase 3: column tile J = 16 wave .. +15 (accumulator layout) ----
+    {
+        const int j = 16 * wave + l16;
+        float dg_part[8][4];
+#pragma unroll
+        for (int it = 0; it < 8; ++it)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dg_part[it][e] = St[it][e] * Dt[it][e];
+        floatx4 Vt, dOt;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            const size_t off = (size_t)(t0 + r) * rowstride + headoff + j;
+            Vt[e] = r < len ? to_f32(v[off]) : 0.f;
+            dOt[e] = r < len ? to_f32(dout[off]) : 0.f;
+        }
+        const floatx4 KS = mm_k128(sKt + l16 * KP, St, zero4(), g);
+        const floatx4 X = Vt - KS;
+        const floatx4 U = mm_k16(sT + l16 * CP, X, zero4(), g);
+        floatx4 dU = mm_k128(sKv + l16 * KP, Dt, zero4(), g);
+        dU += mm_k16(sPt + l16 * CP, dOt, zero4(), g);
+        const floatx4 dX = mm_k16(sTt + l16 * CP, dU, zero4(), g);
+        TIn* dv = static_cast<TIn*>(a.dv);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            if (r < len) dv[(size_t)(t0 + r) * rowstride + headoff + j] = from_f32<TIn>(dX[e]);
+            sX[r * KP + j] = from_f32<TOp>(X[e]);
+            sU[r * KP + j] = from_f32<TOp>(U[e]);
+            sdU[r * KP + j] = from_f32<TOp>(dU[e]);
+            sdX[r * KP + j] = from_f32<TOp>(dX[e]);
+        }
+        // row sums of D o S over this wave's 16 columns, then across waves
+#pragma unroll
+        for (int it = 0; it < 8; ++it)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float s = dg_part[it][e];
+                s += __shfl_xor(s, 8, 16);
+                s += __shfl_xor(s, 4, 16);
+                s += __shfl_xor(s, 2, 16);
+                s += __shfl_xor(s, 1, 16);
+                if (l16 == 0) atomicAdd(&sDG[16 * it + 4 * g + e], s);
+            }
+    }
+    __syncthreads();
+
+    // ---- phase 4: dT = dU X^T (wave 0), dP = lower_incl(dO U^T) (wave 1) ----
+    if (wave < 2) {
+        const bool isP = wave == 1;
+        const TOp* arow = (isP ? sdO : sdU) + l16 * KP;   // A rows r, k = value column
+        const TOp* brow = (isP ? sU : sX) + l16 * KP;     // B columns r' (rows of X / U)
+        floatx4 acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < kHeadDim; kb += 16) {
+            if constexpr (sizeof(TOp) == 2) {
+                if (kb % 32 == 0)
+                    acc = mma_bf16_k32(frag_k32(arow, kb, g), frag_k32(brow, kb, g), acc);
+            } else {
+                acc = mma_f32_k16(frag_k16(arow, kb, g), frag_k16(brow, kb, g), acc);
+            }
+        }
+        // acc(row = 4g + e, col = l16): element [r][r'] with r = 4g + e, r' = l16
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e, rp = l16;
+            if (!isP) {
+                sdT[r * FP + rp] = acc[e];
+            } else {
+                const float dp = (rp <= r) ? acc[e] : 0.f;
+                sdPo[r * FP + rp] = dp;
+                sdPt[rp * FP + r] = dp;
+            }
+        }
+    }
+    __syncthreads();
+    // ---- phase 4b: the 16 x 16 algebra of the UT transform (fp32) ----
+    // Y = M^T (dT diag beta), dA = -(Y M^T) on the strict lower part
+    if (tid < C * C) {
+        const int r = tid / C, qq = tid % C;
+        float y = 0.f;
+#pragma unroll
+        for (int p = 0; p < C; ++p) y += sM[p * FP + r] * sdT[p * FP + qq];
+        sY[r * FP + qq] = y * sBeta[qq];
+    }
+    __syncthreads();
+    if (tid < C * C) {
+        const int r = tid / C, s = tid % C;
+        float da = 0.f;
+        if (s < r) {
+#pragma unroll
+            for (int qq = 0; qq < C; ++qq) da -= sY[r * FP + qq] * sM[s * FP + qq];
+        }
+        const float dw = sBeta[r] * da;
+        sdW[r * FP + s] = dw;
+        sdWt[s * FP + r] = dw;
+        sAW[r * FP + s] = da * sW[r * FP + s];
+    }
+    __syncthreads();
+    if (tid < C) {
+        const int cc = tid;
+        float db = 0.f;
+#pragma unroll
+        for (int r = 0; r < C; ++r) db += sM[r * FP + cc] * sdT[r * FP + cc];
+#pragma unroll
+        for (int s = 0; s < C; ++s) db += sAW[cc * FP + s];
+        if (cc < len) static_cast<TIn*>(a.dbeta)[(size_t)(t0 + cc) * a.H + h] = from_f32<TIn>(db);
+    }
+
+    // ---- phase 5: key-channel tile I = 16 wave .. +15 ----
+    {
+        const int i = 16 * wave + l16;
+        const float* srow = Sc ? Sc + (size_t)i * kHeadDim : nullptr;
+        const float* drow = Dd + (size_t)i * kHeadDim;
+        floatx4 dQt = zero4(), dKt = zero4(), dKv = zero4();
+        if (srow) {
+            dQt = mm_rowB(sdO + l16 * KP, srow, dQt, g);
+            dKt = mm_rowB(sdX + l16 * KP, srow, dKt, g);
+        }
+        dKv = mm_rowB(sU + l16 * KP, drow, dKv, g);
+        // (small products in fresh tiles, added on the VALU)
+        // (fp32 B columns rebuilt from q, k and E: rows s = 4g .. 4g+3 of channel i)
+        floatx4 cKh, cQt, cKt;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int sr = 4 * g + e;
+            const float E = sE[sr * kHeadDim + i];
+            cKh[e] = sk[sr * kHeadDim + i] / E;
+            cQt[e] = sq[sr * kHeadDim + i] * E;
+            cKt[e] = sk[sr * kHeadDim + i] * E;
+        }
+        dQt += mma_f32_k16(frag_k16(sdPo + l16 * FP, 0, g), cKh, zero4());
+        dKt = mma_f32_k16(frag_k16(sdW + l16 * FP, 0, g), cKh, zero4()) - dKt;
+        floatx4 dKh = mma_f32_k16(frag_k16(sdPt + l16 * FP, 0, g), cQt, zero4());
+        dKh += mma_f32_k16(frag_k16(sdWt + l16 * FP, 0, g), cKt, zero4());
+        // chain rule per (token r = 4g + e, channel i)
+        const float gam = sGam[i];
+        float dG[4], kvk = 0.f;
+        TIn* dq = static_cast<TIn*>(a.dq);
+        TIn* dk = static_cast<TIn*>(a.dk);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            const float E = sE[r * kHeadDim + i], inv = 1.f / E;
+            const float qv = sq[r * kHeadDim + i], kv = sk[r * kHeadDim + i];
+            const float Qt = qv * E, Kt = kv * E, Kh = kv * inv, Kv = kv * gam * inv;
+            const float gq = dQt[e] * E;
+            const float gk = dKt[e] * E + dKh[e] * inv + dKv[e] * gam * inv;
+            dG[e] = dQt[e] * Qt + dKt[e] * Kt - dKh[e] * Kh - dKv[e] * Kv;
+            kvk += dKv[e] * Kv;
+            if (r < len) {
+                const size_t off = (size_t)(t0 + r) * rowstride + headoff + i;
+                dq[off] = from_f32<TIn>(gq);
+                dk[off] = from_f32<TIn>(gk);
+            }
+        }
+        // the chunk-total decay Gamma = exp(G_15)
+        kvk += __shfl_xor(kvk, 16, 64);
+        kvk += __shfl_xor(kvk, 32, 64);
+        if (g == 3) dG[3] += gam * sDG[i] + kvk;
+        // dlog_alpha_s = sum_{r >= s} dG_r: suffix over the lane's rows, then
+        // over the lane groups above it
+        float suf[4];
+        suf[3] = dG[3];
+        suf[2] = suf[3] + dG[2];
+        suf[1] = suf[2] + dG[1];
+        suf[0] = suf[1] + dG[0];
+        const float tot = suf[0];
+        const float t1 = __shfl_xor(tot, 16, 64), t2 = __shfl_xor(tot, 32, 64),
+                    t3 = __shfl_xor(tot, 48, 64);
+        // totals of groups g ^ 1, g ^ 2, g ^ 3; add those with a larger group index
+        float above = 0.f;
+        if ((g ^ 1) > g) above += t1;
+        if ((g ^ 2) > g) above += t2;
+        if ((g ^ 3) > g) above += t3;
+        TIn* dgl = static_cast<TIn*>(a.dlog_alpha);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            if (r < len)
+                dgl[(size_t)(t0 + r) * rowstride + headoff + i] = from_f32<TIn>(suf[e] + above);
+        }
+    }
+}
+
+template <typename TIn, int NW, int NCT>
+hipError_t launch_dh(const BwdArgs& a, hipStream_t stream) {
+    constexpr int split = kHeadDim / (16 * NW * NCT);
+    const int64_t nwg = (int64_t)a.N * a.H * split;
+    if (nwg == 0) return hipSuccess;
+    bwd_dh_kernel<TIn, NW, NCT><<<dim3((unsigned)nwg), dim3(64 * NW), 0, stream>>>(a, split);
+    return hipGetLastError();
+}
+
+template <typename TIn>
+hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
+    // enough chains of the recursion to fill the chip: split the value
+    // columns (independent in it) when there are few (sequence, head) pairs
+    const int64_t chains = (int64_t)a.N * a.H;
+    hipError_t e = chains >= 512   ? launch_dh<TIn, 4, 2>(a, stream)
+                   : chains >= 256 ? launch_dh<TIn, 4, 1>(a, stream)
+                                   : launch_dh<TIn, 2, 1>(a, stream);
+    if (e != hipSuccess) return e;
+    const int64_t nwg = a.n_slots * a.H;
+    if (a.T_total == 0 || nwg == 0) return hipSuccess;
+    bwd_grad_kernel<TIn><<<dim3((unsigned)nwg), dim3(512), 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdArgs& a, int dtype, hipStream_t stream) {
+    return dtype == 0 ? launch_bwd_t<float>(a, stream) : launch_bwd_t<bf16>(a, stream);
+}
+
+}  // namespace kda

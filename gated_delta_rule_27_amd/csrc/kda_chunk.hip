@@ -530,7 +530,9 @@ __global__ __launch_bounds__(64 * NW) void chunk_kernel(
             const int64_t done = t0 + C - bos;  // tokens of the sequence consumed
             const int64_t every = (int64_t)kSnapUnit * snap.every_chunks;
             if (done % every == 0) {
-                const int64_t idx = (snap.snap_cu ? (int64_t)snap.snap_cu[n] : 0) + done / every - 1;
+                const int64_t base = (flags & kChunkSnapSlots) ? chunk_slot(bos, n)
+                                     : snap.snap_cu ? (int64_t)snap.snap_cu[n] : 0;
+                const int64_t idx = base + done / every - 1;
                 if (idx < snap.n_snap) {
                     // buffer stores: one lane offset, the rest in the scalar
                     // offset, so no per-element addresses stay live

@@ -219,7 +219,8 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
         // prefetch distance keeps the memory-counter wait for a chunk's V
         // clear of the output stores of the iterations just before it.
         const int colw0 = col0 + 16 * NCT * wave + l16;  // this lane's first column
-        const int64_t snap_base = snap.snap_cu ? (int64_t)snap.snap_cu[n] : 0;
+        const int64_t snap_base = (flags & kChunkSnapSlots) ? chunk_slot(bos, n)
+                                  : snap.snap_cu ? (int64_t)snap.snap_cu[n] : 0;
         const uint32_t vo_lane = (uint32_t)(((size_t)(4 * g) * rowstride + headoff + colw0) * 2);
         const uint32_t vo_row = (uint32_t)(rowstride * 2);
         const uint32_t snap_lane = (uint32_t)((4 * g * kHeadDim + colw0) * 4);

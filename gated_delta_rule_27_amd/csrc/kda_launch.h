@@ -31,7 +31,20 @@ enum ChunkFlags : int32_t {
     kChunkNoOutput = 1,     // o is not written (may be null)
     kChunkVZero = 2,        // V is taken as zero (v may be null)
     kChunkH0Identity = 4,   // the initial state of every sequence is I
+    kChunkSnapSlots = 8,    // snapshot j of sequence n goes to entry chunk_slot(n) + j
+                            // (with a snapshot after every chunk: the per-chunk
+                            // state store of the backward pass)
 };
+
+constexpr int kChunk = 16;  // tokens per chunk of the chunk kernels and the backward pass
+
+// Entry of chunk c of sequence n (first token bos) in a per-chunk table:
+// bos / 16 + n + c.  Strictly increasing over (n, c) without a scan over
+// the sequence lengths; a table of T / 16 + N + 1 entries holds every chunk.
+__host__ __device__ inline int64_t chunk_slot(int64_t bos, int64_t n) { return bos / kChunk + n; }
+__host__ __device__ inline int64_t chunk_slots(int64_t T_total, int64_t N) {
+    return T_total / kChunk + N + 1;
+}
 
 struct ChunkArgs {
     const void* q;
@@ -123,6 +136,33 @@ struct EpilogueArgs {
     float eps;
     void* y;                   // [T, H, 128]
 };
+
+// Backward pass (kda_bwd.hip): all tensors in the forward's layouts.
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* log_alpha;
+    const void* beta;
+    const float* h0;           // may be null
+    const int32_t* cu_seqlens; // may be null
+    int32_t N;
+    int64_t T_total;
+    int32_t H;
+    const void* dout;          // dLoss / do
+    const float* dhT;          // dLoss / dh_T, may be null
+    void* dq;
+    void* dk;
+    void* dv;
+    void* dlog_alpha;
+    void* dbeta;
+    float* dh0;                // may be null
+    const float* states;       // [n_slots, H, 128, 128]: state after chunk (slot)
+    float* dstates;            // [n_slots, H, 128, 128]: dLoss / d(state after chunk)
+    int64_t n_slots;
+};
+
+hipError_t launch_bwd(const BwdArgs& a, int dtype, hipStream_t stream);
 
 int32_t prologue_tokens_per_wave(int64_t T_total, int32_t H);
 hipError_t launch_prologue(const PrologueArgs& a, int dtype, hipStream_t stream);

@@ -223,6 +223,41 @@ kda_status kda_segment_scan(const float* M, const float* B, const float* h0,
                             float* S_in, float* S_final, hipStream_t stream);
 
 /*
+ * Backward pass of kda_chunk_fwd (training runs the chunkwise mode: "From
+ * GPT-2 to Kimi K3", ch. 6, "Training, prefill, and decode use different
+ * paths").  For the loss  sum(dout * o) + sum(dhT * h_T)  of the forward
+ * pass on the same inputs (same layouts, same packed sequences), writes
+ *   dq, dk, dv, dlog_alpha : [T_total, H, D]  dt
+ *   dbeta                  : [T_total, H]     dt
+ *   dh0                    : [N, H, Dk, Dv]   fp32 (NULL: not written)
+ * from dout [T_total, H, Dv] (dt) and dhT [N, H, Dk, Dv] fp32 (NULL: zero).
+ * The pages give no gradient formulas; they are the reverse mode of the
+ * recurrence, checked against a token-by-token reverse-mode oracle that is
+ * itself pinned by finite differences.
+ *
+ * The workspace (kda_chunk_bwd_workspace_size bytes, 16-byte aligned,
+ * required) holds the state after every 16-token chunk and its gradient:
+ * 2 x (T_total / 16 + N + 1) x H x 64 KiB.  Three launches on `stream`:
+ * the forward state recursion again (storing those states), the reverse
+ * recursion of the state gradient, and all per-chunk gradients at once.
+ * Errors as kda_chunk_fwd; dout and the five token gradients are required
+ * when T_total > 0 (KDA_ERR_NULL_ARG); no output may overlap an input,
+ * another output or the workspace (KDA_ERR_ALIAS); a missing or short
+ * workspace is KDA_ERR_WORKSPACE.
+ */
+size_t kda_chunk_bwd_workspace_size(int64_t T_total, int32_t N, int32_t H,
+                                    int32_t Dk, int32_t Dv, kda_dtype dt);
+
+kda_status kda_chunk_bwd(const void* q, const void* k, const void* v,
+                         const void* log_alpha, const void* beta,
+                         const float* h0, const int32_t* cu_seqlens, int32_t N,
+                         int64_t T_total, int32_t H, int32_t Dk, int32_t Dv,
+                         kda_dtype dt, const void* dout, const float* dhT,
+                         void* dq, void* dk, void* dv, void* dlog_alpha,
+                         void* dbeta, float* dh0, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Prologue of a KDA layer: from the outputs of its input projections to the
  * inputs of kda_chunk_fwd / kda_decode_step ("From GPT-2 to Kimi K3", ch. 6,
  * "Where q, k, v, alpha, and beta come from"; "An infra-oriented diagram of

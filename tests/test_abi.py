@@ -40,7 +40,8 @@ def test_exports_every_declared_symbol(L):
     assert {"kda_chunk_fwd", "kda_chunk_fwd_ex", "kda_decode_step",
             "kda_chunk_fwd_workspace_size", "kda_status_str", "kda_abi_version",
             "kda_chunk_fwd_snap", "kda_decode_multi", "kda_segment_summary",
-            "kda_segment_scan", "kda_prologue", "kda_epilogue"} <= set(names)
+            "kda_segment_scan", "kda_prologue", "kda_epilogue", "kda_chunk_bwd",
+            "kda_chunk_bwd_workspace_size"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -199,6 +200,51 @@ def test_segment_summary_without_q_or_v_passes_validation(L):
 ])
 def test_segment_scan_argument_errors(L, kw, code):
     assert seg_scan(L, **kw) == code
+
+
+def bwd(L, **kw):
+    T, N, H = kw.get("T", 64), kw.get("N", 1), kw.get("H", 2)
+    wsb = L.kda_chunk_bwd_workspace_size(T, N, H, D, D, BF16)
+    a = dict(q=P(0), k=P(1), v=P(2), g=P(3), b=P(4), h0=P(5), cu=None, N=N, T=T, H=H, Dk=D,
+             Dv=D, dt=BF16, do=P(6), dhT=P(7), dq=P(8), dk=P(9), dv=P(10), dg=P(11), db=P(12),
+             dh0=P(13), ws=P(14), wsb=wsb, stream=None)
+    a.update(kw)
+    return L.kda_chunk_bwd(a["q"], a["k"], a["v"], a["g"], a["b"], a["h0"], a["cu"], a["N"],
+                           a["T"], a["H"], a["Dk"], a["Dv"], a["dt"], a["do"], a["dhT"], a["dq"],
+                           a["dk"], a["dv"], a["dg"], a["db"], a["dh0"], a["ws"], a["wsb"],
+                           a["stream"])
+
+
+def test_bwd_workspace_size(L):
+    # 2 tables x (T/16 + N + 1) entries x H x 64 KiB
+    assert L.kda_chunk_bwd_workspace_size(4096, 1, 96, D, D, BF16) == 2 * (256 + 2) * 96 * 65536
+    assert L.kda_chunk_bwd_workspace_size(0, 3, 2, D, D, BF16) == 2 * 4 * 2 * 65536
+    assert L.kda_chunk_bwd_workspace_size(10, 1, 2, 64, D, BF16) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=9), BAD_DTYPE),
+    (dict(Dk=64), BAD_SHAPE),
+    (dict(N=2, cu=None), BAD_SHAPE),
+    (dict(do=None), NULL_ARG),
+    (dict(dg=None), NULL_ARG),
+    (dict(q=None), NULL_ARG),
+    (dict(ws=None), WORKSPACE),
+    (dict(wsb=1024), WORKSPACE),
+    (dict(dq=P(8, 4)), MISALIGNED),
+    (dict(db=P(12, 1)), MISALIGNED),
+    (dict(dq=P(0)), ALIAS),                 # gradient over an input
+    (dict(dk=P(8)), ALIAS),                 # two gradients
+    (dict(dh0=P(14)), ALIAS),               # over the workspace
+    (dict(ws=P(6)), ALIAS),                 # workspace over dout
+    (dict(ws=P(0)), ALIAS),                 # workspace over q (the state table is an output)
+])
+def test_bwd_argument_errors(L, kw, code):
+    assert bwd(L, **kw) == code
+
+
+def test_bwd_optional_arguments(L):
+    assert bwd(L, h0=None, dhT=None, dh0=None) == DEVICE   # valid: the launch is what fails
 
 
 def prologue(L, **kw):
