@@ -137,7 +137,8 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
                scu = span(cu_seqlens, cu_seqlens ? (uint64_t)(N + 1) * 4 : 0),
                so = span(o, nTok * es), shT = span(h_T, h_T ? nState * 4 : 0),
                sws = span(workspace, workspace_bytes);
-    const Span ssn = span(sr.snap, sr.snap ? (uint64_t)sr.n_snap * (nState / N) * 4 : 0),
+    const uint64_t snap_es = (flags & kda::kChunkSnapBf16) ? 2 : 4;
+    const Span ssn = span(sr.snap, sr.snap ? (uint64_t)sr.n_snap * (nState / N) * snap_es : 0),
                sscu = span(sr.snap_cu, sr.snap_cu ? (uint64_t)(N + 1) * 4 : 0);
     if (overlaps_any(so, {sq, sk, sv, sg, sb, sh0, scu, sws, sscu})) return KDA_ERR_ALIAS;
     if (overlaps_any(shT, {sq, sk, sv, sg, sb, sh0, scu, so, sws, sscu})) return KDA_ERR_ALIAS;
@@ -153,6 +154,9 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
     if (dv_split) s = dv_split;
     if (!kda::chunk_config_supported((int)dt, c, s)) return KDA_ERR_BAD_SHAPE;
     if (sr.interval != 0 && sr.interval % c != 0) return KDA_ERR_BAD_SHAPE;
+    // bf16 snapshots exist in the pipelined bf16 kernel only (chunk 16, split 1 or 2)
+    if ((flags & kda::kChunkSnapBf16) && !(dt == KDA_BF16 && c == 16 && s <= 2))
+        return KDA_ERR_BAD_SHAPE;
     if (check_only) return KDA_OK;
 
     kda::ChunkArgs a;
@@ -352,11 +356,13 @@ kda_status kda_decode_multi(const void* q, const void* k, const void* v, const v
 
 size_t kda_chunk_bwd_workspace_size(int64_t T_total, int32_t N, int32_t H, int32_t Dk,
                                     int32_t Dv, kda_dtype dt) {
-    (void)dt;
-    if (T_total < 0 || N < 1 || H < 1 || Dk != kda::kHeadDim || Dv != kda::kHeadDim) return 0;
-    // the state after every chunk and its gradient, one table entry per chunk
+    if (!valid_dtype(dt) || T_total < 0 || N < 1 || H < 1 || Dk != kda::kHeadDim ||
+        Dv != kda::kHeadDim)
+        return 0;
+    // the state after every chunk and its gradient, one table entry per
+    // chunk, in the input dtype (fp32 for fp32 inputs, bf16 for bf16 inputs)
     return 2u * (size_t)kda::chunk_slots(T_total, N) * (size_t)H * kda::kHeadDim *
-           kda::kHeadDim * sizeof(float);
+           kda::kHeadDim * esize(dt);
 }
 
 kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void* log_alpha,
@@ -385,16 +391,17 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void
     if (dbeta && !aligned(dbeta, esize(dt))) return KDA_ERR_MISALIGNED;
     const size_t need = kda_chunk_bwd_workspace_size(T_total, N, H, Dk, Dv, dt);
     if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE;
-    float* states = static_cast<float*>(workspace);
-    float* dstates = states + (size_t)n_slots * per;
+    void* states = workspace;
+    void* dstates = static_cast<unsigned char*>(workspace) + (size_t)n_slots * per * esize(dt);
 
     // the forward pass again, keeping the state after every chunk (validates
     // the forward arguments and the state table against them)
     SnapReq sr;
     sr.interval = kda::kChunk;
     sr.n_snap = n_slots;
-    sr.snap = states;
-    const int32_t fflags = kda::kChunkNoOutput | kda::kChunkSnapSlots;
+    sr.snap = static_cast<float*>(states);
+    const int32_t fflags = kda::kChunkNoOutput | kda::kChunkSnapSlots |
+                           (dt == KDA_BF16 ? kda::kChunkSnapBf16 : 0);
     kda_status st = chunk_fwd_impl(q, k, v, log_alpha, beta, h0, cu_seqlens, N, T_total, H, Dk,
                                    Dv, dt, nullptr, nullptr, nullptr, 0, kda::kChunk, 0, sr,
                                    fflags, stream, true);

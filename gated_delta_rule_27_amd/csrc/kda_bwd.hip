@@ -102,6 +102,8 @@ __device__ __forceinline__ floatx4 mm_rowB(const float* arow, const float* brow,
     return c;
 }
 
+__device__ __forceinline__ bf16 z16() { return (bf16)0.f; }
+
 template <typename TOp>
 struct BwdLds {
     static constexpr int PAD = 16 / (int)sizeof(TOp);
@@ -308,16 +310,28 @@ __global__ __launch_bounds__(64 * NW) void bwd_dh_kernel(BwdArgs a, int32_t spli
         // this chunk's D goes to the table before the update (buffer stores:
         // one lane offset, the rest in the scalar offset)
         {
-            const rsrc_t rs = make_rsrc(a.dstates + ((size_t)(slot0 + c) * a.H + h) * kState,
-                                        (int64_t)kState * 4);
+            const size_t eo = ((size_t)(slot0 + c) * a.H + h) * kState;
+            if constexpr (sizeof(TIn) == 2) {   // bf16 table for bf16 inputs
+                const rsrc_t rs = make_rsrc(static_cast<bf16*>(a.dstates) + eo, (int64_t)kState * 2);
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
+                for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-                for (int it = 0; it < 8; ++it)
+                    for (int it = 0; it < 8; ++it)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        buf_store_f32(D[ct][it][e], rs, dlane,
-                                      ((16 * it + e) * kHeadDim + 16 * ct) * 4);
+                        for (int e = 0; e < 4; ++e)
+                            buf_store_bf16((bf16)D[ct][it][e], rs, dlane / 2,
+                                           ((16 * it + e) * kHeadDim + 16 * ct) * 2);
+            } else {
+                const rsrc_t rs = make_rsrc(static_cast<float*>(a.dstates) + eo, (int64_t)kState * 4);
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                    for (int it = 0; it < 8; ++it)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            buf_store_f32(D[ct][it][e], rs, dlane,
+                                          ((16 * it + e) * kHeadDim + 16 * ct) * 4);
+            }
         }
         __syncthreads();
 #pragma unroll
@@ -427,8 +441,8 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdArgs a) {
 
     // S at the chunk start and D at its end
     const float* Sc = (c == 0) ? (a.h0 ? a.h0 + ((size_t)n * a.H + h) * kState : nullptr)
-                               : a.states + ((size_t)(slot - 1) * a.H + h) * kState;
-    const float* Dd = a.dstates + ((size_t)slot * a.H + h) * kState;
+                               : static_cast<const float*>(a.states) + ((size_t)(slot - 1) * a.H + h) * kState;
+    const float* Dd = static_cast<const float*>(a.dstates) + ((size_t)slot * a.H + h) * kState;
 
     // the state tiles of phase 3 are loaded first, so their latency overlaps
     // phases 1 and 2 (column tile J = 16 wave .. +15, accumulator layout)
@@ -707,6 +721,421 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdArgs a) {
     }
 }
 
+// The bf16 form of (G), staged: the per-chunk tables are bf16 for bf16
+// inputs (the products use bf16 operands anyway), every global read of a
+// work item is a 16-byte load into registers issued while the previous item
+// is computed, then written to LDS (the chunk's state and state gradient,
+// q, k, log alpha as fp32, v and dO); both layouts of the state (tiles over
+// key channels for the products over keys, rows for the products over value
+// columns) are read from LDS.  The row sums of D o S (for the chunk-total
+// decay) accumulate in fp32.
+__global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
+    typedef bf16 TOp;
+    typedef BwdLds<TOp> L;
+    constexpr int KP = L::KP, CP = L::CP, FP = L::FP;
+    constexpr size_t kState = (size_t)kHeadDim * kHeadDim;
+
+    __shared__ __attribute__((aligned(16))) bf16 sS[kHeadDim * KP];   // state, rows i
+    __shared__ __attribute__((aligned(16))) bf16 sD[kHeadDim * KP];   // state gradient
+    __shared__ __attribute__((aligned(16))) bf16 sQt[C * KP];
+    __shared__ __attribute__((aligned(16))) bf16 sKt[C * KP];
+    __shared__ __attribute__((aligned(16))) bf16 sKh[C * KP];
+    __shared__ __attribute__((aligned(16))) bf16 sKv[C * KP];
+    __shared__ __attribute__((aligned(16))) bf16 sV[C * KP];
+    __shared__ __attribute__((aligned(16))) bf16 sdO[C * KP];
+    __shared__ __attribute__((aligned(16))) bf16 sX[C * KP];
+    __shared__ __attribute__((aligned(16))) bf16 sU[C * KP];
+    __shared__ __attribute__((aligned(16))) bf16 sdU[C * KP];
+    __shared__ __attribute__((aligned(16))) bf16 sdX[C * KP];
+    __shared__ __attribute__((aligned(16))) float sq[C * kHeadDim];
+    __shared__ __attribute__((aligned(16))) float sk[C * kHeadDim];
+    __shared__ __attribute__((aligned(16))) float sg[C * kHeadDim];  // log alpha, then E
+    __shared__ __attribute__((aligned(16))) float sW[C * FP];
+    __shared__ __attribute__((aligned(16))) float sM[C * FP];
+    __shared__ __attribute__((aligned(16))) float sdT[C * FP];
+    __shared__ __attribute__((aligned(16))) float sY[C * FP];
+    __shared__ __attribute__((aligned(16))) float sAW[C * FP];
+    __shared__ __attribute__((aligned(16))) float sdPo[C * FP];
+    __shared__ __attribute__((aligned(16))) float sdPt[C * FP];
+    __shared__ __attribute__((aligned(16))) float sdW[C * FP];
+    __shared__ __attribute__((aligned(16))) float sdWt[C * FP];
+    __shared__ __attribute__((aligned(16))) bf16 sT[C * CP];
+    __shared__ __attribute__((aligned(16))) bf16 sTt[C * CP];
+    __shared__ __attribute__((aligned(16))) bf16 sPt[C * CP];
+    __shared__ float sGam[kHeadDim];
+    __shared__ float sDG[kHeadDim];
+    __shared__ float sBeta[C];
+
+    const bf16* q = static_cast<const bf16*>(a.q);
+    const bf16* k = static_cast<const bf16*>(a.k);
+    const bf16* v = static_cast<const bf16*>(a.v);
+    const bf16* lg = static_cast<const bf16*>(a.log_alpha);
+    const bf16* bt = static_cast<const bf16*>(a.beta);
+    const bf16* dout = static_cast<const bf16*>(a.dout);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, g = lane >> 4;
+    const size_t rowstride = (size_t)a.H * kHeadDim;
+    const int64_t n_items = a.n_slots * a.H;
+
+    // A work item is one (table slot, head); slots in the gaps of the table
+    // (past the last chunk of a sequence) are skipped.  The grid is
+    // persistent: workgroup b takes items b, b + grid, ...
+    struct Item {
+        int64_t id, t0;
+        int len, h;
+        const float* S32;   // h0 (the first chunk of a sequence), or null
+        const bf16* S16;    // the state table entry (later chunks), or null
+        const bf16* Dd;
+    };
+    auto locate = [&](int64_t id) {
+        Item it{-1, 0, 0, 0, nullptr, nullptr, nullptr};
+        for (; id < n_items; id += gridDim.x) {
+            const int64_t slot = id / a.H;
+            const int h = (int)(id % a.H);
+            int64_t n = 0;
+            if (a.cu_seqlens) {
+                int64_t lo = 0, hi = a.N - 1;
+                while (lo < hi) {
+                    const int64_t mid = (lo + hi + 1) >> 1;
+                    if (chunk_slot(a.cu_seqlens[mid], mid) <= slot) lo = mid;
+                    else hi = mid - 1;
+                }
+                n = lo;
+            }
+            const int64_t bos = a.cu_seqlens ? (int64_t)a.cu_seqlens[n] : 0;
+            const int64_t eos = a.cu_seqlens ? (int64_t)a.cu_seqlens[n + 1] : a.T_total;
+            const int64_t c = slot - chunk_slot(bos, n);
+            if (c < 0 || C * c >= eos - bos) continue;
+            it.id = id;
+            it.t0 = bos + C * c;
+            it.len = (int)((eos - it.t0) < C ? (eos - it.t0) : C);
+            it.h = h;
+            if (c == 0) it.S32 = a.h0 ? a.h0 + ((size_t)n * a.H + h) * kState : nullptr;
+            else it.S16 = static_cast<const bf16*>(a.states) + ((size_t)(slot - 1) * a.H + h) * kState;
+            it.Dd = static_cast<const bf16*>(a.dstates) + ((size_t)slot * a.H + h) * kState;
+            break;
+        }
+        return it;
+    };
+
+    // staging registers: the next item's global reads are in flight while
+    // the current item is computed.  State rows: thread t takes row t / 4,
+    // 32 columns; token rows: thread t < 256 takes row t / 16, 8 channels.
+    const int si = tid >> 2, sj0 = (tid & 3) * 32;
+    const int tr = (tid & 255) >> 4, tc8 = (tid & 15) * 8;
+    bf16x8 sr8[4], dr8[4];  // this thread's 32 columns of a state row and its gradient
+    float pds = 0.f;        // their partial row sum of D o S (fp32)
+    bf16x8 rq, rk, rg, rv, rdo;
+    float rb = 0.f;
+    auto load = [&](const Item& it) {
+        const size_t ro = (size_t)si * kHeadDim + sj0;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            dr8[m] = *reinterpret_cast<const bf16x8*>(it.Dd + ro + 8 * m);
+            if (it.S16) {
+                sr8[m] = *reinterpret_cast<const bf16x8*>(it.S16 + ro + 8 * m);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) sr8[m][e] = it.S32 ? (bf16)it.S32[ro + 8 * m + e] : z16();
+            }
+        }
+        if (tid < 256 && tr < it.len) {
+            const size_t off = (size_t)(it.t0 + tr) * rowstride + (size_t)it.h * kHeadDim + tc8;
+            rq = *reinterpret_cast<const bf16x8*>(q + off);
+            rk = *reinterpret_cast<const bf16x8*>(k + off);
+            rg = *reinterpret_cast<const bf16x8*>(lg + off);
+            rv = *reinterpret_cast<const bf16x8*>(v + off);
+            rdo = *reinterpret_cast<const bf16x8*>(dout + off);
+        }
+        rb = (tid < it.len) ? (float)bt[(size_t)(it.t0 + tid) * a.H + it.h] : 0.f;
+    };
+    auto pack = [&]() {
+        float ds = 0.f;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ds += (float)sr8[m][e] * (float)dr8[m][e];
+        pds = ds;
+    };
+    auto store = [&](const Item& it) {
+        float ds = pds;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            *reinterpret_cast<bf16x8*>(sS + si * KP + sj0 + 8 * m) = sr8[m];
+            *reinterpret_cast<bf16x8*>(sD + si * KP + sj0 + 8 * m) = dr8[m];
+        }
+        ds += __shfl_xor(ds, 1, 64);
+        ds += __shfl_xor(ds, 2, 64);
+        if ((tid & 3) == 0) sDG[si] = ds;
+        if (tid < 256) {
+            const bool tok = tr < it.len;
+            const bf16 z = (bf16)0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                sq[tr * kHeadDim + tc8 + e] = tok ? (float)rq[e] : 0.f;
+                sk[tr * kHeadDim + tc8 + e] = tok ? (float)rk[e] : 0.f;
+                sg[tr * kHeadDim + tc8 + e] = tok ? (float)rg[e] : 0.f;
+            }
+            *reinterpret_cast<bf16x8*>(sV + tr * KP + tc8) = tok ? rv : bf16x8{z, z, z, z, z, z, z, z};
+            *reinterpret_cast<bf16x8*>(sdO + tr * KP + tc8) =
+                tok ? rdo : bf16x8{z, z, z, z, z, z, z, z};
+        }
+        if (tid < C) sBeta[tid] = rb;
+        for (int idx = tid; idx < C * CP; idx += 512) sT[idx] = sTt[idx] = sPt[idx] = z16();
+    };
+
+    Item cur = locate(blockIdx.x);
+    if (cur.id >= 0) {
+        load(cur);
+        pack();
+    }
+    while (cur.id >= 0) {
+    // lane indices re-derived opaquely each item, so that the compiler does
+    // not hoist every LDS address of the item out of the loop
+    int tid_o = threadIdx.x;
+    asm volatile("" : "+v"(tid_o));
+    const int tid = tid_o, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, g = lane >> 4;
+    const int64_t t0 = cur.t0;
+    const int len = cur.len;
+    const int h = cur.h;
+    const size_t headoff = (size_t)h * kHeadDim;
+    store(cur);
+    __syncthreads();
+    const Item nxt = locate(cur.id + gridDim.x);
+
+    // ---- phase 1: decay and scaled operands (thread = key channel) ----
+    if (tid < kHeadDim) {
+        const int i = tid;
+        float cum = 0.f, E[C];
+#pragma unroll
+        for (int r = 0; r < C; ++r) {
+            cum += sg[r * kHeadDim + i];
+            E[r] = __expf(cum);
+        }
+        const float gam = E[C - 1];
+        sGam[i] = gam;
+#pragma unroll
+        for (int r = 0; r < C; ++r) {
+            const float inv = 1.f / E[r];
+            const float qv = sq[r * kHeadDim + i], kv = sk[r * kHeadDim + i];
+            sg[r * kHeadDim + i] = E[r];
+            sQt[r * KP + i] = (bf16)(qv * E[r]);
+            sKt[r * KP + i] = (bf16)(kv * E[r]);
+            sKh[r * KP + i] = (bf16)(kv * inv);
+            sKv[r * KP + i] = (bf16)(kv * gam * inv);
+        }
+    }
+    __syncthreads();
+
+    if (nxt.id >= 0) load(nxt);   // in flight during phases 2 to 5
+
+    // ---- phase 2: Gram tiles (waves 0, 1) ----
+    if (wave < 2) {
+        const bool isP = wave == 1;
+        const bf16* arow = sKh + l16 * KP;
+        const bf16* brow = (isP ? sQt : sKt) + l16 * KP;
+        floatx4 acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < kHeadDim; kb += 32)
+            acc = mma_bf16_k32(frag_k32(arow, kb, g), frag_k32(brow, kb, g), acc);
+        const int r = l16;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int s = 4 * g + e;
+            if (!isP) sW[r * FP + s] = (s < r) ? acc[e] : 0.f;
+            else sPt[s * CP + r] = (bf16)((s <= r) ? acc[e] : 0.f);
+        }
+    }
+    __syncthreads();
+    if (wave == 0 && lane < C) {
+        const int cc = lane;
+        float x[C];
+#pragma unroll
+        for (int rr = 0; rr < C; ++rr) {
+            float val = (rr == cc) ? 1.f : 0.f;
+#pragma unroll
+            for (int s2 = 0; s2 < rr; ++s2) val -= sBeta[rr] * sW[rr * FP + s2] * x[s2];
+            x[rr] = val;
+        }
+        const float bc = sBeta[cc];
+#pragma unroll
+        for (int rr = 0; rr < C; ++rr) {
+            sM[rr * FP + cc] = x[rr];
+            sT[rr * CP + cc] = (bf16)(x[rr] * bc);
+            sTt[cc * CP + rr] = (bf16)(x[rr] * bc);
+        }
+    }
+    __syncthreads();
+
+    // ---- phase 3: column tile J = 16 wave .. +15 (state tiles from LDS) ----
+    {
+        const int j = 16 * wave + l16;
+        floatx4 KS = zero4(), KvD = zero4();
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            bf16x8 sb, db;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sb[e] = sS[(32 * b + 4 * g + e) * KP + j];
+                sb[4 + e] = sS[(32 * b + 16 + 4 * g + e) * KP + j];
+                db[e] = sD[(32 * b + 4 * g + e) * KP + j];
+                db[4 + e] = sD[(32 * b + 16 + 4 * g + e) * KP + j];
+            }
+            KS = mma_bf16_k32(frag_k32(sKt + l16 * KP, 32 * b, g), sb, KS);
+            KvD = mma_bf16_k32(frag_k32(sKv + l16 * KP, 32 * b, g), db, KvD);
+        }
+        floatx4 Vt, dOt;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            Vt[e] = (float)sV[(4 * g + e) * KP + j];
+            dOt[e] = (float)sdO[(4 * g + e) * KP + j];
+        }
+        const floatx4 X = Vt - KS;
+        const floatx4 U = mm_k16(sT + l16 * CP, X, zero4(), g);
+        const floatx4 dU = KvD + mm_k16(sPt + l16 * CP, dOt, zero4(), g);
+        const floatx4 dX = mm_k16(sTt + l16 * CP, dU, zero4(), g);
+        bf16* dv = static_cast<bf16*>(a.dv);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            if (r < len) dv[(size_t)(t0 + r) * rowstride + headoff + j] = (bf16)dX[e];
+            sX[r * KP + j] = (bf16)X[e];
+            sU[r * KP + j] = (bf16)U[e];
+            sdU[r * KP + j] = (bf16)dU[e];
+            sdX[r * KP + j] = (bf16)dX[e];
+        }
+    }
+    __syncthreads();
+
+    if (nxt.id >= 0) pack();      // the next item's state rows have landed
+
+    // ---- phase 4: dT = dU X^T (wave 0), dP = lower_incl(dO U^T) (wave 1) ----
+    if (wave < 2) {
+        const bool isP = wave == 1;
+        const bf16* arow = (isP ? sdO : sdU) + l16 * KP;
+        const bf16* brow = (isP ? sU : sX) + l16 * KP;
+        floatx4 acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < kHeadDim; kb += 32)
+            acc = mma_bf16_k32(frag_k32(arow, kb, g), frag_k32(brow, kb, g), acc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e, rp = l16;
+            if (!isP) {
+                sdT[r * FP + rp] = acc[e];
+            } else {
+                const float dp = (rp <= r) ? acc[e] : 0.f;
+                sdPo[r * FP + rp] = dp;
+                sdPt[rp * FP + r] = dp;
+            }
+        }
+    }
+    __syncthreads();
+    if (tid < C * C) {
+        const int r = tid / C, qq = tid % C;
+        float y = 0.f;
+#pragma unroll
+        for (int p = 0; p < C; ++p) y += sM[p * FP + r] * sdT[p * FP + qq];
+        sY[r * FP + qq] = y * sBeta[qq];
+    }
+    __syncthreads();
+    if (tid < C * C) {
+        const int r = tid / C, s = tid % C;
+        float da = 0.f;
+        if (s < r) {
+#pragma unroll
+            for (int qq = 0; qq < C; ++qq) da -= sY[r * FP + qq] * sM[s * FP + qq];
+        }
+        const float dw = sBeta[r] * da;
+        sdW[r * FP + s] = dw;
+        sdWt[s * FP + r] = dw;
+        sAW[r * FP + s] = da * sW[r * FP + s];
+    }
+    __syncthreads();
+    if (tid < C) {
+        const int cc = tid;
+        float db = 0.f;
+#pragma unroll
+        for (int r = 0; r < C; ++r) db += sM[r * FP + cc] * sdT[r * FP + cc];
+#pragma unroll
+        for (int s2 = 0; s2 < C; ++s2) db += sAW[cc * FP + s2];
+        if (cc < len) static_cast<bf16*>(a.dbeta)[(size_t)(t0 + cc) * a.H + h] = (bf16)db;
+    }
+
+    // ---- phase 5: key-channel tile I = 16 wave .. +15 ----
+    {
+        const int i = 16 * wave + l16;
+        floatx4 dQt = zero4(), dKt = zero4(), dKv = zero4();
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const bf16x8 sr = frag_k32(sS + i * KP, 32 * b, g);
+            const bf16x8 dr = frag_k32(sD + i * KP, 32 * b, g);
+            dQt = mma_bf16_k32(frag_k32(sdO + l16 * KP, 32 * b, g), sr, dQt);
+            dKt = mma_bf16_k32(frag_k32(sdX + l16 * KP, 32 * b, g), sr, dKt);
+            dKv = mma_bf16_k32(frag_k32(sU + l16 * KP, 32 * b, g), dr, dKv);
+        }
+        floatx4 cKh, cQt, cKt;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int sr2 = 4 * g + e;
+            const float E = sg[sr2 * kHeadDim + i];
+            cKh[e] = sk[sr2 * kHeadDim + i] / E;
+            cQt[e] = sq[sr2 * kHeadDim + i] * E;
+            cKt[e] = sk[sr2 * kHeadDim + i] * E;
+        }
+        dQt += mma_f32_k16(frag_k16(sdPo + l16 * FP, 0, g), cKh, zero4());
+        dKt = mma_f32_k16(frag_k16(sdW + l16 * FP, 0, g), cKh, zero4()) - dKt;
+        floatx4 dKh = mma_f32_k16(frag_k16(sdPt + l16 * FP, 0, g), cQt, zero4());
+        dKh += mma_f32_k16(frag_k16(sdWt + l16 * FP, 0, g), cKt, zero4());
+        const float gam = sGam[i];
+        float dG[4], kvk = 0.f;
+        bf16* dq = static_cast<bf16*>(a.dq);
+        bf16* dk = static_cast<bf16*>(a.dk);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            const float E = sg[r * kHeadDim + i], inv = 1.f / E;
+            const float qv = sq[r * kHeadDim + i], kv = sk[r * kHeadDim + i];
+            const float Qt = qv * E, Kt = kv * E, Kh = kv * inv, Kv = kv * gam * inv;
+            const float gq = dQt[e] * E;
+            const float gk = dKt[e] * E + dKh[e] * inv + dKv[e] * gam * inv;
+            dG[e] = dQt[e] * Qt + dKt[e] * Kt - dKh[e] * Kh - dKv[e] * Kv;
+            kvk += dKv[e] * Kv;
+            if (r < len) {
+                const size_t off = (size_t)(t0 + r) * rowstride + headoff + i;
+                dq[off] = (bf16)gq;
+                dk[off] = (bf16)gk;
+            }
+        }
+        kvk += __shfl_xor(kvk, 16, 64);
+        kvk += __shfl_xor(kvk, 32, 64);
+        if (g == 3) dG[3] += gam * sDG[i] + kvk;
+        float suf[4];
+        suf[3] = dG[3];
+        suf[2] = suf[3] + dG[2];
+        suf[1] = suf[2] + dG[1];
+        suf[0] = suf[1] + dG[0];
+        const float tot = suf[0];
+        const float t1 = __shfl_xor(tot, 16, 64), t2 = __shfl_xor(tot, 32, 64),
+                    t3 = __shfl_xor(tot, 48, 64);
+        float above = 0.f;
+        if ((g ^ 1) > g) above += t1;
+        if ((g ^ 2) > g) above += t2;
+        if ((g ^ 3) > g) above += t3;
+        bf16* dgl = static_cast<bf16*>(a.dlog_alpha);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            if (r < len) dgl[(size_t)(t0 + r) * rowstride + headoff + i] = (bf16)(suf[e] + above);
+        }
+    }
+    __syncthreads();   // the next item's staging rewrites LDS
+    cur = nxt;
+    }
+}
+
 template <typename TIn, int NW, int NCT>
 hipError_t launch_dh(const BwdArgs& a, hipStream_t stream) {
     constexpr int split = kHeadDim / (16 * NW * NCT);
@@ -727,7 +1156,16 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     const int64_t nwg = a.n_slots * a.H;
     if (a.T_total == 0 || nwg == 0) return hipSuccess;
-    bwd_grad_kernel<TIn><<<dim3((unsigned)nwg), dim3(512), 0, stream>>>(a);
+    if constexpr (sizeof(TIn) == 2) {
+        // persistent: one workgroup per compute unit (its LDS allows one)
+        int dev = 0, cus = 256;
+        if (hipGetDevice(&dev) == hipSuccess)
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        const int64_t grid = nwg < (int64_t)cus ? nwg : (int64_t)cus;
+        bwd_grad_kernel_bf16<<<dim3((unsigned)grid), dim3(512), 0, stream>>>(a);
+    }
+    else
+        bwd_grad_kernel<TIn><<<dim3((unsigned)nwg), dim3(512), 0, stream>>>(a);
     return hipGetLastError();
 }
 

@@ -298,17 +298,29 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
                     (int64_t)kWsC * (c + 1) <= seqlen) {
                     const int64_t idx = snap_base + (c + 1) / snap.every_chunks - 1;
                     if (idx < snap.n_snap) {
-                        const rsrc_t rs = make_rsrc(
-                            snap.snap + ((size_t)idx * (size_t)H + h) * (kHeadDim * kHeadDim),
-                            kHeadDim * kHeadDim * 4);
+                        const size_t eo = ((size_t)idx * (size_t)H + h) * (kHeadDim * kHeadDim);
+                        if (flags & kChunkSnapBf16) {
+                            const rsrc_t rs = make_rsrc(reinterpret_cast<bf16*>(snap.snap) + eo,
+                                                        kHeadDim * kHeadDim * 2);
 #pragma unroll
-                        for (int ct = 0; ct < NCT; ++ct)
+                            for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-                            for (int it = 0; it < 8; ++it)
+                                for (int it = 0; it < 8; ++it)
 #pragma unroll
-                                for (int e = 0; e < 4; ++e)
-                                    buf_store_f32(S[ct][it][e], rs, snap_lane,
-                                                  ((16 * it + e) * kHeadDim + 16 * ct) * 4);
+                                    for (int e = 0; e < 4; ++e)
+                                        buf_store_bf16((bf16)S[ct][it][e], rs, snap_lane / 2,
+                                                       ((16 * it + e) * kHeadDim + 16 * ct) * 2);
+                        } else {
+                            const rsrc_t rs = make_rsrc(snap.snap + eo, kHeadDim * kHeadDim * 4);
+#pragma unroll
+                            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                                for (int it = 0; it < 8; ++it)
+#pragma unroll
+                                    for (int e = 0; e < 4; ++e)
+                                        buf_store_f32(S[ct][it][e], rs, snap_lane,
+                                                      ((16 * it + e) * kHeadDim + 16 * ct) * 4);
+                        }
                     }
                 }
             }

@@ -207,6 +207,10 @@ __device__ __forceinline__ bf16x4 buf_load_bf16x4(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ void buf_store_bf16(bf16 x, rsrc_t r, uint32_t off) {
     __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(short, x), r, (int)off, 0, 0);
 }
+// bf16 store at voff (per lane) + soff (uniform)
+__device__ __forceinline__ void buf_store_bf16(bf16 x, rsrc_t r, uint32_t voff, int soff) {
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(short, x), r, (int)voff, soff, 0);
+}
 // fp32 store at voff (per lane) + soff (uniform, e.g. a compile-time constant:
 // it travels in the instruction's scalar offset, not in a vector register)
 __device__ __forceinline__ void buf_store_f32(float x, rsrc_t r, uint32_t voff, int soff) {

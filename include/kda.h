@@ -236,8 +236,9 @@ kda_status kda_segment_scan(const float* M, const float* B, const float* h0,
  * itself pinned by finite differences.
  *
  * The workspace (kda_chunk_bwd_workspace_size bytes, 16-byte aligned,
- * required) holds the state after every 16-token chunk and its gradient:
- * 2 x (T_total / 16 + N + 1) x H x 64 KiB.  Three launches on `stream`:
+ * required) holds the state after every 16-token chunk and its gradient
+ * in the input dtype: 2 x (T_total / 16 + N + 1) x H x 128 x 128 elements
+ * (bf16 tables for bf16 inputs: the products read them as bf16 operands).  Three launches on `stream`:
  * the forward state recursion again (storing those states), the reverse
  * recursion of the state gradient, and all per-chunk gradients at once.
  * Errors as kda_chunk_fwd; dout and the five token gradients are required

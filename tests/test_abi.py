@@ -216,9 +216,11 @@ def bwd(L, **kw):
 
 
 def test_bwd_workspace_size(L):
-    # 2 tables x (T/16 + N + 1) entries x H x 64 KiB
-    assert L.kda_chunk_bwd_workspace_size(4096, 1, 96, D, D, BF16) == 2 * (256 + 2) * 96 * 65536
-    assert L.kda_chunk_bwd_workspace_size(0, 3, 2, D, D, BF16) == 2 * 4 * 2 * 65536
+    # 2 tables x (T/16 + N + 1) entries x H x 128 x 128 in the input dtype
+    assert L.kda_chunk_bwd_workspace_size(4096, 1, 96, D, D, BF16) == 2 * (256 + 2) * 96 * 32768
+    assert L.kda_chunk_bwd_workspace_size(4096, 1, 96, D, D, F32) == 2 * (256 + 2) * 96 * 65536
+    assert L.kda_chunk_bwd_workspace_size(0, 3, 2, D, D, BF16) == 2 * 4 * 2 * 32768
+    assert L.kda_chunk_bwd_workspace_size(10, 1, 2, D, D, 7) == 0
     assert L.kda_chunk_bwd_workspace_size(10, 1, 2, 64, D, BF16) == 0
 
 
