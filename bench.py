@@ -392,6 +392,9 @@ def main():
                     help="skip the 16-document varlen prefill line")
     ap.add_argument("--long", action="store_true",
                     help="also time the 1M-token single-sequence prefill (129 GB of HBM)")
+    ap.add_argument("--section", default=None,
+                    choices=["backward", "layer", "context_parallel", "verify_replay"],
+                    help="time only this section (one JSON object), e.g. under a profiler")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
@@ -409,6 +412,20 @@ def main():
         from gated_delta_rule_27_amd import build
         build.build()
     dev = torch.device("cuda:0")
+    if args.section:
+        stream = torch.cuda.current_stream(dev)
+        if args.section == "backward":
+            res = backward(torch, kda, kda_inputs, dev, stream, args.steps, args.warmup, 1.0)
+            res.pop("vs_forward")
+        elif args.section == "layer":
+            res = layer_elementwise(torch, kda, kda_inputs, dev, stream, args.steps, args.warmup,
+                                    None, None)
+        elif args.section == "context_parallel":
+            res = context_parallel(torch, kda, kda_inputs, dev, stream, args.steps, args.warmup)
+        else:
+            res = verify_replay(torch, kda, kda_inputs, dev, stream, args.steps, args.warmup)
+        print(json.dumps({"section": args.section, **res}), flush=True)
+        return
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
 
