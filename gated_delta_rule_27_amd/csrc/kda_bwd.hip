@@ -104,6 +104,39 @@ __device__ __forceinline__ floatx4 mm_rowB(const float* arow, const float* brow,
 
 __device__ __forceinline__ bf16 z16() { return (bf16)0.f; }
 
+// (I + A)^{-1} of a strictly lower 16 x 16 A, element (row l16, column col)
+// per lane: forward elimination down the columns, the pivot of column sc
+// broadcast along the 16-lane row by DPP (lanes of a row are the rows of
+// one column of the inverse).  `arow` is row l16 of A times `scale`.
+__device__ __forceinline__ float unit_lower_inverse(const float* arow, float scale, int col,
+                                                    int l16) {
+    float a[C];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+        const floatx4 v4 = *reinterpret_cast<const floatx4*>(arow + 4 * q4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[4 * q4 + e] = v4[e] * scale;
+    }
+    float x = (l16 == col) ? 1.f : 0.f;
+    // A[r][sc] = 0 for sc >= r, so lanes above the pivot are unchanged
+    x -= a[0] * row_bcast<0>(x);
+    x -= a[1] * row_bcast<1>(x);
+    x -= a[2] * row_bcast<2>(x);
+    x -= a[3] * row_bcast<3>(x);
+    x -= a[4] * row_bcast<4>(x);
+    x -= a[5] * row_bcast<5>(x);
+    x -= a[6] * row_bcast<6>(x);
+    x -= a[7] * row_bcast<7>(x);
+    x -= a[8] * row_bcast<8>(x);
+    x -= a[9] * row_bcast<9>(x);
+    x -= a[10] * row_bcast<10>(x);
+    x -= a[11] * row_bcast<11>(x);
+    x -= a[12] * row_bcast<12>(x);
+    x -= a[13] * row_bcast<13>(x);
+    x -= a[14] * row_bcast<14>(x);
+    return x;
+}
+
 template <typename TOp>
 struct BwdLds {
     static constexpr int PAD = 16 / (int)sizeof(TOp);
@@ -292,20 +325,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_dh_kernel(BwdArgs a, int32_t spli
             }
         }
         __syncthreads();
-        // M = (I + A)^{-1} by forward substitution, column c per lane; T^T
-        if (wave == 0 && lane < C) {
-            const int cc = lane;
-            float x[C];
-#pragma unroll
-            for (int rr = 0; rr < C; ++rr) {
-                float v = (rr == cc) ? 1.f : 0.f;
-#pragma unroll
-                for (int s2 = 0; s2 < rr; ++s2) v -= sA[rr * FP + s2] * x[s2];
-                x[rr] = v;
-            }
-            const float bc = sBeta[cc];
-#pragma unroll
-            for (int rr = 0; rr < C; ++rr) sTt[cc * CP + rr] = from_f32<TOp>(x[rr] * bc);
+        // M = (I + A)^{-1}, one element per lane (4 columns per wave); T^T
+        for (int col = 4 * wave + g; col < C; col += 4 * NW) {
+            const float x = unit_lower_inverse(sA + l16 * FP, 1.f, col, l16);
+            sTt[col * CP + l16] = from_f32<TOp>(x * sBeta[col]);
         }
         // this chunk's D goes to the table before the update (buffer stores:
         // one lane offset, the rest in the scalar offset)
@@ -515,24 +538,14 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdArgs a) {
         }
     }
     __syncthreads();
-    // ---- M = (I + A)^{-1}, T = M diag(beta) (wave 0, one column per lane) ----
-    if (wave == 0 && lane < C) {
-        const int cc = lane;
-        float x[C];
-#pragma unroll
-        for (int rr = 0; rr < C; ++rr) {
-            float val = (rr == cc) ? 1.f : 0.f;
-#pragma unroll
-            for (int s2 = 0; s2 < rr; ++s2) val -= sBeta[rr] * sW[rr * FP + s2] * x[s2];
-            x[rr] = val;
-        }
-        const float bc = sBeta[cc];
-#pragma unroll
-        for (int rr = 0; rr < C; ++rr) {
-            sM[rr * FP + cc] = x[rr];
-            sT[rr * CP + cc] = from_f32<TOp>(x[rr] * bc);
-            sTt[cc * CP + rr] = from_f32<TOp>(x[rr] * bc);
-        }
+    // ---- M = (I + A)^{-1}, T = M diag(beta) (waves 0-3, one element per lane) ----
+    if (wave < 4) {
+        const int col = 4 * wave + g;
+        const float x = unit_lower_inverse(sW + l16 * FP, sBeta[l16], col, l16);
+        const float bc = sBeta[col];
+        sM[l16 * FP + col] = x;
+        sT[l16 * CP + col] = from_f32<TOp>(x * bc);
+        sTt[col * CP + l16] = from_f32<TOp>(x * bc);
     }
     __syncthreads();
 
@@ -949,23 +962,14 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
         }
     }
     __syncthreads();
-    if (wave == 0 && lane < C) {
-        const int cc = lane;
-        float x[C];
-#pragma unroll
-        for (int rr = 0; rr < C; ++rr) {
-            float val = (rr == cc) ? 1.f : 0.f;
-#pragma unroll
-            for (int s2 = 0; s2 < rr; ++s2) val -= sBeta[rr] * sW[rr * FP + s2] * x[s2];
-            x[rr] = val;
-        }
-        const float bc = sBeta[cc];
-#pragma unroll
-        for (int rr = 0; rr < C; ++rr) {
-            sM[rr * FP + cc] = x[rr];
-            sT[rr * CP + cc] = (bf16)(x[rr] * bc);
-            sTt[cc * CP + rr] = (bf16)(x[rr] * bc);
-        }
+    // M = (I + A)^{-1} with A = diag(beta) W (waves 0-3, one element per lane)
+    if (wave < 4) {
+        const int col = 4 * wave + g;
+        const float x = unit_lower_inverse(sW + l16 * FP, sBeta[l16], col, l16);
+        const float bc = sBeta[col];
+        sM[l16 * FP + col] = x;
+        sT[l16 * CP + col] = (bf16)(x * bc);
+        sTt[col * CP + l16] = (bf16)(x * bc);
     }
     __syncthreads();
 
