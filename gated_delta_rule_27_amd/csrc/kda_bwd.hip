@@ -1154,9 +1154,13 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
     // enough chains of the recursion to fill the chip: split the value
     // columns (independent in it) when there are few (sequence, head) pairs
     const int64_t chains = (int64_t)a.N * a.H;
-    hipError_t e = chains >= 512   ? launch_dh<TIn, 4, 2>(a, stream)
-                   : chains >= 256 ? launch_dh<TIn, 4, 1>(a, stream)
-                                   : launch_dh<TIn, 2, 1>(a, stream);
+    hipError_t e;
+    if constexpr (sizeof(TIn) == 2)
+        e = launch_bwd_dh_ws(a, stream);   // pipelined, kda_bwd_ws.hip
+    else
+        e = chains >= 512   ? launch_dh<TIn, 4, 2>(a, stream)
+            : chains >= 256 ? launch_dh<TIn, 4, 1>(a, stream)
+                            : launch_dh<TIn, 2, 1>(a, stream);
     if (e != hipSuccess) return e;
     const int64_t nwg = a.n_slots * a.H;
     if (a.T_total == 0 || nwg == 0) return hipSuccess;

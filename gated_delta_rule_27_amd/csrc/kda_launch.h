@@ -165,6 +165,8 @@ struct BwdArgs {
 };
 
 hipError_t launch_bwd(const BwdArgs& a, int dtype, hipStream_t stream);
+// the reverse recursion for bf16 inputs, pipelined (kda_bwd_ws.hip)
+hipError_t launch_bwd_dh_ws(const BwdArgs& a, hipStream_t stream);
 
 int32_t prologue_tokens_per_wave(int64_t T_total, int32_t H);
 hipError_t launch_prologue(const PrologueArgs& a, int dtype, hipStream_t stream);

@@ -25,7 +25,7 @@ def usage():
 def test_every_kernel_is_reported(usage):
     names = " ".join(usage)
     for k in ("chunk_ws_kernel", "chunk_kernel", "decode_kernel", "decode_multi_kernel",
-              "segment_scan_kernel", "prologue_kernel", "epilogue_kernel", "bwd_dh_kernel",
+              "segment_scan_kernel", "prologue_kernel", "epilogue_kernel", "bwd_dh_kernel", "bwd_dh_ws_kernel",
               "bwd_grad_kernel"):
         assert k in names, k
 
