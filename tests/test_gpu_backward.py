@@ -95,3 +95,45 @@ def test_backward_full_size_sampled_heads():
     ref = _oracle(d, heads)
     for name, gv, r in zip(NAMES, got, ref):
         check(f"{name} heads {heads}", np.take(np_(gv), list(heads), axis=1), r, TOL["bf16"])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_decay_at_the_bound(dtype):
+    """log alpha = -5 on every channel: a 16-token chunk spans e^-80, the
+    largest reciprocal factor the chunk form meets."""
+    kda = need_gpu()
+    case(f"backward decay at the bound dtype={dtype}")
+    d = _inputs(80, 2, dtype, seed=91)
+    d["log_alpha"].fill_(-5.0)
+    got = _gpu(kda, d)
+    ref = _oracle(d)
+    for name, gv, r in zip(NAMES, got, ref):
+        check(name, np_(gv), r, TOL[dtype])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_no_decay_full_writes(dtype):
+    """log alpha = 0 and beta = 1: the plain delta rule with full overwrites."""
+    kda = need_gpu()
+    case(f"backward no decay, beta = 1, dtype={dtype}")
+    d = _inputs(64, 2, dtype, seed=92)
+    d["log_alpha"].zero_()
+    d["beta"].fill_(1.0)
+    got = _gpu(kda, d)
+    ref = _oracle(d)
+    for name, gv, r in zip(NAMES, got, ref):
+        check(name, np_(gv), r, TOL[dtype])
+
+
+def test_backward_single_token_and_empty():
+    kda = need_gpu()
+    case("backward T=1 H=1, and all-empty sequences")
+    d = _inputs(1, 1, "bf16", seed=93)
+    got = _gpu(kda, d)
+    ref = _oracle(d)
+    for name, gv, r in zip(NAMES, got, ref):
+        check(name, np_(gv), r, TOL["bf16"])
+    e = _inputs(0, 2, "bf16", seed=94, lengths=[0, 0])
+    got = _gpu(kda, e)
+    # no tokens: dh0 is dhT itself
+    assert torch.equal(got[5], e["dhT"])

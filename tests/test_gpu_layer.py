@@ -55,6 +55,8 @@ PROLOGUE_CASES = [
     ("f32", 64, 4, [1] * 64, True),
     ("bf16", 77, 2, [1, 2, 3, 4, 0, 67], True),      # sequences shorter than the window
     ("bf16", 4100, 6, [4000, 100], False),           # several token blocks per wave row
+    ("bf16", 33, 1, [10, 23], True),                 # one head: three dead rows per wave
+    ("f32", 1, 1, None, True),                       # one token
 ]
 
 
