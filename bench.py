@@ -139,6 +139,50 @@ def cpu_baseline(T, H):
             "fp64_tokens_per_s": round(T / dt64, 1), "cpu_model": model, "host_mem_gib": mem_gib}
 
 
+def cpu_oracle_rows(kind):
+    """The CPU oracle of another row of the path, timed on a bounded sample of
+    its workload on this host (a reported baseline, never tuned): returns
+    {value, unit, cores, kind, sample}.  Single-threaded NumPy for the layer
+    and the backward (their oracles are plain NumPy), the multithreaded C
+    oracle for decode."""
+    import kda_inputs
+    import oracle
+    n = kda_inputs.to_numpy
+    if kind == "decode":
+        B, H = 64, 96
+        d = kda_inputs.decode_inputs(B, H, dtype="bf16", device="cpu", seed=2001)
+        args = [n(d[x]) for x in ("q", "k", "v", "log_alpha", "beta", "S")]
+        t0 = time.perf_counter()
+        oracle.decode(*args, precision="f32")
+        dt = time.perf_counter() - t0
+        state = B * H * 128 * 128 * 4 * 2
+        return {"value": round(state / dt / 1e9, 2), "unit": "state GB/s",
+                "cores": oracle.default_threads(), "kind": "oracle",
+                "sample": f"{B} sequences x {H} heads, fp32 C oracle, {dt:.2f} s"}
+    if kind == "backward":
+        from oracle import backward as obwd
+        T, H = 1024, 2
+        d = kda_inputs.prefill_inputs(T, H, dtype="bf16", device="cpu", seed=2002)
+        do = n(kda_inputs.prefill_inputs(T, H, dtype="bf16", device="cpu", seed=2003)["v"])
+        t0 = time.perf_counter()
+        obwd.bwd(*(n(d[x]) for x in ("q", "k", "v", "log_alpha", "beta")), do)
+        dt = time.perf_counter() - t0
+        return {"value": round(T * H / dt, 1), "unit": "token-heads/s", "cores": 1,
+                "kind": "oracle", "sample": f"T={T}, {H} heads, float64 NumPy oracle, {dt:.2f} s"}
+    if kind == "layer":
+        from oracle import layer as olayer
+        T, H = 512, 96
+        d = kda_inputs.layer_inputs(T, H, dtype="bf16", device="cpu", seed=2004)
+        t0 = time.perf_counter()
+        olayer.prologue(*(n(d[x]) for x in ("xq", "xk", "xv", "a_raw", "b_raw", "conv_w",
+                                            "a_bias")))
+        olayer.epilogue(n(d["o"]), n(d["g"]), n(d["norm_w"]))
+        dt = time.perf_counter() - t0
+        return {"value": round(T / dt, 1), "unit": "tokens/s (prologue + epilogue)", "cores": 1,
+                "kind": "oracle", "sample": f"T={T}, {H} heads, float64 NumPy oracle, {dt:.2f} s"}
+    raise ValueError(kind)
+
+
 def median(xs):
     ys = sorted(xs)
     n = len(ys)
@@ -576,6 +620,13 @@ def main():
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(T, H)
+        # the oracle beside the other rows, on bounded samples
+        if "decode" in out:
+            out["decode"]["cpu_oracle"] = cpu_oracle_rows("decode")
+        if "backward" in out:
+            out["backward"]["cpu_oracle"] = cpu_oracle_rows("backward")
+        if "layer_elementwise" in out:
+            out["layer_elementwise"]["cpu_oracle"] = cpu_oracle_rows("layer")
     print(json.dumps(out), flush=True)
 
 
