@@ -52,6 +52,8 @@ namespace kda {
 
 namespace {
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 constexpr int C = kChunk;  // 16
 
 // ---- generic MFMA helpers over the operand type ---------------------------
@@ -776,7 +778,6 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) bf16 sTt[C * CP];
     __shared__ __attribute__((aligned(16))) bf16 sPt[C * CP];
     __shared__ float sGam[kHeadDim];
-    __shared__ float sDG[kHeadDim];
     __shared__ float sBeta[C];
 
     const bf16* q = static_cast<const bf16*>(a.q);
@@ -833,25 +834,20 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
     };
 
     // staging registers: the next item's global reads are in flight while
-    // the current item is computed.  State rows: thread t takes row t / 4,
-    // 32 columns; token rows: thread t < 256 takes row t / 16, 8 channels.
-    const int si = tid >> 2, sj0 = (tid & 3) * 32;
+    // the current item is computed.  State: instruction m of wave w reads
+    // the contiguous kilobyte (4 w + m) of the table entry, lane = 8
+    // columns of row (4 w + m) * 4 + lane / 16; token rows: thread t < 256
+    // takes row t / 16, 8 channels.
     const int tr = (tid & 255) >> 4, tc8 = (tid & 15) * 8;
-    bf16x8 sr8[4], dr8[4];  // this thread's 32 columns of a state row and its gradient
-    float pds = 0.f;        // their partial row sum of D o S (fp32)
+    bf16x8 sr8[4], dr8[4];  // this thread's four 8-column pieces of the state and its gradient
     bf16x8 rq, rk, rg, rv, rdo;
-    float rb = 0.f;
+    bf16 rb;   // raw: a conversion here would wait for every load in flight
+    auto state_off = [&](int m) { return (size_t)((wave * 4 + m) * 64 + lane) * 8; };
     auto load = [&](const Item& it) {
-        const size_t ro = (size_t)si * kHeadDim + sj0;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            dr8[m] = *reinterpret_cast<const bf16x8*>(it.Dd + ro + 8 * m);
-            if (it.S16) {
-                sr8[m] = *reinterpret_cast<const bf16x8*>(it.S16 + ro + 8 * m);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) sr8[m][e] = it.S32 ? (bf16)it.S32[ro + 8 * m + e] : z16();
-            }
+            dr8[m] = *reinterpret_cast<const bf16x8*>(it.Dd + state_off(m));
+            if (it.S16) sr8[m] = *reinterpret_cast<const bf16x8*>(it.S16 + state_off(m));
         }
         if (tid < 256 && tr < it.len) {
             const size_t off = (size_t)(it.t0 + tr) * rowstride + (size_t)it.h * kHeadDim + tc8;
@@ -861,47 +857,88 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
             rv = *reinterpret_cast<const bf16x8*>(v + off);
             rdo = *reinterpret_cast<const bf16x8*>(dout + off);
         }
-        rb = (tid < it.len) ? (float)bt[(size_t)(it.t0 + tid) * a.H + it.h] : 0.f;
+        if (tid < it.len) rb = bt[(size_t)(it.t0 + tid) * a.H + it.h];
     };
-    auto pack = [&]() {
-        float ds = 0.f;
+    // a sequence's first chunk starts from h0 (fp32) or zero; read when the
+    // item is packed, as eight 16-byte loads with one wait
+    auto pack = [&](const Item& it) {
+        if (it.S16) return;
+        if (!it.S32) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
+            for (int m = 0; m < 4; ++m)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) ds += (float)sr8[m][e] * (float)dr8[m][e];
-        pds = ds;
-    };
-    auto store = [&](const Item& it) {
-        float ds = pds;
+                for (int e = 0; e < 8; ++e) sr8[m][e] = z16();
+            return;
+        }
+        float4 f[8];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            *reinterpret_cast<bf16x8*>(sS + si * KP + sj0 + 8 * m) = sr8[m];
-            *reinterpret_cast<bf16x8*>(sD + si * KP + sj0 + 8 * m) = dr8[m];
+            const float4* src = reinterpret_cast<const float4*>(it.S32 + state_off(m));
+            f[2 * m] = src[0];
+            f[2 * m + 1] = src[1];
         }
-        ds += __shfl_xor(ds, 1, 64);
-        ds += __shfl_xor(ds, 2, 64);
-        if ((tid & 3) == 0) sDG[si] = ds;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const float4 lo = f[2 * m], hi = f[2 * m + 1];
+            sr8[m] = bf16x8{(bf16)lo.x, (bf16)lo.y, (bf16)lo.z, (bf16)lo.w,
+                            (bf16)hi.x, (bf16)hi.y, (bf16)hi.z, (bf16)hi.w};
+        }
+    };
+    auto store = [&](const Item& it) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int row = (wave * 4 + m) * 4 + (lane >> 4), col = (lane & 15) * 8;
+            *reinterpret_cast<bf16x8*>(sS + row * KP + col) = sr8[m];
+            *reinterpret_cast<bf16x8*>(sD + row * KP + col) = dr8[m];
+        }
         if (tid < 256) {
             const bool tok = tr < it.len;
             const bf16 z = (bf16)0.f;
+            float4 fq[2], fk[2], fg[2];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                sq[tr * kHeadDim + tc8 + e] = tok ? (float)rq[e] : 0.f;
-                sk[tr * kHeadDim + tc8 + e] = tok ? (float)rk[e] : 0.f;
-                sg[tr * kHeadDim + tc8 + e] = tok ? (float)rg[e] : 0.f;
+            for (int hh = 0; hh < 2; ++hh) {
+                const int e = 4 * hh;
+                fq[hh] = tok ? float4{(float)rq[e], (float)rq[e + 1], (float)rq[e + 2], (float)rq[e + 3]}
+                             : float4{0.f, 0.f, 0.f, 0.f};
+                fk[hh] = tok ? float4{(float)rk[e], (float)rk[e + 1], (float)rk[e + 2], (float)rk[e + 3]}
+                             : float4{0.f, 0.f, 0.f, 0.f};
+                fg[hh] = tok ? float4{(float)rg[e], (float)rg[e + 1], (float)rg[e + 2], (float)rg[e + 3]}
+                             : float4{0.f, 0.f, 0.f, 0.f};
+                *reinterpret_cast<float4*>(sq + tr * kHeadDim + tc8 + e) = fq[hh];
+                *reinterpret_cast<float4*>(sk + tr * kHeadDim + tc8 + e) = fk[hh];
+                *reinterpret_cast<float4*>(sg + tr * kHeadDim + tc8 + e) = fg[hh];
             }
             *reinterpret_cast<bf16x8*>(sV + tr * KP + tc8) = tok ? rv : bf16x8{z, z, z, z, z, z, z, z};
             *reinterpret_cast<bf16x8*>(sdO + tr * KP + tc8) =
                 tok ? rdo : bf16x8{z, z, z, z, z, z, z, z};
         }
-        if (tid < C) sBeta[tid] = rb;
+        if (tid < C) sBeta[tid] = tid < it.len ? (float)rb : 0.f;
         for (int idx = tid; idx < C * CP; idx += 512) sT[idx] = sTt[idx] = sPt[idx] = z16();
     };
+    // dq, dk and dlog alpha of an item are staged in LDS (over its Q~, K~
+    // and K^ tiles, free by then) and written with 16-byte stores while the
+    // next item is staged
+    bf16* const g_dq = static_cast<bf16*>(a.dq);
+    bf16* const g_dk = static_cast<bf16*>(a.dk);
+    bf16* const g_dla = static_cast<bf16*>(a.dlog_alpha);
+    auto write_out = [&](const Item& it) {
+        // 3 tiles x 16 rows x 16 pieces: waves 0-3 dq, 4-7 dk, then 0-3 dlog alpha
+        const int row = (tid >> 4) & 15, col = (tid & 15) * 8;
+        if (row < it.len) {
+            const size_t off = (size_t)(it.t0 + row) * rowstride + (size_t)it.h * kHeadDim + col;
+            const bf16* src = (tid < 256 ? sQt : sKt) + row * KP + col;
+            *reinterpret_cast<bf16x8*>((tid < 256 ? g_dq : g_dk) + off) =
+                *reinterpret_cast<const bf16x8*>(src);
+            if (tid < 256)
+                *reinterpret_cast<bf16x8*>(g_dla + off) =
+                    *reinterpret_cast<const bf16x8*>(sKh + row * KP + col);
+        }
+    };
 
-    Item cur = locate(blockIdx.x);
+    Item cur = locate(blockIdx.x), prev{-1, 0, 0, 0, nullptr, nullptr, nullptr};
     if (cur.id >= 0) {
         load(cur);
-        pack();
+        pack(cur);
     }
     while (cur.id >= 0) {
     // lane indices re-derived opaquely each item, so that the compiler does
@@ -913,34 +950,52 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
     const int64_t t0 = cur.t0;
     const int len = cur.len;
     const int h = cur.h;
-    const size_t headoff = (size_t)h * kHeadDim;
+    if (prev.id >= 0) write_out(prev);
     store(cur);
     __syncthreads();
     const Item nxt = locate(cur.id + gridDim.x);
 
-    // ---- phase 1: decay and scaled operands (thread = key channel) ----
-    if (tid < kHeadDim) {
-        const int i = tid;
-        float cum = 0.f, E[C];
+    // ---- phase 1: decay and scaled operands (thread = key channel i and
+    // rows 4 qr .. 4 qr + 3; the running sum is taken from row 0 in order) ----
+    float Eq[4];
+    {
+        const int i = tid & 127;
+        const int qr = __builtin_amdgcn_readfirstlane(tid >> 7);   // wave-uniform
+        float x[C], run[C], tot = 0.f;
 #pragma unroll
         for (int r = 0; r < C; ++r) {
-            cum += sg[r * kHeadDim + i];
-            E[r] = __expf(cum);
+            x[r] = sg[r * kHeadDim + i];
+            tot += x[r];
+            run[r] = tot;
         }
-        const float gam = E[C - 1];
-        sGam[i] = gam;
+        const float gam = __expf(tot);
+        if (qr == 0) sGam[i] = gam;
+        // the running sum before row 4 qr, and the rows' log decays
+        const float pre = qr == 0 ? 0.f : qr == 1 ? run[3] : qr == 2 ? run[7] : run[11];
+        float xr[4];
 #pragma unroll
-        for (int r = 0; r < C; ++r) {
-            const float inv = 1.f / E[r];
+        for (int e = 0; e < 4; ++e)
+            xr[e] = qr == 0 ? x[e] : qr == 1 ? x[4 + e] : qr == 2 ? x[8 + e] : x[12 + e];
+        float cum = pre;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 4 * qr + e;
+            cum += xr[e];
+            const float E = __expf(cum), inv = __builtin_amdgcn_rcpf(E);
+            Eq[e] = E;
             const float qv = sq[r * kHeadDim + i], kv = sk[r * kHeadDim + i];
-            sg[r * kHeadDim + i] = E[r];
-            sQt[r * KP + i] = (bf16)(qv * E[r]);
-            sKt[r * KP + i] = (bf16)(kv * E[r]);
+            sQt[r * KP + i] = (bf16)(qv * E);
+            sKt[r * KP + i] = (bf16)(kv * E);
             sKh[r * KP + i] = (bf16)(kv * inv);
             sKv[r * KP + i] = (bf16)(kv * gam * inv);
         }
     }
     __syncthreads();
+    {   // log alpha is no longer read: keep E in its place
+        const int i = tid & 127, qr = tid >> 7;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sg[(4 * qr + e) * kHeadDim + i] = Eq[e];
+    }
 
     if (nxt.id >= 0) load(nxt);   // in flight during phases 2 to 5
 
@@ -1000,11 +1055,9 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
         const floatx4 U = mm_k16(sT + l16 * CP, X, zero4(), g);
         const floatx4 dU = KvD + mm_k16(sPt + l16 * CP, dOt, zero4(), g);
         const floatx4 dX = mm_k16(sTt + l16 * CP, dU, zero4(), g);
-        bf16* dv = static_cast<bf16*>(a.dv);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = 4 * g + e;
-            if (r < len) dv[(size_t)(t0 + r) * rowstride + headoff + j] = (bf16)dX[e];
             sX[r * KP + j] = (bf16)X[e];
             sU[r * KP + j] = (bf16)U[e];
             sdU[r * KP + j] = (bf16)dU[e];
@@ -1013,9 +1066,17 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
     }
     __syncthreads();
 
-    if (nxt.id >= 0) pack();      // the next item's state rows have landed
+    if (nxt.id >= 0) pack(nxt);
 
-    // ---- phase 4: dT = dU X^T (wave 0), dP = lower_incl(dO U^T) (wave 1) ----
+    // ---- phase 4: dT = dU X^T (wave 0), dP = lower_incl(dO U^T) (wave 1);
+    // waves 4 to 7 write dv = dX from its LDS tile with 16-byte stores ----
+    if (wave >= 4) {
+        const int u = tid - 256, row = u >> 4, col = (u & 15) * 8;
+        if (row < len)
+            *reinterpret_cast<bf16x8*>(static_cast<bf16*>(a.dv) + (size_t)(t0 + row) * rowstride +
+                                       (size_t)h * kHeadDim + col) =
+                *reinterpret_cast<const bf16x8*>(sdX + row * KP + col);
+    }
     if (wave < 2) {
         const bool isP = wave == 1;
         const bf16* arow = (isP ? sdO : sdU) + l16 * KP;
@@ -1072,22 +1133,30 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
     {
         const int i = 16 * wave + l16;
         floatx4 dQt = zero4(), dKt = zero4(), dKv = zero4();
+        float ds = 0.f;   // this lane's part of sum_j D[i][j] S[i][j]
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const bf16x8 sr = frag_k32(sS + i * KP, 32 * b, g);
             const bf16x8 dr = frag_k32(sD + i * KP, 32 * b, g);
+#pragma unroll
+            for (int e = 0; e < 8; e += 2)
+                ds = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{sr[e], sr[e + 1]},
+                                                     bf16x2{dr[e], dr[e + 1]}, ds, false);
             dQt = mma_bf16_k32(frag_k32(sdO + l16 * KP, 32 * b, g), sr, dQt);
             dKt = mma_bf16_k32(frag_k32(sdX + l16 * KP, 32 * b, g), sr, dKt);
             dKv = mma_bf16_k32(frag_k32(sU + l16 * KP, 32 * b, g), dr, dKv);
         }
-        floatx4 cKh, cQt, cKt;
+        floatx4 cKh, cQt, cKt, cE, cInv, cq, ck;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int sr2 = 4 * g + e;
-            const float E = sg[sr2 * kHeadDim + i];
-            cKh[e] = sk[sr2 * kHeadDim + i] / E;
-            cQt[e] = sq[sr2 * kHeadDim + i] * E;
-            cKt[e] = sk[sr2 * kHeadDim + i] * E;
+            cE[e] = sg[sr2 * kHeadDim + i];
+            cInv[e] = __builtin_amdgcn_rcpf(cE[e]);
+            cq[e] = sq[sr2 * kHeadDim + i];
+            ck[e] = sk[sr2 * kHeadDim + i];
+            cKh[e] = ck[e] * cInv[e];
+            cQt[e] = cq[e] * cE[e];
+            cKt[e] = ck[e] * cE[e];
         }
         dQt += mma_f32_k16(frag_k16(sdPo + l16 * FP, 0, g), cKh, zero4());
         dKt = mma_f32_k16(frag_k16(sdW + l16 * FP, 0, g), cKh, zero4()) - dKt;
@@ -1095,27 +1164,23 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
         dKh += mma_f32_k16(frag_k16(sdWt + l16 * FP, 0, g), cKt, zero4());
         const float gam = sGam[i];
         float dG[4], kvk = 0.f;
-        bf16* dq = static_cast<bf16*>(a.dq);
-        bf16* dk = static_cast<bf16*>(a.dk);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = 4 * g + e;
-            const float E = sg[r * kHeadDim + i], inv = 1.f / E;
-            const float qv = sq[r * kHeadDim + i], kv = sk[r * kHeadDim + i];
-            const float Qt = qv * E, Kt = kv * E, Kh = kv * inv, Kv = kv * gam * inv;
+            const float E = cE[e], inv = cInv[e];
+            const float Qt = cQt[e], Kt = cKt[e], Kh = cKh[e], Kv = ck[e] * gam * inv;
             const float gq = dQt[e] * E;
             const float gk = dKt[e] * E + dKh[e] * inv + dKv[e] * gam * inv;
             dG[e] = dQt[e] * Qt + dKt[e] * Kt - dKh[e] * Kh - dKv[e] * Kv;
             kvk += dKv[e] * Kv;
-            if (r < len) {
-                const size_t off = (size_t)(t0 + r) * rowstride + headoff + i;
-                dq[off] = (bf16)gq;
-                dk[off] = (bf16)gk;
-            }
+            sQt[r * KP + i] = (bf16)gq;   // staged dq
+            sKt[r * KP + i] = (bf16)gk;   // staged dk
         }
         kvk += __shfl_xor(kvk, 16, 64);
         kvk += __shfl_xor(kvk, 32, 64);
-        if (g == 3) dG[3] += gam * sDG[i] + kvk;
+        ds += __shfl_xor(ds, 16, 64);
+        ds += __shfl_xor(ds, 32, 64);
+        if (g == 3) dG[3] += gam * ds + kvk;
         float suf[4];
         suf[3] = dG[3];
         suf[2] = suf[3] + dG[2];
@@ -1128,16 +1193,14 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
         if ((g ^ 1) > g) above += t1;
         if ((g ^ 2) > g) above += t2;
         if ((g ^ 3) > g) above += t3;
-        bf16* dgl = static_cast<bf16*>(a.dlog_alpha);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g + e;
-            if (r < len) dgl[(size_t)(t0 + r) * rowstride + headoff + i] = (bf16)(suf[e] + above);
-        }
+        for (int e = 0; e < 4; ++e) sKh[(4 * g + e) * KP + i] = (bf16)(suf[e] + above);
     }
     __syncthreads();   // the next item's staging rewrites LDS
+    prev = cur;
     cur = nxt;
     }
+    if (prev.id >= 0) write_out(prev);
 }
 
 template <typename TIn, int NW, int NCT>
