@@ -767,9 +767,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) float sg[C * kHeadDim];  // log alpha, then E
     __shared__ __attribute__((aligned(16))) float sW[C * FP];
     __shared__ __attribute__((aligned(16))) float sM[C * FP];
-    __shared__ __attribute__((aligned(16))) float sdT[C * FP];
-    __shared__ __attribute__((aligned(16))) float sY[C * FP];
-    __shared__ __attribute__((aligned(16))) float sAW[C * FP];
+    __shared__ __attribute__((aligned(16))) float sMt[C * FP];
     __shared__ __attribute__((aligned(16))) float sdPo[C * FP];
     __shared__ __attribute__((aligned(16))) float sdPt[C * FP];
     __shared__ __attribute__((aligned(16))) float sdW[C * FP];
@@ -778,7 +776,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) bf16 sTt[C * CP];
     __shared__ __attribute__((aligned(16))) bf16 sPt[C * CP];
     __shared__ float sGam[kHeadDim];
-    __shared__ float sBeta[C];
+    __shared__ __attribute__((aligned(16))) float sBeta[C];
 
     const bf16* q = static_cast<const bf16*>(a.q);
     const bf16* k = static_cast<const bf16*>(a.k);
@@ -805,8 +803,16 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
     auto locate = [&](int64_t id) {
         Item it{-1, 0, 0, 0, nullptr, nullptr, nullptr};
         for (; id < n_items; id += gridDim.x) {
-            const int64_t slot = id / a.H;
-            const int h = (int)(id % a.H);
+            int64_t slot;
+            int h;
+            if (n_items <= 0x7fffffff) {
+                const uint32_t u = (uint32_t)id, hh = (uint32_t)a.H;
+                slot = (int64_t)(u / hh);
+                h = (int)(u - (uint32_t)slot * hh);
+            } else {
+                slot = id / a.H;
+                h = (int)(id % a.H);
+            }
             int64_t n = 0;
             if (a.cu_seqlens) {
                 int64_t lo = 0, hi = a.N - 1;
@@ -843,12 +849,18 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
     bf16x8 rq, rk, rg, rv, rdo;
     bf16 rb;   // raw: a conversion here would wait for every load in flight
     auto state_off = [&](int m) { return (size_t)((wave * 4 + m) * 64 + lane) * 8; };
+    // the state rows are requested separately (load_s), a few phases later,
+    // so that the two batches of requests overlap different phases
+    auto load_s = [&](const Item& it) {
+        if (it.S16) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                sr8[m] = *reinterpret_cast<const bf16x8*>(it.S16 + state_off(m));
+        }
+    };
     auto load = [&](const Item& it) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            dr8[m] = *reinterpret_cast<const bf16x8*>(it.Dd + state_off(m));
-            if (it.S16) sr8[m] = *reinterpret_cast<const bf16x8*>(it.S16 + state_off(m));
-        }
+        for (int m = 0; m < 4; ++m) dr8[m] = *reinterpret_cast<const bf16x8*>(it.Dd + state_off(m));
         if (tid < 256 && tr < it.len) {
             const size_t off = (size_t)(it.t0 + tr) * rowstride + (size_t)it.h * kHeadDim + tc8;
             rq = *reinterpret_cast<const bf16x8*>(q + off);
@@ -938,6 +950,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
     Item cur = locate(blockIdx.x), prev{-1, 0, 0, 0, nullptr, nullptr, nullptr};
     if (cur.id >= 0) {
         load(cur);
+        load_s(cur);
         pack(cur);
     }
     while (cur.id >= 0) {
@@ -997,7 +1010,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
         for (int e = 0; e < 4; ++e) sg[(4 * qr + e) * kHeadDim + i] = Eq[e];
     }
 
-    if (nxt.id >= 0) load(nxt);   // in flight during phases 2 to 5
+    if (nxt.id >= 0) load(nxt);   // in flight during phases 2 to 5 (state rows: 3 to 5)
 
     // ---- phase 2: Gram tiles (waves 0, 1) ----
     if (wave < 2) {
@@ -1023,10 +1036,13 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
         const float x = unit_lower_inverse(sW + l16 * FP, sBeta[l16], col, l16);
         const float bc = sBeta[col];
         sM[l16 * FP + col] = x;
+        sMt[col * FP + l16] = x;
         sT[l16 * CP + col] = (bf16)(x * bc);
         sTt[col * CP + l16] = (bf16)(x * bc);
     }
     __syncthreads();
+
+    if (nxt.id >= 0) load_s(nxt);
 
     // ---- phase 3: column tile J = 16 wave .. +15 (state tiles from LDS) ----
     {
@@ -1068,8 +1084,9 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
 
     if (nxt.id >= 0) pack(nxt);
 
-    // ---- phase 4: dT = dU X^T (wave 0), dP = lower_incl(dO U^T) (wave 1);
-    // waves 4 to 7 write dv = dX from its LDS tile with 16-byte stores ----
+    // ---- phase 4: dT = dU X^T and the small chain to dW and d beta (wave 0),
+    // dP = lower_incl(dO U^T) (wave 1); waves 4 to 7 write dv = dX from its
+    // LDS tile with 16-byte stores ----
     if (wave >= 4) {
         const int u = tid - 256, row = u >> 4, col = (u & 15) * 8;
         if (row < len)
@@ -1077,57 +1094,51 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
                                        (size_t)h * kHeadDim + col) =
                 *reinterpret_cast<const bf16x8*>(sdX + row * KP + col);
     }
-    if (wave < 2) {
-        const bool isP = wave == 1;
-        const bf16* arow = (isP ? sdO : sdU) + l16 * KP;
-        const bf16* brow = (isP ? sU : sX) + l16 * KP;
+    if (wave == 0) {
+        // dT = dU X^T, then on fp32 MFMAs with dT's accumulator as the
+        // (transposed) left operand: Y^T = diag(beta) dT^T M, and
+        // -dA^T = M Y^T, so that lane (l16, g) holds dA[l16][4 g + e]
+        floatx4 dT = zero4();
+#pragma unroll
+        for (int kb = 0; kb < kHeadDim; kb += 32)
+            dT = mma_bf16_k32(frag_k32(sdU + l16 * KP, kb, g), frag_k32(sX + l16 * KP, kb, g), dT);
+        const floatx4 mt = frag_k16(sMt + l16 * FP, 0, g);   // M[4 g + e][l16]
+        floatx4 YT = mma_f32_k16(dT, mt, zero4());
+        const floatx4 bq = *reinterpret_cast<const floatx4*>(sBeta + 4 * g);
+        YT = YT * bq;
+        const floatx4 nA = mma_f32_k16(frag_k16(sM + l16 * FP, 0, g), YT, zero4());
+        const floatx4 wr = frag_k16(sW + l16 * FP, 0, g);    // W[l16][4 g + e]
+        const float br = sBeta[l16];
+        float db = 0.f;
+        floatx4 dW;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int sc = 4 * g + e;
+            const float dA = sc < l16 ? -nA[e] : 0.f;
+            dW[e] = br * dA;
+            sdWt[sc * FP + l16] = dW[e];
+            // d beta_c = sum_r M[r][c] dT[r][c] + sum_s dA[c][s] W[c][s]:
+            // column l16 of the first, row l16 of the second
+            db += dT[e] * mt[e] + dA * wr[e];
+        }
+        *reinterpret_cast<floatx4*>(sdW + l16 * FP + 4 * g) = dW;
+        db += __shfl_xor(db, 16, 64);
+        db += __shfl_xor(db, 32, 64);
+        if (g == 0 && l16 < len) static_cast<bf16*>(a.dbeta)[(size_t)(t0 + l16) * a.H + h] = (bf16)db;
+    } else if (wave == 1) {
         floatx4 acc = zero4();
 #pragma unroll
         for (int kb = 0; kb < kHeadDim; kb += 32)
-            acc = mma_bf16_k32(frag_k32(arow, kb, g), frag_k32(brow, kb, g), acc);
+            acc = mma_bf16_k32(frag_k32(sdO + l16 * KP, kb, g), frag_k32(sU + l16 * KP, kb, g), acc);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = 4 * g + e, rp = l16;
-            if (!isP) {
-                sdT[r * FP + rp] = acc[e];
-            } else {
-                const float dp = (rp <= r) ? acc[e] : 0.f;
-                sdPo[r * FP + rp] = dp;
-                sdPt[rp * FP + r] = dp;
-            }
+            const float dp = (rp <= r) ? acc[e] : 0.f;
+            sdPo[r * FP + rp] = dp;
+            sdPt[rp * FP + r] = dp;
         }
     }
     __syncthreads();
-    if (tid < C * C) {
-        const int r = tid / C, qq = tid % C;
-        float y = 0.f;
-#pragma unroll
-        for (int p = 0; p < C; ++p) y += sM[p * FP + r] * sdT[p * FP + qq];
-        sY[r * FP + qq] = y * sBeta[qq];
-    }
-    __syncthreads();
-    if (tid < C * C) {
-        const int r = tid / C, s = tid % C;
-        float da = 0.f;
-        if (s < r) {
-#pragma unroll
-            for (int qq = 0; qq < C; ++qq) da -= sY[r * FP + qq] * sM[s * FP + qq];
-        }
-        const float dw = sBeta[r] * da;
-        sdW[r * FP + s] = dw;
-        sdWt[s * FP + r] = dw;
-        sAW[r * FP + s] = da * sW[r * FP + s];
-    }
-    __syncthreads();
-    if (tid < C) {
-        const int cc = tid;
-        float db = 0.f;
-#pragma unroll
-        for (int r = 0; r < C; ++r) db += sM[r * FP + cc] * sdT[r * FP + cc];
-#pragma unroll
-        for (int s2 = 0; s2 < C; ++s2) db += sAW[cc * FP + s2];
-        if (cc < len) static_cast<bf16*>(a.dbeta)[(size_t)(t0 + cc) * a.H + h] = (bf16)db;
-    }
 
     // ---- phase 5: key-channel tile I = 16 wave .. +15 ----
     {
