@@ -1046,26 +1046,28 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
 
     // ---- phase 3: column tile J = 16 wave .. +15 (state tiles from LDS) ----
     {
-        const int j = 16 * wave + l16;
+        const int j = 16 * wave + l16, j0 = 16 * wave;
         floatx4 KS = zero4(), KvD = zero4();
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            bf16x8 sb, db;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sb[e] = sS[(32 * b + 4 * g + e) * KP + j];
-                sb[4 + e] = sS[(32 * b + 16 + 4 * g + e) * KP + j];
-                db[e] = sD[(32 * b + 4 * g + e) * KP + j];
-                db[4 + e] = sD[(32 * b + 16 + 4 * g + e) * KP + j];
-            }
+            // rows 32 b + 4 g + e and 32 b + 16 + 4 g + e of column j (transposed reads)
+            const int r0 = (32 * b + 4 * g) * KP + j0, r1 = (32 * b + 16 + 4 * g) * KP + j0;
+            const bf16x4 s0 = lds_col4(sS + r0, KP, l16), s1 = lds_col4(sS + r1, KP, l16);
+            const bf16x4 d0 = lds_col4(sD + r0, KP, l16), d1 = lds_col4(sD + r1, KP, l16);
+            const bf16x8 sb{s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+            const bf16x8 db{d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
             KS = mma_bf16_k32(frag_k32(sKt + l16 * KP, 32 * b, g), sb, KS);
             KvD = mma_bf16_k32(frag_k32(sKv + l16 * KP, 32 * b, g), db, KvD);
         }
         floatx4 Vt, dOt;
+        {
+            const bf16x4 v4 = lds_col4(sV + 4 * g * KP + j0, KP, l16);
+            const bf16x4 o4 = lds_col4(sdO + 4 * g * KP + j0, KP, l16);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            Vt[e] = (float)sV[(4 * g + e) * KP + j];
-            dOt[e] = (float)sdO[(4 * g + e) * KP + j];
+            for (int e = 0; e < 4; ++e) {
+                Vt[e] = (float)v4[e];
+                dOt[e] = (float)o4[e];
+            }
         }
         const floatx4 X = Vt - KS;
         const floatx4 U = mm_k16(sT + l16 * CP, X, zero4(), g);

@@ -101,6 +101,22 @@ __device__ __forceinline__ bf16x4 acc_frag_k16(floatx4 t) {
     return bf16x4{(bf16)t[0], (bf16)t[1], (bf16)t[2], (bf16)t[3]};
 }
 
+// ---- transposed LDS reads (ds_read_b64_tr_b16) -------------------------------
+// In each group of 16 lanes, lane j names 4 consecutive 16-bit elements and
+// lane i receives element i % 4 of the pieces named by lanes i / 4, i / 4 + 4,
+// i / 4 + 8 and i / 4 + 12 (layout measured on gfx950).  col4 points lane j
+// at row j / 4, columns 4 (j % 4) .. +3 of a row-major tile at `base` (row
+// stride ld elements), so lane l16 receives rows 0..3 of column l16: four
+// consecutive k of one column, the B-operand layout, in one instruction.
+// Every lane of the wave must execute it; addresses are 8-byte aligned.
+__device__ __forceinline__ bf16x4 lds_col4(const bf16* base, int ld, int l16) {
+    typedef short shortx4_t __attribute__((ext_vector_type(4)));
+    const bf16* p = base + (l16 >> 2) * ld + 4 * (l16 & 3);
+    const shortx4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) shortx4_t*)(p));
+    return __builtin_bit_cast(bf16x4, r);
+}
+
 // ---- DPP lane shifts within a row of 16 lanes --------------------------------
 // row_shr:n (lane r reads lane r - n of its row) and row_shl:n (lane r reads
 // lane r + n); lanes whose source falls outside the row keep `fill`.
