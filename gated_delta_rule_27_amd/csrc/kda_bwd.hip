@@ -750,8 +750,10 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
     constexpr int KP = L::KP, CP = L::CP, FP = L::FP;
     constexpr size_t kState = (size_t)kHeadDim * kHeadDim;
 
-    __shared__ __attribute__((aligned(16))) bf16 sS[kHeadDim * KP];   // state, rows i
-    __shared__ __attribute__((aligned(16))) bf16 sD[kHeadDim * KP];   // state gradient
+    // the chunk's state and state gradient, transposed like their tables:
+    // row j (value column), 128 key channels i
+    __shared__ __attribute__((aligned(16))) bf16 sSt[kHeadDim * KP];
+    __shared__ __attribute__((aligned(16))) bf16 sDt[kHeadDim * KP];
     __shared__ __attribute__((aligned(16))) bf16 sQt[C * KP];
     __shared__ __attribute__((aligned(16))) bf16 sKt[C * KP];
     __shared__ __attribute__((aligned(16))) bf16 sKh[C * KP];
@@ -840,10 +842,10 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
     };
 
     // staging registers: the next item's global reads are in flight while
-    // the current item is computed.  State: instruction m of wave w reads
-    // the contiguous kilobyte (4 w + m) of the table entry, lane = 8
-    // columns of row (4 w + m) * 4 + lane / 16; token rows: thread t < 256
-    // takes row t / 16, 8 channels.
+    // the current item is computed.  State tables (transposed, rows j):
+    // instruction m of wave w reads the contiguous kilobyte (4 w + m) of the
+    // entry, lane = key channels 8 (lane % 16) .. +7 of row j = (4 w + m) * 4
+    // + lane / 16; token rows: thread t < 256 takes row t / 16, 8 channels.
     const int tr = (tid & 255) >> 4, tc8 = (tid & 15) * 8;
     bf16x8 sr8[4], dr8[4];  // this thread's four 8-column pieces of the state and its gradient
     bf16x8 rq, rk, rg, rv, rdo;
@@ -871,8 +873,9 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
         }
         if (tid < it.len) rb = bt[(size_t)(it.t0 + tid) * a.H + it.h];
     };
-    // a sequence's first chunk starts from h0 (fp32) or zero; read when the
-    // item is packed, as eight 16-byte loads with one wait
+    // a sequence's first chunk starts from h0 (fp32, rows i) or zero; read
+    // when the item is packed: 32 loads (8 rows i of this thread's columns
+    // j) with one wait
     auto pack = [&](const Item& it) {
         if (it.S16) return;
         if (!it.S32) {
@@ -882,26 +885,25 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
                 for (int e = 0; e < 8; ++e) sr8[m][e] = z16();
             return;
         }
-        float4 f[8];
+        float f[4][8];
+        const int i0 = (lane & 15) * 8;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const float4* src = reinterpret_cast<const float4*>(it.S32 + state_off(m));
-            f[2 * m] = src[0];
-            f[2 * m + 1] = src[1];
+            const int jr = (wave * 4 + m) * 4 + (lane >> 4);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[m][e] = it.S32[(size_t)(i0 + e) * kHeadDim + jr];
         }
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const float4 lo = f[2 * m], hi = f[2 * m + 1];
-            sr8[m] = bf16x8{(bf16)lo.x, (bf16)lo.y, (bf16)lo.z, (bf16)lo.w,
-                            (bf16)hi.x, (bf16)hi.y, (bf16)hi.z, (bf16)hi.w};
-        }
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sr8[m][e] = (bf16)f[m][e];
     };
     auto store = [&](const Item& it) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int row = (wave * 4 + m) * 4 + (lane >> 4), col = (lane & 15) * 8;
-            *reinterpret_cast<bf16x8*>(sS + row * KP + col) = sr8[m];
-            *reinterpret_cast<bf16x8*>(sD + row * KP + col) = dr8[m];
+            *reinterpret_cast<bf16x8*>(sSt + row * KP + col) = sr8[m];
+            *reinterpret_cast<bf16x8*>(sDt + row * KP + col) = dr8[m];
         }
         if (tid < 256) {
             const bool tok = tr < it.len;
@@ -1050,14 +1052,11 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
         floatx4 KS = zero4(), KvD = zero4();
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            // rows 32 b + 4 g + e and 32 b + 16 + 4 g + e of column j (transposed reads)
-            const int r0 = (32 * b + 4 * g) * KP + j0, r1 = (32 * b + 16 + 4 * g) * KP + j0;
-            const bf16x4 s0 = lds_col4(sS + r0, KP, l16), s1 = lds_col4(sS + r1, KP, l16);
-            const bf16x4 d0 = lds_col4(sD + r0, KP, l16), d1 = lds_col4(sD + r1, KP, l16);
-            const bf16x8 sb{s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-            const bf16x8 db{d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
-            KS = mma_bf16_k32(frag_k32(sKt + l16 * KP, 32 * b, g), sb, KS);
-            KvD = mma_bf16_k32(frag_k32(sKv + l16 * KP, 32 * b, g), db, KvD);
+            // S[i][j] over the key channels i of the block: row j of the transposed tile
+            KS = mma_bf16_k32(frag_k32(sKt + l16 * KP, 32 * b, g), frag_k32(sSt + j * KP, 32 * b, g),
+                              KS);
+            KvD = mma_bf16_k32(frag_k32(sKv + l16 * KP, 32 * b, g),
+                               frag_k32(sDt + j * KP, 32 * b, g), KvD);
         }
         floatx4 Vt, dOt;
         {
@@ -1149,8 +1148,13 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
         float ds = 0.f;   // this lane's part of sum_j D[i][j] S[i][j]
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            const bf16x8 sr = frag_k32(sS + i * KP, 32 * b, g);
-            const bf16x8 dr = frag_k32(sD + i * KP, 32 * b, g);
+            // S[i][j] and D[i][j] over the value columns j of the block:
+            // column i of the transposed tiles (transposed reads)
+            const int r0 = (32 * b + 4 * g) * KP + 16 * wave, r1 = (32 * b + 16 + 4 * g) * KP + 16 * wave;
+            const bf16x4 s0 = lds_col4(sSt + r0, KP, l16), s1 = lds_col4(sSt + r1, KP, l16);
+            const bf16x4 d0 = lds_col4(sDt + r0, KP, l16), d1 = lds_col4(sDt + r1, KP, l16);
+            const bf16x8 sr{s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+            const bf16x8 dr{d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
 #pragma unroll
             for (int e = 0; e < 8; e += 2)
                 ds = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{sr[e], sr[e + 1]},

@@ -54,7 +54,8 @@ struct RwsCfg {
     static constexpr size_t A0 = BETA0 + 3 * 64;             // A, 2 slots
     static constexpr size_t PT0 = A0 + 2 * szA;              // P^T, 3 slots
     static constexpr size_t TT0 = PT0 + 3 * szTile;          // T^T, 2 slots
-    static constexpr size_t bytes = TT0 + 2 * szTile;
+    static constexpr size_t TILE0 = TT0 + 2 * szTile;        // per state wave: D table staging
+    static constexpr size_t bytes = TILE0 + NSW * kC * kTileTP * 2;
     static_assert(bytes <= 160 * 1024, "LDS budget");
 };
 
@@ -176,7 +177,6 @@ __global__ __launch_bounds__((RwsCfg<NSW>::NT)) void bwd_dh_ws_kernel(BwdArgs a,
         // dO of a step: rows 4g .. 4g+3 of this lane's column, four steps ahead
         const uint32_t do_lane = (uint32_t)(((size_t)(4 * g) * rowstride + headoff + colw0) * 2);
         const uint32_t do_row = (uint32_t)(rowstride * 2);
-        const uint32_t d_lane = (uint32_t)((4 * g * kHeadDim + colw0) * 2);
         bf16 dor[4][4];
         auto load_do = [&](auto slot_c, int y) {
             constexpr int sv = decltype(slot_c)::value;
@@ -198,12 +198,11 @@ __global__ __launch_bounds__((RwsCfg<NSW>::NT)) void bwd_dh_ws_kernel(BwdArgs a,
                     const rsrc_t rs = make_rsrc(
                         static_cast<bf16*>(a.dstates) + ((size_t)(slot0 + cc) * a.H + h) * kState,
                         (int64_t)kState * 2);
-#pragma unroll
-                    for (int it = 0; it < 8; ++it)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            buf_store_bf16((bf16)D[it][e], rs, d_lane,
-                                           ((16 * it + e) * kHeadDim) * 2);
+                    // transposed like the state table: this wave's 16
+                    // columns are 16 contiguous rows of 128
+                    store_tile_t(D, reinterpret_cast<bf16*>(smem + K::TILE0) +
+                                        (size_t)wave * kC * kTileTP,
+                                 rs, (uint32_t)((col0 + 16 * wave) * kHeadDim * 2), lane);
                 }
                 // dU = Kv D + P^T dO
                 const bf16* Kv = kv_s(y) + l16 * KP;

@@ -79,7 +79,8 @@ struct WsCfg {
     static constexpr size_t A0 = BETA0 + 3 * 64;            //  A, 2 slots
     static constexpr size_t P0 = A0 + 2 * szA;              //  P, 3 slots
     static constexpr size_t T0 = P0 + 3 * szTile;           //  T, 2 slots
-    static constexpr size_t bytes = T0 + 2 * szTile;
+    static constexpr size_t TILE0 = T0 + 2 * szTile;        //  per state wave: bf16 snapshot staging
+    static constexpr size_t bytes = TILE0 + NSW * kWsC * kTileTP * 2;
 
     static_assert(bytes <= 160 * 1024, "LDS budget");
     static_assert(kWsC == kSnapUnit, "snapshots fall on chunk ends");
@@ -300,16 +301,17 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
                     if (idx < snap.n_snap) {
                         const size_t eo = ((size_t)idx * (size_t)H + h) * (kHeadDim * kHeadDim);
                         if (flags & kChunkSnapBf16) {
+                            // transposed entry: this wave's 16 columns are 16
+                            // contiguous rows of 128
                             const rsrc_t rs = make_rsrc(reinterpret_cast<bf16*>(snap.snap) + eo,
                                                         kHeadDim * kHeadDim * 2);
+                            bf16* tile = reinterpret_cast<bf16*>(smem + K::TILE0) +
+                                         (size_t)wave * kWsC * kTileTP;
 #pragma unroll
                             for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-                                for (int it = 0; it < 8; ++it)
-#pragma unroll
-                                    for (int e = 0; e < 4; ++e)
-                                        buf_store_bf16((bf16)S[ct][it][e], rs, snap_lane / 2,
-                                                       ((16 * it + e) * kHeadDim + 16 * ct) * 2);
+                                store_tile_t(S[ct], tile, rs,
+                                             (uint32_t)((col0 + 16 * (NCT * wave + ct)) * kHeadDim * 2),
+                                             lane);
                         } else {
                             const rsrc_t rs = make_rsrc(snap.snap + eo, kHeadDim * kHeadDim * 4);
 #pragma unroll

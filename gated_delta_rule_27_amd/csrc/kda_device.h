@@ -227,10 +227,55 @@ __device__ __forceinline__ void buf_store_bf16(bf16 x, rsrc_t r, uint32_t off) {
 __device__ __forceinline__ void buf_store_bf16(bf16 x, rsrc_t r, uint32_t voff, int soff) {
     __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(short, x), r, (int)voff, soff, 0);
 }
+// four bf16 (8 bytes) at voff (per lane) + soff (uniform)
+__device__ __forceinline__ void buf_store_bf16x4(bf16x4 x, rsrc_t r, uint32_t voff, int soff) {
+    typedef unsigned int uintx2_t __attribute__((ext_vector_type(2)));
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(uintx2_t, x), r, (int)voff, soff, 0);
+}
+// 16 bytes at voff (per lane) + soff (uniform)
+__device__ __forceinline__ void buf_store_b128(bf16x8 x, rsrc_t r, uint32_t voff, int soff) {
+    typedef unsigned int uintx4_t __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(uintx4_t, x), r, (int)voff, soff, 0);
+}
 // fp32 store at voff (per lane) + soff (uniform, e.g. a compile-time constant:
 // it travels in the instruction's scalar offset, not in a vector register)
 __device__ __forceinline__ void buf_store_f32(float x, rsrc_t r, uint32_t voff, int soff) {
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, x), r, (int)voff, soff, 0);
+}
+
+// ---- a wave's 128 x 16 accumulator tile out to memory, transposed ----------
+// Lane (l16, g) of the wave holds rows 16 it + 4 g + e of column l16 (it =
+// 0..7, e = 0..3): a 128 x 16 column block of a state in MFMA accumulators.
+// Its transpose (16 rows of 128, 4 KB, contiguous in a transposed table
+// entry) goes out through a wave-private LDS tile of 16 x kTileTP bf16:
+// eight 8-byte LDS writes, four 16-byte LDS reads, four 1-KB stores, so
+// every store instruction covers whole cache lines.  r / voff0: the block's
+// first byte.  Only this wave touches `tile`; its LDS operations execute in
+// order, and the fence keeps the compiler from moving them across.
+constexpr int kTileTP = 128 + 8;   // a 128-channel row plus 16 bytes of padding
+__device__ __forceinline__ void store_tile_t(const floatx4 (&T)[8], bf16* tile, rsrc_t r,
+                                             uint32_t voff0, int lane) {
+    const int l16 = lane & 15, g = lane >> 4;
+    // (one conversion live at a time: the scheduler may not hoist them all)
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        *reinterpret_cast<bf16x4*>(tile + l16 * kTileTP + 16 * it + 4 * g) = acc_frag_k16(T[it]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    // piece 64 s + lane: row 4 s + lane / 16, columns 8 (lane % 16) .. +7;
+    // one base address each (re-derived here, not kept live across the
+    // caller's loop), the rest immediate offsets
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const bf16* rb = tile + (ln >> 4) * kTileTP + (ln & 15) * 8;
+    const uint32_t vb = voff0 + (uint32_t)ln * 16;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(rb + 4 * s * kTileTP);
+        buf_store_b128(v, r, vb, 1024 * s);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 }
 
 // ---- vector global loads of 4 or 8 elements ----------------------------------

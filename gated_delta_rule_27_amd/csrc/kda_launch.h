@@ -16,7 +16,7 @@ constexpr int kSnapUnit = 16;  // prefix-snapshot intervals are multiples of thi
 // snap[(base_n + j - 1), h] with base_n = snap_cu[n] (0 without snap_cu);
 // indices at or past n_snap are not written.  snap == nullptr disables them.
 struct SnapArgs {
-    float* snap;              // [n_snap, H, 128, 128] fp32 (bf16 under kChunkSnapBf16)
+    float* snap;              // [n_snap, H, 128, 128] fp32 (bf16 [.., 128 j, 128 i] under kChunkSnapBf16)
     const int32_t* snap_cu;   // device [N + 1], may be null (one sequence)
     int64_t n_snap;
     int32_t every_chunks;     // >= 1
@@ -31,7 +31,11 @@ enum ChunkFlags : int32_t {
     kChunkNoOutput = 1,     // o is not written (may be null)
     kChunkVZero = 2,        // V is taken as zero (v may be null)
     kChunkH0Identity = 4,   // the initial state of every sequence is I
-    kChunkSnapBf16 = 16,    // snapshots stored as bf16 (the bf16 pipelined kernel only)
+    kChunkSnapBf16 = 16,    // snapshots stored as bf16 and transposed: entry element
+                            // (i, j) at j * 128 + i, so that the four consecutive rows
+                            // of one column an MFMA lane holds go out as one 8-byte
+                            // store (the bf16 pipelined kernel only; read by the
+                            // backward's per-chunk gradient kernel)
     kChunkSnapSlots = 8,    // snapshot j of sequence n goes to entry chunk_slot(n) + j
                             // (with a snapshot after every chunk: the per-chunk
                             // state store of the backward pass)
