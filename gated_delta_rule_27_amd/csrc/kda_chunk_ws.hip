@@ -79,7 +79,11 @@ struct WsCfg {
     static constexpr size_t A0 = BETA0 + 3 * 64;            //  A, 2 slots
     static constexpr size_t P0 = A0 + 2 * szA;              //  P, 3 slots
     static constexpr size_t T0 = P0 + 3 * szTile;           //  T, 2 slots
-    static constexpr size_t TILE0 = T0 + 2 * szTile;        //  per state wave: bf16 snapshot staging
+    static constexpr int VP = DV + 8;                       // bf16 stride of the V / O tiles
+    static constexpr size_t szVO = kWsC * VP * 2;           // [16][DV] bf16
+    static constexpr size_t VT0 = T0 + 2 * szTile;          //  V of the workgroup's columns, 4 slots
+    static constexpr size_t OT0 = VT0 + 4 * szVO;           //  O of the workgroup's columns, 2 slots
+    static constexpr size_t TILE0 = OT0 + 2 * szVO;         //  per state wave: bf16 snapshot staging
     static constexpr size_t bytes = TILE0 + NSW * kWsC * kTileTP * 2;
 
     static_assert(bytes <= 160 * 1024, "LDS budget");
@@ -116,6 +120,8 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
     auto a_s = [&](int y) { return reinterpret_cast<float*>(smem + K::A0 + (y & 1) * K::szA); };
     auto p_s = [&](int y) { return reinterpret_cast<bf16*>(smem + K::P0 + (y % 3) * K::szTile); };
     auto t_s = [&](int y) { return reinterpret_cast<bf16*>(smem + K::T0 + (y & 1) * K::szTile); };
+    auto vt_s = [&](int y) { return reinterpret_cast<bf16*>(smem + K::VT0 + (y & 3) * K::szVO); };
+    auto ot_s = [&](int y) { return reinterpret_cast<bf16*>(smem + K::OT0 + (y & 1) * K::szVO); };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -212,36 +218,15 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
                 }
             }
         }
-        // V of a chunk: rows 4g..4g+3 of this lane's columns, four chunks in
-        // flight, through a buffer resource over the chunk's rows inside the
-        // sequence: rows past its end read 0 (they never reach an output,
-        // since their beta is zero) and output stores there are dropped, so
-        // every chunk issues the same loads and stores without branches.  The
-        // prefetch distance keeps the memory-counter wait for a chunk's V
-        // clear of the output stores of the iterations just before it.
+        // V arrives in, and O leaves through, LDS tiles of the workgroup's
+        // DV columns (the prep waves move them between LDS and memory), so
+        // the state waves issue no global memory operations per chunk.
         const int colw0 = col0 + 16 * NCT * wave + l16;  // this lane's first column
         const int64_t snap_base = (flags & kChunkSnapSlots) ? chunk_slot(bos, n)
                                   : snap.snap_cu ? (int64_t)snap.snap_cu[n] : 0;
-        const uint32_t vo_lane = (uint32_t)(((size_t)(4 * g) * rowstride + headoff + colw0) * 2);
-        const uint32_t vo_row = (uint32_t)(rowstride * 2);
         const uint32_t snap_lane = (uint32_t)((4 * g * kHeadDim + colw0) * 4);
-        // (an empty resource when the pass takes V as zero / writes no output)
-        auto rows_rsrc = [&](const bf16* base, int y, bool none) {
-            const int64_t rows = (!none && y >= 0 && y < nch) ? seqlen - (int64_t)kWsC * y : 0;
-            return make_rsrc(base + (size_t)(bos + (int64_t)kWsC * (y < 0 ? 0 : y)) * rowstride,
-                             rows * (int64_t)rowstride * 2);
-        };
-        bf16 vr[4][NCT][4];
-        auto load_v = [&](auto slot_c, int y) {
-            constexpr int sv = decltype(slot_c)::value;
-            const rsrc_t rv = rows_rsrc(v, y, flags & kChunkVZero);
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    vr[sv][ct][e] = buf_load_bf16(rv, vo_lane + e * vo_row + 32 * ct);
-        };
-        load_v(std::integral_constant<int, 0>{}, 0);
+        constexpr int VP = K::VP;
+        const bool write_o = !(flags & kChunkNoOutput);
 
         auto state_iter = [&](auto slot_c, int c) {
             constexpr int sv = decltype(slot_c)::value;  // == c & 3
@@ -252,8 +237,10 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
                 floatx4 X[NCT], Ov[NCT], U[NCT];
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) {
+                    // rows 4g..4g+3 of this lane's column (transposed read)
+                    const bf16x4 v4 = lds_col4(vt_s(c) + 4 * g * VP + 16 * (NCT * wave + ct), VP, l16);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) X[ct][e] = (float)vr[sv][ct][e];
+                    for (int e = 0; e < 4; ++e) X[ct][e] = (float)v4[e];
                     Ov[ct] = zero4();
                 }
                 // X = V - Ktil S, O = Qtil S
@@ -278,12 +265,13 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
                     ub[ct] = acc_frag_k16(U[ct]);
                     Ov[ct] = mma_bf16_k16_as_k32(ap, ub[ct], Ov[ct]);  // same opcode as Qtil S
                 }
-                const rsrc_t ro = rows_rsrc(o, c, flags & kChunkNoOutput);
+                if (write_o) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
+                    for (int e = 0; e < 4; ++e)
 #pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct)
-                        buf_store_bf16((bf16)Ov[ct][e], ro, vo_lane + e * vo_row + 32 * ct);
+                        for (int ct = 0; ct < NCT; ++ct)
+                            ot_s(c)[(4 * g + e) * VP + 16 * (NCT * wave + ct) + l16] = (bf16)Ov[ct][e];
+                }
                 // S <- Diag(Gamma) S + Kvec^T U
                 const bf16* KvT = kvt_s(c);
 #pragma unroll
@@ -332,9 +320,6 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
                 const int zc = c + 2;
                 if (zc >= 0 && zc < nch) gram_tile(wave == 1, zc);
             }
-            // refill this V slot with chunk c+4 on the one path every
-            // iteration takes, so its registers and memory count are fixed
-            load_v(slot_c, c + 4);
             __syncthreads();
         };
         for (int c = -3; c < nit - 3; c += 4) {
@@ -368,6 +353,28 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
     // sequence, so rows past its end read 0: they neither decay nor write.
     bf16x4 rq[PD], rk[PD], rg[PD];
     bf16 rb[PD];
+    // V in / O out for the state waves: prep waves 4 - DV / 32 .. 3 move
+    // one 16-byte piece of a row of the 16 x DV tile per lane: V of chunk
+    // c+3 into its LDS tile (loaded PD iterations earlier) and O of chunk
+    // c-1 out of its tile, in iteration c.  (Those waves also solve; the
+    // prep waves that do not are the last to be issued and the busiest.)
+    constexpr int VP = K::VP;
+    static_assert(DV / 32 <= 4, "V / O waves are prep waves 0..3");
+    const bool io_wave = pw >= 4 - DV / 32 && pw < 4;
+    const int io_u = (pw - (4 - DV / 32)) * 64 + lane;
+    const int io_row = io_u / (DV / 8), io_col = (io_u % (DV / 8)) * 8;
+    const uint32_t io_off = (uint32_t)(((size_t)io_row * rowstride + headoff + col0 + io_col) * 2);
+    const bool write_o = !(flags & kChunkNoOutput);
+    auto rows_rsrc = [&](const bf16* base, int y, bool none) {
+        const int64_t rows = (!none && y >= 0 && y < nch) ? seqlen - (int64_t)kWsC * y : 0;
+        return make_rsrc(base + (size_t)(bos + (int64_t)kWsC * (y < 0 ? 0 : y)) * rowstride,
+                         rows * (int64_t)rowstride * 2);
+    };
+    bf16x8 rv[PD];
+    auto store_o = [&](int y) {
+        buf_store_b128(*reinterpret_cast<const bf16x8*>(ot_s(y) + io_row * VP + io_col),
+                       rows_rsrc(o, y, !write_o), io_off, 0);
+    };
     const uint32_t qo_lane = (uint32_t)(((size_t)r * rowstride + headoff + ch0) * 2);
     const uint32_t bo_lane = (uint32_t)(((size_t)r * H + h) * 2);
     const bool q_none = flags & kChunkNoOutput;
@@ -382,6 +389,9 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
         rk[s] = buf_load_bf16x4(make_rsrc(k + t0 * rowstride, tok_bytes), qo_lane);
         rg[s] = buf_load_bf16x4(make_rsrc(log_alpha + t0 * rowstride, tok_bytes), qo_lane);
         rb[s] = buf_load_bf16(make_rsrc(beta + t0 * H, rows * (int64_t)H * 2), bo_lane);
+        if (io_wave)
+            rv[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   rows_rsrc(v, yc, flags & kChunkVZero), (int)io_off, 0, 0));
     };
     load_chunk(std::integral_constant<int, 0>{}, 0);
     if constexpr (PD > 1) load_chunk(std::integral_constant<int, 1 % PD>{}, 1);
@@ -421,7 +431,9 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
             *reinterpret_cast<bf16x4*>(kh_s(yc) + r * KP + ch0) = kh;
             if (r == 0) *reinterpret_cast<floatx4*>(gam_s(yc) + ch0) = gam;
             if (pw == 0 && g == 0) beta_s(yc)[r] = bt;
+            if (io_wave) *reinterpret_cast<bf16x8*>(vt_s(yc) + io_row * VP + io_col) = rv[s];
         }
+        if (io_wave && write_o && c - 1 >= 0 && c - 1 < nch) store_o(c - 1);
         load_chunk(slot_c, yc + PD);
         // (3) UT transform of chunk c+1 on prep waves 0-3: lane = (row
         // l16, column 4 * pw + g) of X = (I + A)^{-1}; forward elimination
@@ -466,6 +478,8 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
         if constexpr (PD > 2) prep_iter(std::integral_constant<int, 2 % PD>{}, c + 2);
         if constexpr (PD > 3) prep_iter(std::integral_constant<int, 3 % PD>{}, c + 3);
     }
+    // O of the last iteration's chunk (its tile was written before the final barrier)
+    if (io_wave && write_o && nit - 4 < nch) store_o(nit - 4);
 }
 
 template <int NCT, int NSW, int PD>
