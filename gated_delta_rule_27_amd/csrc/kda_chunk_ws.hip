@@ -365,33 +365,42 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
     const int io_row = io_u / (DV / 8), io_col = (io_u % (DV / 8)) * 8;
     const uint32_t io_off = (uint32_t)(((size_t)io_row * rowstride + headoff + col0 + io_col) * 2);
     const bool write_o = !(flags & kChunkNoOutput);
-    auto rows_rsrc = [&](const bf16* base, int y, bool none) {
-        const int64_t rows = (!none && y >= 0 && y < nch) ? seqlen - (int64_t)kWsC * y : 0;
-        return make_rsrc(base + (size_t)(bos + (int64_t)kWsC * (y < 0 ? 0 : y)) * rowstride,
-                         rows * (int64_t)rowstride * 2);
+    // Per-chunk buffer resources, from scalar bases kept per sequence (the
+    // scalar unit is shared by the waves of a SIMD, and 64-bit address and
+    // size arithmetic per chunk and tensor was a large part of this
+    // stage): chunk y starts y * cstride elements after the sequence's
+    // first row and has chunk_rows(y) rows inside it (0 past the end).
+    const size_t cstride = (size_t)kWsC * rowstride;
+    const uint32_t last_rows = (uint32_t)(seqlen - (int64_t)kWsC * (nch - 1));
+    auto chunk_rows = [&](int y) -> uint32_t {
+        return y < nch - 1 ? (uint32_t)kWsC : y == nch - 1 ? last_rows : 0u;
     };
+    const uint32_t row_bytes = (uint32_t)(rowstride * 2);
+    const size_t seq0 = (size_t)bos * rowstride;
+    const bf16 *q_seq = q + seq0, *k_seq = k + seq0, *g_seq = log_alpha + seq0, *v_seq = v + seq0;
+    bf16* o_seq = o + seq0;
+    const bf16* b_seq = beta + (size_t)bos * H;
+    const bool q_none = flags & kChunkNoOutput, v_none = flags & kChunkVZero;
     bf16x8 rv[PD];
     auto store_o = [&](int y) {
         buf_store_b128(*reinterpret_cast<const bf16x8*>(ot_s(y) + io_row * VP + io_col),
-                       rows_rsrc(o, y, !write_o), io_off, 0);
+                       make_rsrc_u32(o_seq + (size_t)y * cstride, chunk_rows(y) * row_bytes), io_off, 0);
     };
     const uint32_t qo_lane = (uint32_t)(((size_t)r * rowstride + headoff + ch0) * 2);
     const uint32_t bo_lane = (uint32_t)(((size_t)r * H + h) * 2);
-    const bool q_none = flags & kChunkNoOutput;
-    auto q_bytes = [&](int64_t b) { return q_none ? (int64_t)0 : b; };
     auto load_chunk = [&](auto slot_c, int yc) {
         constexpr int s = decltype(slot_c)::value;
-        const int64_t rows = yc < nch ? seqlen - (int64_t)kWsC * yc : 0;
-        const size_t t0 = (size_t)(bos + (int64_t)kWsC * yc);
-        const int64_t tok_bytes = rows * (int64_t)rowstride * 2;
+        const size_t off = (size_t)yc * cstride;
+        const uint32_t rows = chunk_rows(yc), bytes = rows * row_bytes;
         // q feeds the outputs only: a pass without them reads none (zeros)
-        rq[s] = buf_load_bf16x4(make_rsrc(q + t0 * rowstride, q_bytes(tok_bytes)), qo_lane);
-        rk[s] = buf_load_bf16x4(make_rsrc(k + t0 * rowstride, tok_bytes), qo_lane);
-        rg[s] = buf_load_bf16x4(make_rsrc(log_alpha + t0 * rowstride, tok_bytes), qo_lane);
-        rb[s] = buf_load_bf16(make_rsrc(beta + t0 * H, rows * (int64_t)H * 2), bo_lane);
+        rq[s] = buf_load_bf16x4(make_rsrc_u32(q_seq + off, q_none ? 0u : bytes), qo_lane);
+        rk[s] = buf_load_bf16x4(make_rsrc_u32(k_seq + off, bytes), qo_lane);
+        rg[s] = buf_load_bf16x4(make_rsrc_u32(g_seq + off, bytes), qo_lane);
+        rb[s] = buf_load_bf16(make_rsrc_u32(b_seq + (size_t)yc * kWsC * H, rows * (uint32_t)H * 2), bo_lane);
         if (io_wave)
             rv[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                                                   rows_rsrc(v, yc, flags & kChunkVZero), (int)io_off, 0, 0));
+                                                   make_rsrc_u32(v_seq + off, v_none ? 0u : bytes),
+                                                   (int)io_off, 0, 0));
     };
     load_chunk(std::integral_constant<int, 0>{}, 0);
     if constexpr (PD > 1) load_chunk(std::integral_constant<int, 1 % PD>{}, 1);

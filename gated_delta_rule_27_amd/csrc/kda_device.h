@@ -214,6 +214,11 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
     const uint32_t n = bytes <= 0 ? 0u : (bytes >= 0xFFFFFFFFll ? 0xFFFFFFFFu : (uint32_t)bytes);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)n, kBufWord3);
 }
+// the same for a size already known to fit 32 bits (no clamping: cheaper
+// scalar code where a resource is made per chunk)
+__device__ __forceinline__ rsrc_t make_rsrc_u32(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufWord3);
+}
 __device__ __forceinline__ bf16 buf_load_bf16(rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(bf16, (short)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0));
 }
