@@ -65,15 +65,14 @@ struct WsCfg {
     static constexpr int AP = 20;                // fp32 stride of the A tile
 
     static constexpr size_t szTok = kWsC * KP * 2;        // [16][128] bf16
-    static constexpr size_t szKvT = kHeadDim * TP * 2;    // [128][16] bf16
     static constexpr size_t szTile = kWsC * TP * 2;       // [16][16] bf16
     static constexpr size_t szA = kWsC * AP * 4;          // [16][16] fp32
     // ring buffers; chunk y's operands are written by the prep stage three
     // iterations before the state stage reads them
     static constexpr size_t KN0 = 0;                        // -Ktil, 4 slots
     static constexpr size_t QS0 = KN0 + 4 * szTok;          //  Qtil, 4 slots
-    static constexpr size_t KVT0 = QS0 + 4 * szTok;         //  Kvec^T, 4 slots
-    static constexpr size_t GAM0 = KVT0 + 4 * szKvT;        //  Gamma, 4 slots
+    static constexpr size_t KV0 = QS0 + 4 * szTok;          //  Kvec rows, 4 slots
+    static constexpr size_t GAM0 = KV0 + 4 * szTok;         //  Gamma, 4 slots
     static constexpr size_t KH0 = GAM0 + 4 * 512;           //  Khat, 2 slots
     static constexpr size_t BETA0 = KH0 + 2 * szTok;        //  beta, 3 slots
     static constexpr size_t A0 = BETA0 + 3 * 64;            //  A, 2 slots
@@ -113,7 +112,7 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     auto kn_s = [&](int y) { return reinterpret_cast<bf16*>(smem + K::KN0 + (y & 3) * K::szTok); };
     auto qs_s = [&](int y) { return reinterpret_cast<bf16*>(smem + K::QS0 + (y & 3) * K::szTok); };
-    auto kvt_s = [&](int y) { return reinterpret_cast<bf16*>(smem + K::KVT0 + (y & 3) * K::szKvT); };
+    auto kv_s = [&](int y) { return reinterpret_cast<bf16*>(smem + K::KV0 + (y & 3) * K::szTok); };
     auto gam_s = [&](int y) { return reinterpret_cast<float*>(smem + K::GAM0 + (y & 3) * 512); };
     auto kh_s = [&](int y) { return reinterpret_cast<bf16*>(smem + K::KH0 + (y & 1) * K::szTok); };
     auto beta_s = [&](int y) { return reinterpret_cast<float*>(smem + K::BETA0 + (y % 3) * 64); };
@@ -273,11 +272,12 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
                             ot_s(c)[(4 * g + e) * VP + 16 * (NCT * wave + ct) + l16] = (bf16)Ov[ct][e];
                 }
                 // S <- Diag(Gamma) S + Kvec^T U
-                const bf16* KvT = kvt_s(c);
+                const bf16* Kv = kv_s(c);
 #pragma unroll
                 for (int it = 0; it < 8; ++it) {
                     const floatx4 gm = *reinterpret_cast<const floatx4*>(Gm + 16 * it + 4 * g);
-                    const bf16x4 a = frag_k16(KvT + (16 * it + l16) * TP, 0, g);
+                    // Kvec^T rows 16 it .. +15 over tokens 4g .. 4g+3: a transposed read
+                    const bf16x4 a = lds_col4(Kv + 4 * g * KP + 16 * it, KP, l16);
 #pragma unroll
                     for (int ct = 0; ct < NCT; ++ct)
                         S[ct][it] = mma_bf16_k16(a, ub[ct], S[ct][it] * gm);
@@ -420,9 +420,8 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
                 qf[e] = (float)rq[s][e];
                 lg[e] = (float)rg[s][e] * kLog2e;
             }
-            bf16x4 kn, qs, kh;
+            bf16x4 kn, qs, kh, kv;
             floatx4 gam;
-            bf16* KvT = kvt_s(yc);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float P = row_prefix_sum(lg[e]);        // G_r / ln 2
@@ -433,8 +432,9 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
                 kn[e] = (bf16)(-kf[e] * E);
                 qs[e] = (bf16)(qf[e] * E);
                 kh[e] = (bf16)(kf[e] * Einv);
-                KvT[(ch0 + e) * TP + r] = (bf16)(kf[e] * Hs);
+                kv[e] = (bf16)(kf[e] * Hs);
             }
+            *reinterpret_cast<bf16x4*>(kv_s(yc) + r * KP + ch0) = kv;
             *reinterpret_cast<bf16x4*>(kn_s(yc) + r * KP + ch0) = kn;
             *reinterpret_cast<bf16x4*>(qs_s(yc) + r * KP + ch0) = qs;
             *reinterpret_cast<bf16x4*>(kh_s(yc) + r * KP + ch0) = kh;
