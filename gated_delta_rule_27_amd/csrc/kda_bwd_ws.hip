@@ -37,20 +37,22 @@ struct RwsCfg {
     static constexpr int KP = kHeadDim + 8;       // bf16 stride of [token][channel]
     static constexpr int TP = kC + 8;             // bf16 stride of [.][token]
     static constexpr int AP = 20;                 // fp32 stride of the A tile
+    static constexpr int VP = DV + 8;              // bf16 stride of the dO tile
     static constexpr size_t szTok = kC * KP * 2;
-    static constexpr size_t szCol = kHeadDim * TP * 2;
     static constexpr size_t szTile = kC * TP * 2;
     static constexpr size_t szA = kC * AP * 4;
+    static constexpr size_t szDO = kC * VP * 2;
     // ring buffers indexed by step; written by prep three iterations before
-    // the state stage reads them (Gram operands: one iteration before)
+    // the state stage reads them (Gram operands: one iteration before).
+    // Token rows throughout: the state stage reads the operands it needs by
+    // columns (Qt^T, -Kt^T) with transposed LDS reads.
     static constexpr size_t KV0 = 0;                         // Kv rows, 4 slots
-    static constexpr size_t QT0 = KV0 + 4 * szTok;           // Qt^T, 4 slots
-    static constexpr size_t KT0 = QT0 + 4 * szCol;           // -Kt^T, 4 slots
-    static constexpr size_t GAM0 = KT0 + 4 * szCol;          // Gamma, 4 slots
-    static constexpr size_t KN0 = GAM0 + 4 * 512;            // -Kt rows (Gram), 2 slots
-    static constexpr size_t QS0 = KN0 + 2 * szTok;           // Qt rows (Gram), 2 slots
-    static constexpr size_t KH0 = QS0 + 2 * szTok;           // Khat rows (Gram), 2 slots
-    static constexpr size_t BETA0 = KH0 + 2 * szTok;         // beta, 3 slots
+    static constexpr size_t KN0 = KV0 + 4 * szTok;           // -Kt rows, 4 slots
+    static constexpr size_t QS0 = KN0 + 4 * szTok;           // Qt rows, 4 slots
+    static constexpr size_t GAM0 = QS0 + 4 * szTok;          // Gamma, 4 slots
+    static constexpr size_t KH0 = GAM0 + 4 * 512;            // Khat rows (Gram), 2 slots
+    static constexpr size_t DO0 = KH0 + 2 * szTok;           // dO of the workgroup's columns, 4 slots
+    static constexpr size_t BETA0 = DO0 + 4 * szDO;          // beta, 3 slots
     static constexpr size_t A0 = BETA0 + 3 * 64;             // A, 2 slots
     static constexpr size_t PT0 = A0 + 2 * szA;              // P^T, 3 slots
     static constexpr size_t TT0 = PT0 + 3 * szTile;          // T^T, 2 slots
@@ -77,11 +79,10 @@ __global__ __launch_bounds__((RwsCfg<NSW>::NT)) void bwd_dh_ws_kernel(BwdArgs a,
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     auto kv_s = [&](int y) { return reinterpret_cast<bf16*>(smem + K::KV0 + (y & 3) * K::szTok); };
-    auto qt_s = [&](int y) { return reinterpret_cast<bf16*>(smem + K::QT0 + (y & 3) * K::szCol); };
-    auto kt_s = [&](int y) { return reinterpret_cast<bf16*>(smem + K::KT0 + (y & 3) * K::szCol); };
     auto gam_s = [&](int y) { return reinterpret_cast<float*>(smem + K::GAM0 + (y & 3) * 512); };
-    auto kn_s = [&](int y) { return reinterpret_cast<bf16*>(smem + K::KN0 + (y & 1) * K::szTok); };
-    auto qs_s = [&](int y) { return reinterpret_cast<bf16*>(smem + K::QS0 + (y & 1) * K::szTok); };
+    auto kn_s = [&](int y) { return reinterpret_cast<bf16*>(smem + K::KN0 + (y & 3) * K::szTok); };
+    auto qs_s = [&](int y) { return reinterpret_cast<bf16*>(smem + K::QS0 + (y & 3) * K::szTok); };
+    auto do_s = [&](int y) { return reinterpret_cast<bf16*>(smem + K::DO0 + (y & 3) * K::szDO); };
     auto kh_s = [&](int y) { return reinterpret_cast<bf16*>(smem + K::KH0 + (y & 1) * K::szTok); };
     auto beta_s = [&](int y) { return reinterpret_cast<float*>(smem + K::BETA0 + (y % 3) * 64); };
     auto a_s = [&](int y) { return reinterpret_cast<float*>(smem + K::A0 + (y & 1) * K::szA); };
@@ -153,13 +154,22 @@ __global__ __launch_bounds__((RwsCfg<NSW>::NT)) void bwd_dh_ws_kernel(BwdArgs a,
         }
     };
 
-    // chunk cc's rows inside the sequence as a buffer resource (empty when
-    // cc is not a chunk): rows past the end read 0
-    auto rows_rsrc = [&](const void* base, size_t esz, size_t stride_elems, int cc) {
-        const int64_t rows = (cc >= 0 && cc < nch) ? seqlen - (int64_t)kC * cc : 0;
-        const size_t t0 = (size_t)(bos + (int64_t)kC * (cc < 0 ? 0 : cc));
-        return make_rsrc(static_cast<const unsigned char*>(base) + t0 * stride_elems * esz,
-                         rows * (int64_t)stride_elems * (int64_t)esz);
+    // chunk cc's rows inside the sequence as buffer resources (empty when
+    // cc is not a chunk: rows past the end read 0), from per-sequence
+    // scalar bases: one multiply per chunk, no 64-bit size arithmetic
+    const size_t cstride = (size_t)kC * rowstride;
+    const uint32_t last_rows = (uint32_t)(seqlen - (int64_t)kC * (nch - 1));
+    auto chunk_rows = [&](int cc) -> uint32_t {
+        return cc < 0 ? 0u : cc < nch - 1 ? (uint32_t)kC : cc == nch - 1 ? last_rows : 0u;
+    };
+    const uint32_t row_bytes = (uint32_t)(rowstride * 2);
+    const size_t seq0 = (size_t)bos * rowstride;
+    auto tok_rsrc = [&](const bf16* base, int cc) {
+        return make_rsrc_u32(base + seq0 + (size_t)(cc < 0 ? 0 : cc) * cstride, chunk_rows(cc) * row_bytes);
+    };
+    auto beta_rsrc = [&](int cc) {
+        return make_rsrc_u32(bt + (size_t)bos * a.H + (size_t)(cc < 0 ? 0 : cc) * kC * a.H,
+                             chunk_rows(cc) * (uint32_t)a.H * 2);
     };
 
     if (wave < NSW) {
@@ -174,25 +184,18 @@ __global__ __launch_bounds__((RwsCfg<NSW>::NT)) void bwd_dh_ws_kernel(BwdArgs a,
                 for (int e = 0; e < 4; ++e)
                     D[it][e] = src ? src[(16 * it + 4 * g + e) * kHeadDim + colw0] : 0.f;
         }
-        // dO of a step: rows 4g .. 4g+3 of this lane's column, four steps ahead
-        const uint32_t do_lane = (uint32_t)(((size_t)(4 * g) * rowstride + headoff + colw0) * 2);
-        const uint32_t do_row = (uint32_t)(rowstride * 2);
-        bf16 dor[4][4];
-        auto load_do = [&](auto slot_c, int y) {
-            constexpr int sv = decltype(slot_c)::value;
-            const rsrc_t rd = rows_rsrc(dout, 2, rowstride, chunk_of(y));
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dor[sv][e] = buf_load_bf16(rd, do_lane + e * do_row);
-        };
-        load_do(std::integral_constant<int, 0>{}, 0);
-
-        auto state_iter = [&](auto slot_c, int y) {
-            constexpr int sv = decltype(slot_c)::value;  // == y & 3
+        // dO of a step arrives in an LDS tile (the prep waves load it):
+        // rows 4g .. 4g+3 of this lane's column by a transposed read
+        constexpr int VP = K::VP;
+        auto state_iter = [&](int y) {
             if (y >= 0 && y < nch) {
                 const int cc = chunk_of(y);
                 floatx4 dob;
+                {
+                    const bf16x4 d4 = lds_col4(do_s(y) + 4 * g * VP + 16 * wave, VP, l16);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) dob[e] = (float)dor[sv][e];
+                    for (int e = 0; e < 4; ++e) dob[e] = (float)d4[e];
+                }
                 // the table entry of this chunk: D before the update
                 {
                     const rsrc_t rs = make_rsrc(
@@ -217,15 +220,16 @@ __global__ __launch_bounds__((RwsCfg<NSW>::NT)) void bwd_dh_ws_kernel(BwdArgs a,
                     mma_bf16_k16(frag_k16(tt_s(y) + l16 * TP, 0, g), acc_frag_k16(dU), zero4());
                 // D <- Diag(Gamma) D + Qt^T dO - Kt^T dX
                 const float* Gm = gam_s(y);
-                const bf16* QtT = qt_s(y);
-                const bf16* KtTn = kt_s(y);
+                const bf16* Qs = qs_s(y);
+                const bf16* Kn = kn_s(y);
                 const bf16x4 dob16 = acc_frag_k16(dob), dX16 = acc_frag_k16(dX);
 #pragma unroll
                 for (int it = 0; it < 8; ++it) {
                     const floatx4 gm = *reinterpret_cast<const floatx4*>(Gm + 16 * it + 4 * g);
                     floatx4 d = D[it] * gm;
-                    d = mma_bf16_k16(frag_k16(QtT + (16 * it + l16) * TP, 0, g), dob16, d);
-                    d = mma_bf16_k16(frag_k16(KtTn + (16 * it + l16) * TP, 0, g), dX16, d);
+                    // Qt^T and -Kt^T rows 16 it .. +15 over tokens 4g .. 4g+3
+                    d = mma_bf16_k16(lds_col4(Qs + 4 * g * KP + 16 * it, KP, l16), dob16, d);
+                    d = mma_bf16_k16(lds_col4(Kn + 4 * g * KP + 16 * it, KP, l16), dX16, d);
                     D[it] = d;
                 }
             }
@@ -233,14 +237,13 @@ __global__ __launch_bounds__((RwsCfg<NSW>::NT)) void bwd_dh_ws_kernel(BwdArgs a,
                 const int zy = y + 2;
                 if (zy >= 0 && zy < nch) gram_tile(wave == 1, zy);
             }
-            load_do(slot_c, y + 4);
             __syncthreads();
         };
         for (int y = -3; y < nit - 3; y += 4) {
-            state_iter(std::integral_constant<int, 1>{}, y);
-            state_iter(std::integral_constant<int, 2>{}, y + 1);
-            state_iter(std::integral_constant<int, 3>{}, y + 2);
-            state_iter(std::integral_constant<int, 0>{}, y + 3);
+            state_iter(y);
+            state_iter(y + 1);
+            state_iter(y + 2);
+            state_iter(y + 3);
         }
         if (a.dh0) {
             float* dst = a.dh0 + ((size_t)n * a.H + h) * kState;
@@ -258,15 +261,28 @@ __global__ __launch_bounds__((RwsCfg<NSW>::NT)) void bwd_dh_ws_kernel(BwdArgs a,
     const int ch0 = 16 * pw + 4 * g;  // first of this lane's 4 key channels
     bf16x4 rq[4], rk[4], rg[4];
     bf16 rb[4];
+    // dO for the state waves: prep waves 4 - DV / 32 .. 3 load one 16-byte
+    // piece of a row of the step's 16 x DV tile per lane, four steps ahead,
+    // and write it to the tile in the iteration that prepares the step
+    constexpr int VP = K::VP;
+    static_assert(DV / 32 <= 4, "dO waves are prep waves 0..3");
+    const bool io_wave = pw >= 4 - DV / 32 && pw < 4;
+    const int io_u = (pw - (4 - DV / 32)) * 64 + lane;
+    const int io_row = io_u / (DV / 8), io_col = (io_u % (DV / 8)) * 8;
+    const uint32_t io_off = (uint32_t)(((size_t)io_row * rowstride + headoff + col0 + io_col) * 2);
+    bf16x8 rdo[4];
     const uint32_t qo_lane = (uint32_t)(((size_t)r * rowstride + headoff + ch0) * 2);
     const uint32_t bo_lane = (uint32_t)(((size_t)r * a.H + h) * 2);
     auto load_step = [&](auto slot_c, int y) {
         constexpr int s = decltype(slot_c)::value;
         const int cc = chunk_of(y);
-        rq[s] = buf_load_bf16x4(rows_rsrc(q, 2, rowstride, cc), qo_lane);
-        rk[s] = buf_load_bf16x4(rows_rsrc(k, 2, rowstride, cc), qo_lane);
-        rg[s] = buf_load_bf16x4(rows_rsrc(lg, 2, rowstride, cc), qo_lane);
-        rb[s] = buf_load_bf16(rows_rsrc(bt, 2, (size_t)a.H, cc), bo_lane);
+        rq[s] = buf_load_bf16x4(tok_rsrc(q, cc), qo_lane);
+        rk[s] = buf_load_bf16x4(tok_rsrc(k, cc), qo_lane);
+        rg[s] = buf_load_bf16x4(tok_rsrc(lg, cc), qo_lane);
+        rb[s] = buf_load_bf16(beta_rsrc(cc), bo_lane);
+        if (io_wave)
+            rdo[s] = __builtin_bit_cast(
+                bf16x8, __builtin_amdgcn_raw_buffer_load_b128(tok_rsrc(dout, cc), (int)io_off, 0, 0));
     };
     load_step(std::integral_constant<int, 0>{}, 0);
     load_step(std::integral_constant<int, 1>{}, 1);
@@ -288,8 +304,6 @@ __global__ __launch_bounds__((RwsCfg<NSW>::NT)) void bwd_dh_ws_kernel(BwdArgs a,
             }
             bf16x4 kv, kn, qs, kh;
             floatx4 gam;
-            bf16* QtT = qt_s(yp);
-            bf16* KtTn = kt_s(yp);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float P = row_prefix_sum(lgv[e]);       // G_r / ln 2
@@ -302,8 +316,6 @@ __global__ __launch_bounds__((RwsCfg<NSW>::NT)) void bwd_dh_ws_kernel(BwdArgs a,
                 kn[e] = (bf16)(-kt);
                 qs[e] = (bf16)qt;
                 kh[e] = (bf16)(kf[e] * Einv);
-                QtT[(ch0 + e) * TP + r] = (bf16)qt;
-                KtTn[(ch0 + e) * TP + r] = (bf16)(-kt);
             }
             *reinterpret_cast<bf16x4*>(kv_s(yp) + r * KP + ch0) = kv;
             *reinterpret_cast<bf16x4*>(kn_s(yp) + r * KP + ch0) = kn;
@@ -311,6 +323,7 @@ __global__ __launch_bounds__((RwsCfg<NSW>::NT)) void bwd_dh_ws_kernel(BwdArgs a,
             *reinterpret_cast<bf16x4*>(kh_s(yp) + r * KP + ch0) = kh;
             if (r == 0) *reinterpret_cast<floatx4*>(gam_s(yp) + ch0) = gam;
             if (pw == 0 && g == 0) beta_s(yp)[r] = b;
+            if (io_wave) *reinterpret_cast<bf16x8*>(do_s(yp) + io_row * VP + io_col) = rdo[s];
         }
         load_step(slot_c, yp + 4);
         // (2) UT transform of step y+1 on prep waves 0-3: lane = (row l16,
