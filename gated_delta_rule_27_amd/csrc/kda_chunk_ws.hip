@@ -54,7 +54,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 // 2^x on the transcendental unit (v_exp_f32); |x| stays far inside its range here
 __device__ __forceinline__ float exp2f_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <int NCT, int NSW_, int PD>
+template <int NCT, int NSW_, int PD, bool DEEP>
 struct WsCfg {
     static constexpr int NSW = NSW_;             // state waves
     static constexpr int NPW = 8;                // prep waves
@@ -67,21 +67,21 @@ struct WsCfg {
     static constexpr size_t szTok = kWsC * KP * 2;        // [16][128] bf16
     static constexpr size_t szTile = kWsC * TP * 2;       // [16][16] bf16
     static constexpr size_t szA = kWsC * AP * 4;          // [16][16] fp32
-    // ring buffers; chunk y's operands are written by the prep stage three
+    // ring buffers; chunk y's operands are written by the prep stage four
     // iterations before the state stage reads them
-    static constexpr size_t KN0 = 0;                        // -Ktil, 4 slots
-    static constexpr size_t QS0 = KN0 + 4 * szTok;          //  Qtil, 4 slots
-    static constexpr size_t KV0 = QS0 + 4 * szTok;          //  Kvec rows, 4 slots
-    static constexpr size_t GAM0 = KV0 + 4 * szTok;         //  Gamma, 4 slots
-    static constexpr size_t KH0 = GAM0 + 4 * 512;           //  Khat, 2 slots
-    static constexpr size_t BETA0 = KH0 + 2 * szTok;        //  beta, 3 slots
-    static constexpr size_t A0 = BETA0 + 3 * 64;            //  A, 2 slots
+    static constexpr size_t KN0 = 0;                        // -Ktil, 5 slots
+    static constexpr size_t QS0 = KN0 + 5 * szTok;          //  Qtil, 5 slots
+    static constexpr size_t KV0 = QS0 + 5 * szTok;          //  Kvec rows, 5 slots
+    static constexpr size_t GAM0 = KV0 + 5 * szTok;         //  Gamma, 5 slots
+    static constexpr size_t KH0 = GAM0 + 5 * 512;           //  Khat, 3 slots
+    static constexpr size_t BETA0 = KH0 + 3 * szTok;        //  beta, 4 slots
+    static constexpr size_t A0 = BETA0 + 4 * 64;            //  A, 2 slots
     static constexpr size_t P0 = A0 + 2 * szA;              //  P, 3 slots
     static constexpr size_t T0 = P0 + 3 * szTile;           //  T, 2 slots
     static constexpr int VP = DV + 8;                       // bf16 stride of the V / O tiles
     static constexpr size_t szVO = kWsC * VP * 2;           // [16][DV] bf16
-    static constexpr size_t VT0 = T0 + 2 * szTile;          //  V of the workgroup's columns, 4 slots
-    static constexpr size_t OT0 = VT0 + 4 * szVO;           //  O of the workgroup's columns, 2 slots
+    static constexpr size_t VT0 = T0 + 2 * szTile;          //  V of the workgroup's columns, 5 slots
+    static constexpr size_t OT0 = VT0 + 5 * szVO;           //  O of the workgroup's columns, 2 slots
     static constexpr size_t TILE0 = OT0 + 2 * szVO;         //  per state wave: bf16 snapshot staging
     static constexpr size_t bytes = TILE0 + NSW * kWsC * kTileTP * 2;
 
@@ -89,14 +89,15 @@ struct WsCfg {
     static_assert(kWsC == kSnapUnit, "snapshots fall on chunk ends");
 };
 
-template <int NCT, int NSW, int PD>
-__global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
+template <int NCT, int NSW, int PD, bool DEEP>
+__global__ __launch_bounds__((WsCfg<NCT, NSW, PD, DEEP>::NT)) void chunk_ws_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ log_alpha, const bf16* __restrict__ beta,
     const float* __restrict__ h0, const int32_t* __restrict__ cu_seqlens, int64_t T_total,
     int32_t H, int32_t split, int32_t units, bf16* __restrict__ o, float* __restrict__ h_T,
     SnapArgs snap, int32_t flags) {
-    typedef WsCfg<NCT, NSW, PD> K;
+    typedef WsCfg<NCT, NSW, PD, DEEP> K;
+    constexpr int GD = DEEP ? 1 : 0;   // extra pipeline depth of the split Gram tiles
     constexpr int KP = K::KP, TP = K::TP, AP = K::AP, DV = K::DV;
 
     // XCD-aware id: slices of one unit share the id's residue mod 8
@@ -110,16 +111,19 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
     const int h = unit % H;
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    auto kn_s = [&](int y) { return reinterpret_cast<bf16*>(smem + K::KN0 + (y & 3) * K::szTok); };
-    auto qs_s = [&](int y) { return reinterpret_cast<bf16*>(smem + K::QS0 + (y & 3) * K::szTok); };
-    auto kv_s = [&](int y) { return reinterpret_cast<bf16*>(smem + K::KV0 + (y & 3) * K::szTok); };
-    auto gam_s = [&](int y) { return reinterpret_cast<float*>(smem + K::GAM0 + (y & 3) * 512); };
-    auto kh_s = [&](int y) { return reinterpret_cast<bf16*>(smem + K::KH0 + (y & 1) * K::szTok); };
-    auto beta_s = [&](int y) { return reinterpret_cast<float*>(smem + K::BETA0 + (y % 3) * 64); };
+    // (chunk indices into the rings are never negative)
+    auto m5 = [](int y) { return (int)((unsigned)y % 5u); };
+    auto m3 = [](int y) { return (int)((unsigned)y % 3u); };
+    auto kn_s = [&](int y) { return reinterpret_cast<bf16*>(smem + K::KN0 + m5(y) * K::szTok); };
+    auto qs_s = [&](int y) { return reinterpret_cast<bf16*>(smem + K::QS0 + m5(y) * K::szTok); };
+    auto kv_s = [&](int y) { return reinterpret_cast<bf16*>(smem + K::KV0 + m5(y) * K::szTok); };
+    auto gam_s = [&](int y) { return reinterpret_cast<float*>(smem + K::GAM0 + m5(y) * 512); };
+    auto kh_s = [&](int y) { return reinterpret_cast<bf16*>(smem + K::KH0 + m3(y) * K::szTok); };
+    auto beta_s = [&](int y) { return reinterpret_cast<float*>(smem + K::BETA0 + (y & 3) * 64); };
     auto a_s = [&](int y) { return reinterpret_cast<float*>(smem + K::A0 + (y & 1) * K::szA); };
-    auto p_s = [&](int y) { return reinterpret_cast<bf16*>(smem + K::P0 + (y % 3) * K::szTile); };
+    auto p_s = [&](int y) { return reinterpret_cast<bf16*>(smem + K::P0 + m3(y) * K::szTile); };
     auto t_s = [&](int y) { return reinterpret_cast<bf16*>(smem + K::T0 + (y & 1) * K::szTile); };
-    auto vt_s = [&](int y) { return reinterpret_cast<bf16*>(smem + K::VT0 + (y & 3) * K::szVO); };
+    auto vt_s = [&](int y) { return reinterpret_cast<bf16*>(smem + K::VT0 + m5(y) * K::szVO); };
     auto ot_s = [&](int y) { return reinterpret_cast<bf16*>(smem + K::OT0 + (y & 1) * K::szVO); };
 
     const int tid = threadIdx.x;
@@ -136,9 +140,14 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
     const size_t rowstride = (size_t)H * kHeadDim;
     const size_t headoff = (size_t)h * kHeadDim;
     const int col0 = slice * DV;
-    // pipeline iterations c = -3 .. nit-4: the prep stage of iteration c
-    // handles chunk c+3, the Gram stage c+2, the solve c+1, the state c
-    const int nit = (nch + 3 + PD - 1) / PD * PD;
+    // pipeline iterations c = -3 .. last: the prep stage of iteration c
+    // handles chunk c+3; the Gram stage chunk c+2 (with DEEP: the first
+    // half, key channels 0-63, of chunk c+2 and the second half of chunk
+    // c+1); the solve chunk c+1 (DEEP: c); the state chunk c (DEEP: c-1).
+    // The loops step PD iterations per trip (register slots are compile-time
+    // per position); iterations past `last` find no chunk to work on.
+    const int last = nch - 1 + GD;
+    const int nit = (last + 4 + PD - 1) / PD * PD;
 
     // An empty sequence has no chunks: only h_T = h0 is written, and no
     // input pointer is touched (they may be null when T_total is 0).  The
@@ -166,15 +175,21 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
 
     // Gram tiles of chunk zc, on MFMA (transposed products: acc(s, r)):
     // A[r][s] = beta_r (Ktil_r . Khat_s), strictly lower (Kn = -Ktil), or
-    // P[r][s] = Qtil_r . Khat_s for s <= r.  Formed by state waves 0 (A) and
-    // 1 (P), which have slack after their own chunk.
-    auto gram_tile = [&](bool isP, int zc) {
+    // P[r][s] = Qtil_r . Khat_s for s <= r.  Without DEEP, state waves 0 (A)
+    // and 1 (P) form whole tiles (nk = 128 key channels from k0 = 0).  With
+    // DEEP a tile is summed over two iterations by one state wave, half of
+    // the key channels in each, the accumulator held in registers across the
+    // barrier: chunks of even index by state waves 0 (A) and 1 (P), odd by 2
+    // and 3, so that every state wave forms half a tile per iteration (one
+    // more pipeline stage: worth it from a few dozen chunks per sequence).
+    auto gram_part = [&](bool isP, int zc, int k0, int nk, bool finish, floatx4& acc) {
         const bf16* arow = kh_s(zc) + l16 * KP;
         const bf16* brow = (isP ? qs_s(zc) : kn_s(zc)) + l16 * KP;
-        floatx4 acc = zero4();
+        if (k0 == 0) acc = zero4();
 #pragma unroll
-        for (int kb = 0; kb < kHeadDim; kb += 32)
-            acc = mma_bf16_k32(frag_k32(arow, kb, g), frag_k32(brow, kb, g), acc);
+        for (int kb = 0; kb < nk; kb += 32)
+            acc = mma_bf16_k32(frag_k32(arow, k0 + kb, g), frag_k32(brow, k0 + kb, g), acc);
+        if (!finish) return;
         if (!isP) {
             const float br = beta_s(zc)[l16];
             floatx4 out;
@@ -227,8 +242,9 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
         constexpr int VP = K::VP;
         const bool write_o = !(flags & kChunkNoOutput);
 
-        auto state_iter = [&](auto slot_c, int c) {
-            constexpr int sv = decltype(slot_c)::value;  // == c & 3
+        floatx4 gacc = zero4();   // the Gram tile this wave is summing
+        auto state_iter = [&](int cit) {
+            const int c = cit - GD;   // the chunk of this iteration's state stage
             if (c >= 0 && c < nch) {
                 const bf16* Kn = kn_s(c) + l16 * KP;
                 const bf16* Qs = qs_s(c) + l16 * KP;
@@ -314,20 +330,24 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
                     }
                 }
             }
-            // the Gram tiles of chunk c+2 (read by the solve and by this
-            // stage two iterations later)
-            if (wave < 2) {
-                const int zc = c + 2;
-                if (zc >= 0 && zc < nch) gram_tile(wave == 1, zc);
+            // Gram tiles: the first half of chunk cit+2 (waves of its parity)
+            // or the second half of chunk cit+1, whose tile is then written
+            // (read by the solve in iteration cit+1 and by this stage in cit+2)
+            if (DEEP && wave < 4) {
+                const bool first = (wave >> 1) == (cit & 1);
+                const int zc = first ? cit + 2 : cit + 1;
+                if (zc >= 0 && zc < nch) gram_part(wave & 1, zc, first ? 0 : 64, 64, !first, gacc);
+            } else if (!DEEP && wave < 2) {
+                const int zc = cit + 2;
+                if (zc >= 0 && zc < nch) gram_part(wave == 1, zc, 0, kHeadDim, true, gacc);
             }
             __syncthreads();
         };
         for (int c = -3; c < nit - 3; c += 4) {
-            // -3 = 1 mod 4: V slots 1, 2, 3, 0
-            state_iter(std::integral_constant<int, 1>{}, c);
-            state_iter(std::integral_constant<int, 2>{}, c + 1);
-            state_iter(std::integral_constant<int, 3>{}, c + 2);
-            state_iter(std::integral_constant<int, 0>{}, c + 3);
+            state_iter(c);
+            state_iter(c + 1);
+            state_iter(c + 2);
+            state_iter(c + 3);
         }
         if (h_T) {
             float* dst = h_T + ((size_t)n * (size_t)H + h) * (kHeadDim * kHeadDim);
@@ -356,7 +376,7 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
     // V in / O out for the state waves: prep waves 4 - DV / 32 .. 3 move
     // one 16-byte piece of a row of the 16 x DV tile per lane: V of chunk
     // c+3 into its LDS tile (loaded PD iterations earlier) and O of chunk
-    // c-1 out of its tile, in iteration c.  (Those waves also solve; the
+    // c-1-GD out of its tile, in iteration c.  (Those waves also solve; the
     // prep waves that do not are the last to be issued and the busiest.)
     constexpr int VP = K::VP;
     static_assert(DV / 32 <= 4, "V / O waves are prep waves 0..3");
@@ -442,13 +462,13 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
             if (pw == 0 && g == 0) beta_s(yc)[r] = bt;
             if (io_wave) *reinterpret_cast<bf16x8*>(vt_s(yc) + io_row * VP + io_col) = rv[s];
         }
-        if (io_wave && write_o && c - 1 >= 0 && c - 1 < nch) store_o(c - 1);
+        if (io_wave && write_o && c - 1 - GD >= 0 && c - 1 - GD < nch) store_o(c - 1 - GD);
         load_chunk(slot_c, yc + PD);
-        // (3) UT transform of chunk c+1 on prep waves 0-3: lane = (row
+        // (3) UT transform of chunk c+1-GD on prep waves 0-3: lane = (row
         // l16, column 4 * pw + g) of X = (I + A)^{-1}; forward elimination
         // down the columns of A, the pivot X[sc][c] broadcast along the row
         // of 16 lanes by DPP.
-        const int wc = c + 1;
+        const int wc = c + 1 - GD;
         if (wc >= 0 && wc < nch && pw < 4) {
             const float* Arow = a_s(wc) + l16 * AP;
             float a[16];
@@ -487,16 +507,16 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD>::NT)) void chunk_ws_kernel(
         if constexpr (PD > 2) prep_iter(std::integral_constant<int, 2 % PD>{}, c + 2);
         if constexpr (PD > 3) prep_iter(std::integral_constant<int, 3 % PD>{}, c + 3);
     }
-    // O of the last iteration's chunk (its tile was written before the final barrier)
-    if (io_wave && write_o && nit - 4 < nch) store_o(nit - 4);
+    // O of the last chunk (its tile was written before the final barrier)
+    if (io_wave && write_o) store_o(nch - 1);
 }
 
-template <int NCT, int NSW, int PD>
+template <int NCT, int NSW, int PD, bool DEEP>
 hipError_t launch_ws_t(const ChunkArgs& a, hipStream_t stream) {
-    typedef WsCfg<NCT, NSW, PD> K;
+    typedef WsCfg<NCT, NSW, PD, DEEP> K;
     static_assert(PD % 2 == 0, "the state waves step two chunks per trip");
     const int split = kHeadDim / K::DV;
-    auto kern = chunk_ws_kernel<NCT, NSW, PD>;
+    auto kern = chunk_ws_kernel<NCT, NSW, PD, DEEP>;
     hipError_t e = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)K::bytes);
     if (e != hipSuccess) return e;
@@ -513,9 +533,14 @@ hipError_t launch_ws_t(const ChunkArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_chunk_ws(const ChunkArgs& a, int split, hipStream_t stream) {
+    // the deeper pipeline costs one more iteration per sequence and saves a
+    // few percent per iteration: used from 512 tokens per sequence on average
+    const bool deep = a.N > 0 && a.T_total >= 512 * (int64_t)a.N;
     switch (split) {
-        case 1: return launch_ws_t<1, 8, 4>(a, stream);  // 16 waves, 128 columns
-        case 2: return launch_ws_t<1, 4, 4>(a, stream);  // 12 waves, 64 columns
+        case 1:   // 16 waves, 128 columns
+            return deep ? launch_ws_t<1, 8, 4, true>(a, stream) : launch_ws_t<1, 8, 4, false>(a, stream);
+        case 2:   // 12 waves, 64 columns
+            return deep ? launch_ws_t<1, 4, 4, true>(a, stream) : launch_ws_t<1, 4, 4, false>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }
