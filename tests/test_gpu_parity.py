@@ -34,6 +34,10 @@ SMALL = [
     ("bf16", [0, 1, 37, 16, 100, 5], 2, 0.3, 32, 0),
     ("bf16", [1000], 8, None, 0, 0),
     ("bf16", [333, 31, 700], 4, 0.02, 0, 0),
+    # 512 tokens or more per sequence on average: the deeper bf16 pipeline
+    # (Gram tiles over two iterations), with empty and sub-chunk sequences
+    ("bf16", [4000, 0, 1, 15, 16, 17], 2, 0.3, 16, 1),
+    ("bf16", [4000, 0, 1, 15, 16, 17], 2, 0.3, 16, 2),
 ]
 
 
@@ -52,20 +56,22 @@ def test_small_parity(dtype, lengths, H, h0_std, chunk, split):
 
 
 PER_CHUNK = [
-    # dtype, chunk, split: every kernel variant of the prefill path
-    ("bf16", 16, 1), ("bf16", 16, 2), ("bf16", 32, 1), ("bf16", 32, 4),
-    ("f32", 16, 1), ("f32", 16, 2), ("f32", 32, 4),
+    # dtype, chunk, split, T: every kernel variant of the prefill path (the
+    # bf16 chunk-16 kernel also with 640 tokens: its deeper schedule)
+    ("bf16", 16, 1, 160), ("bf16", 16, 2, 160), ("bf16", 32, 1, 160), ("bf16", 32, 4, 160),
+    ("f32", 16, 1, 160), ("f32", 16, 2, 160), ("f32", 32, 4, 160),
+    ("bf16", 16, 1, 640), ("bf16", 16, 2, 640),
 ]
 
 
-@pytest.mark.parametrize("dtype,chunk,split", PER_CHUNK)
-def test_every_chunk_output_under_slow_decay(dtype, chunk, split):
+@pytest.mark.parametrize("dtype,chunk,split,T", PER_CHUNK)
+def test_every_chunk_output_under_slow_decay(dtype, chunk, split, T):
     """Each chunk's output separately, with slow decay (log alpha near 0) so
     that the incoming state carries into every chunk, and a non-zero h0:
     a wrong output in any one chunk (for instance in one unrolled copy of a
     pipelined loop) fails here even when the whole-tensor norm would hide it."""
     kda = need_gpu()
-    T, H = 160, 2
+    H = 2
     case(f"per-chunk dtype={dtype} T={T} H={H} chunk={chunk} split={split} decay_mu=-6")
     d = kda_inputs.prefill_inputs(T, H, dtype=dtype, device="cuda", seed=4242, h0_std=0.1,
                                   decay_mu=-6.0)
