@@ -162,171 +162,142 @@ __global__ __launch_bounds__(256 * NS) void decode_kernel(
 // only when update_state is set (a speculative draft is verified without
 // touching the cached state, and the accepted prefix replayed on chip:
 // "From GPT-2 to Kimi K3", "Speculative decoding cannot naively roll KDA
-// back").  Same thread mapping as decode_kernel; per token the small vectors
-// go to an LDS buffer chosen by the token's parity, so one token's reads and
-// the next token's writes never meet, and three barriers order each step.
-// Token t of sequence b is applied only for t < n_b (n_tok[b] clamped to
-// [0, K]); later tokens become exact no-ops (alpha = 1, beta = 0, k = 0) and
-// write no output.
+// back").  Token t of sequence b is applied only for t < n_b (n_tok[b]
+// clamped to [0, K]); later tokens are skipped and write no output.
+//
+// Mapping: a workgroup of 256 * NS threads owns NS states, four wavefronts
+// per state; wavefront w of a state owns value columns 32 w .. 32 w + 31 over
+// all 128 rows, lane = (row slice lane / 8: rows 16 (lane / 8) .. +15,
+// column group lane % 8: 4 columns).  The column sums p = S'^T k and
+// r = S'^T q then stay inside the wavefront (16 rows in registers, then 8
+// row slices by lane exchanges), so a token needs no barrier: the per-token
+// vectors of up to KB tokens are staged in LDS per block (two barriers per
+// block), and each wavefront runs its tokens on its own.
 template <typename TIn, int NS>
 __global__ __launch_bounds__(256 * NS) void decode_multi_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
     const TIn* __restrict__ log_alpha, const TIn* __restrict__ beta,
     float* __restrict__ S, const int32_t* __restrict__ n_tok, TIn* __restrict__ o,
     int32_t units, int32_t H, int32_t K, int32_t update_state) {
-    constexpr int kWaves = 4 * NS;
-    constexpr int kRowStep = 8 * NS;
-    constexpr int kLoadsPerState = kStateLoads / NS;
-    static_assert(kRowStep * kLoadsPerState == kHeadDim, "a state is 128 rows");
+    constexpr int KB = 8;   // tokens per block of staged vectors
 
     const int t = threadIdx.x;
-    const int cg = t & 31;
-    const int rg = t >> 5;
+    const int lane = t & 63;
+    const int w = t >> 6;
+    const int s = w >> 2;                 // state of this wavefront in the block
+    const int c0 = 32 * (w & 3) + 4 * (lane & 7);   // this lane's first column
+    const int r0 = 16 * (lane >> 3);               // this lane's first row
     const int first = NS * blockIdx.x;
     const int nvalid = min(NS, units - first);
 
-    __shared__ float sk[2][NS][kHeadDim], sq[2][NS][kHeadDim], sa[2][NS][kHeadDim],
-        sv[2][NS][kHeadDim];
-    __shared__ float skq[2][NS][2];
-    __shared__ float su[NS][kHeadDim];
-    __shared__ floatx4 sred[kWaves][NS][2][kHeadDim / 4];
+    __shared__ __attribute__((aligned(16))) float sk[KB][NS][kHeadDim];
+    __shared__ __attribute__((aligned(16))) float sq[KB][NS][kHeadDim];
+    __shared__ __attribute__((aligned(16))) float sa[KB][NS][kHeadDim];
+    __shared__ __attribute__((aligned(16))) float sv[KB][NS][kHeadDim];
+    __shared__ float sb[KB][NS], skq[KB][NS];
 
-    // tokens to apply for each state of the block (uniform)
-    int nt[NS];
-    int tmax = 0;
+    // tokens to apply per state of the block; the block loop runs to the
+    // largest (uniform over the workgroup), each wavefront to its own
+    int tmax = 0, nt = 0;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
+    for (int j = 0; j < NS; ++j) {
         int c = 0;
-        if (s < nvalid) {
-            const int b = (first + s) / H;
-            c = n_tok ? n_tok[b] : K;
+        if (j < nvalid) {
+            c = n_tok ? n_tok[(first + j) / H] : K;
             c = c < 0 ? 0 : (c > K ? K : c);
         }
-        nt[s] = __builtin_amdgcn_readfirstlane(c);
-        tmax = max(tmax, nt[s]);
+        tmax = max(tmax, c);
+        if (j == s) nt = c;
     }
+    tmax = __builtin_amdgcn_readfirstlane(tmax);
+    nt = __builtin_amdgcn_readfirstlane(nt);
 
-    // thread t serves the per-token vectors of state t / 256 (as in decode)
-    const int ms = t >> 8;
-    const int j = t & 255;
-    const int jc = j & (kHeadDim - 1);
-    const bool kside = j < kHeadDim;
-    const int unit_v = first + min(ms, nvalid - 1);
-    const size_t bv = (size_t)(unit_v / H) * K;   // first token row of the sequence
-    const size_t hv = (size_t)(unit_v % H);
-    auto tok_off = [&](int tt) { return ((bv + tt) * (size_t)H + hv) * kHeadDim; };
-    auto tok_beta = [&](int tt) { return (bv + tt) * (size_t)H + hv; };
-    int nt_ms = nt[0];
+    const int unit = first + min(s, nvalid - 1);   // a valid state for addressing
+    const size_t b = (size_t)(unit / H), h = (size_t)(unit % H);
+    float* Sw = S + (size_t)unit * (kHeadDim * kHeadDim) + (size_t)r0 * kHeadDim + c0;
+    floatx4 st[16];
 #pragma unroll
-    for (int s = 1; s < NS; ++s) nt_ms = ms == s ? nt[s] : nt_ms;
+    for (int m = 0; m < 16; ++m)
+        st[m] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(Sw + m * kHeadDim));
 
-    // token 0's vectors first, then the state (its wait does not hold them back)
-    TIn r0, r1, r2, rb;
-    auto load_tok = [&](int tt) {
-        const int tc = tt < K ? tt : K - 1;   // always a valid token row
-        const size_t off = tok_off(tc);
-        r0 = (kside ? k : v)[off + jc];
-        r1 = q[off + jc];
-        r2 = log_alpha[off + jc];
-        rb = beta[tok_beta(tc)];
-    };
-    load_tok(0);
-
-    float* Sb = S + (size_t)first * (kHeadDim * kHeadDim);
-    floatx4 st[kStateLoads];
-#pragma unroll
-    for (int m = 0; m < kStateLoads; ++m) {
-        const int s = m / kLoadsPerState;
-        const int row = rg + kRowStep * m;
-        const int src = s < nvalid ? row : (row & (kHeadDim - 1));
-        st[m] = __builtin_nontemporal_load(
-            reinterpret_cast<const floatx4*>(Sb + src * kHeadDim + 4 * cg));
-    }
-
-    const int pr = (t >> 7) & 1;
-    const int col = t & (kHeadDim - 1);
-    const float* red = reinterpret_cast<const float*>(&sred[0][0][0][0]);
-
-    for (int tt = 0; tt < tmax; ++tt) {
-        const int par = tt & 1;
-        // this token's vectors to LDS; a token past the sequence's count is
-        // an exact no-op: alpha = 1, beta = 0, k = 0
-        const bool live = tt < nt_ms;
-        const float x0 = live ? to_f32(r0) : (kside ? 0.f : to_f32(r0));
-        const float x1 = to_f32(r1);
-        const float x2 = live ? to_f32(r2) : 0.f;
-        const float bcur = live ? to_f32(rb) : 0.f;
-        (kside ? sk[par][ms] : sv[par][ms])[jc] = x0;
-        sq[par][ms][jc] = x1;
-        sa[par][ms][jc] = expf(x2);
-        const float kq_part = wave_sum(x0 * x1);
-        if (kside && (j & 63) == 0) skq[par][ms][j >> 6] = kq_part;
-        // the next token's vectors are in flight during this token's work
-        load_tok(tt + 1);
+    // staging: wavefront w takes (state, token) pairs w, w + 4 NS, ... of the
+    // block; lane = channels 2 lane, 2 lane + 1
+    constexpr int kPairs = KB * NS;
+    for (int tb = 0; tb < tmax; tb += KB) {
+        __syncthreads();   // the previous block's vectors are no longer read
+        for (int pi = w; pi < kPairs; pi += 4 * NS) {
+            const int js = pi % NS, jt = pi / NS;
+            const int ju = first + min(js, nvalid - 1);
+            const int tt = min(tb + jt, K - 1);   // always a valid token row
+            const size_t row = ((size_t)(ju / H) * K + tt) * H + (size_t)(ju % H);
+            const size_t off = row * kHeadDim + 2 * lane;
+            const float k0 = to_f32(k[off]), k1 = to_f32(k[off + 1]);
+            const float q0 = to_f32(q[off]), q1 = to_f32(q[off + 1]);
+            sk[jt][js][2 * lane] = k0;
+            sk[jt][js][2 * lane + 1] = k1;
+            sq[jt][js][2 * lane] = q0;
+            sq[jt][js][2 * lane + 1] = q1;
+            sa[jt][js][2 * lane] = expf(to_f32(log_alpha[off]));
+            sa[jt][js][2 * lane + 1] = expf(to_f32(log_alpha[off + 1]));
+            sv[jt][js][2 * lane] = to_f32(v[off]);
+            sv[jt][js][2 * lane + 1] = to_f32(v[off + 1]);
+            const float kq = wave_sum(k0 * q0 + k1 * q1);
+            if (lane == 0) {
+                skq[jt][js] = kq;
+                sb[jt][js] = to_f32(beta[row]);
+            }
+        }
         __syncthreads();
 
-        // retain, partial recall p = S'^T k and read r = S'^T q
-        floatx4 p[NS], r[NS];
+        const int nb = min(KB, nt - tb);   // this wavefront's tokens in the block
+        for (int i = 0; i < nb; ++i) {
+            const int tt = tb + i;
+            // retain (scale rows), partial recall p = S'^T k and read r = S'^T q,
+            // four rows at a time
+            floatx4 p = zero4(), r = zero4();
 #pragma unroll
-        for (int s = 0; s < NS; ++s) p[s] = r[s] = zero4();
+            for (int e = 0; e < 4; ++e) {
+                const floatx4 al = *reinterpret_cast<const floatx4*>(&sa[i][s][r0 + 4 * e]);
+                const floatx4 kk = *reinterpret_cast<const floatx4*>(&sk[i][s][r0 + 4 * e]);
+                const floatx4 qq = *reinterpret_cast<const floatx4*>(&sq[i][s][r0 + 4 * e]);
 #pragma unroll
-        for (int m = 0; m < kStateLoads; ++m) {
-            const int s = m / kLoadsPerState;
-            const int i = (rg + kRowStep * m) & (kHeadDim - 1);
-            st[m] *= sa[par][s][i];
-            p[s] += sk[par][s][i] * st[m];
-            r[s] += sq[par][s][i] * st[m];
-        }
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
+                for (int x = 0; x < 4; ++x) {
+                    st[4 * e + x] *= al[x];
+                    p += kk[x] * st[4 * e + x];
+                    r += qq[x] * st[4 * e + x];
+                }
+            }
+            // over the 8 row slices of the wavefront
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                p[s][c] += __shfl_xor(p[s][c], 32, 64);
-                r[s][c] += __shfl_xor(r[s][c], 32, 64);
+#pragma unroll
+                for (int x = 8; x < 64; x <<= 1) {
+                    p[c] += __shfl_xor(p[c], x, 64);
+                    r[c] += __shfl_xor(r[c], x, 64);
+                }
             }
-        }
-        if ((t & 32) == 0) {
-            const int w = t >> 6;
+            // u = beta (v - p); read-out o = r + u (k . q); S = S' + k u^T
+            const floatx4 vv = *reinterpret_cast<const floatx4*>(&sv[i][s][c0]);
+            const floatx4 u = sb[i][s] * (vv - p);
+            if (lane < 8 && s < nvalid) {
+                const floatx4 ov = r + u * skq[i][s];
+                TIn* dst = o + ((b * K + tt) * H + h) * kHeadDim + c0;
 #pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                sred[w][s][0][cg] = p[s];
-                sred[w][s][1][cg] = r[s];
+                for (int c = 0; c < 4; ++c) dst[c] = from_f32<TIn>(ov[c]);
             }
-        }
-        __syncthreads();
-
-        // column sums; the recall sums give u = beta (v - p)
-        float acc = 0.f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) acc += red[((w * NS + ms) * 2 + pr) * kHeadDim + col];
-        if (pr == 0) su[ms][col] = bcur * (sv[par][ms][col] - acc);
-        __syncthreads();
-
-        // read-out o = r + u (k . q)
-        if (pr == 1 && ms < nvalid && live) {
-            const float kq = skq[par][ms][0] + skq[par][ms][1];
-            o[tok_off(tt) + col] = from_f32<TIn>(acc + su[ms][col] * kq);
-        }
-        // erase + write: S = S' + k u^T
-        floatx4 uu[NS];
+            for (int e = 0; e < 4; ++e) {
+                const floatx4 kk = *reinterpret_cast<const floatx4*>(&sk[i][s][r0 + 4 * e]);
 #pragma unroll
-        for (int s = 0; s < NS; ++s) uu[s] = *reinterpret_cast<const floatx4*>(&su[s][4 * cg]);
-#pragma unroll
-        for (int m = 0; m < kStateLoads; ++m) {
-            const int s = m / kLoadsPerState;
-            const int i = (rg + kRowStep * m) & (kHeadDim - 1);
-            st[m] += sk[par][s][i] * uu[s];
+                for (int x = 0; x < 4; ++x) st[4 * e + x] += kk[x] * u;
+            }
         }
     }
 
-    if (update_state) {
+    if (update_state && s < nvalid && nt > 0) {
 #pragma unroll
-        for (int m = 0; m < kStateLoads; ++m) {
-            const int s = m / kLoadsPerState;
-            const int row = rg + kRowStep * m;
-            if (s < nvalid)
-                __builtin_nontemporal_store(st[m], reinterpret_cast<floatx4*>(Sb + row * kHeadDim + 4 * cg));
-        }
+        for (int m = 0; m < 16; ++m)
+            __builtin_nontemporal_store(st[m], reinterpret_cast<floatx4*>(Sw + m * kHeadDim));
     }
 }
 
@@ -349,7 +320,7 @@ void launch_decode_ns(const DecodeArgs& a, int dtype, int32_t units, hipStream_t
 hipError_t launch_decode_multi(const DecodeMultiArgs& a, int dtype, hipStream_t stream) {
     const int64_t units = (int64_t)a.B * a.H;
     if (units == 0) return hipSuccess;
-    constexpr int NS = kDecodeStates;
+    constexpr int NS = 1;   // one state (four wavefronts) per workgroup: three workgroups per CU
     const dim3 grid((unsigned)((units + NS - 1) / NS)), block(256 * NS);
     if (dtype == 0) {
         decode_multi_kernel<float, NS><<<grid, block, 0, stream>>>(

@@ -320,8 +320,10 @@ kda_status kda_epilogue(const void* o, const void* g, const float* norm_w,
  * the pre-draft state ("From GPT-2 to Kimi K3", "Speculative decoding
  * cannot naively roll KDA back"); with update_state = 0 this call is the
  * verify pass (outputs only), with update_state = 1 and n_tok = the accepted
- * counts it is the replay.  Token t of sequence b gives exactly what t + 1
- * calls of kda_decode_step would.
+ * counts it is the replay.  Token t of sequence b gives what t + 1 calls of
+ * kda_decode_step would, to rounding (the column sums over the state's rows
+ * are accumulated in another order); verify and replay of the same tokens
+ * give bit-identical outputs, being the same kernel.
  *
  *   q, k, log_alpha : [B, K, H, Dk]  dt   (sequence-major, then token)
  *   v               : [B, K, H, Dv]  dt

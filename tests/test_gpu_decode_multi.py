@@ -42,6 +42,7 @@ MULTI = [
     ("f32", 5, 4, 2, None, True),
     ("f32", 6, 16, 2, [16, 9, 1, 0, 12, 15], True),
     ("bf16", 3, 1, 96, None, True),                          # K = 1 at the K3 width
+    ("bf16", 4, 20, 3, [20, 17, 8, 9], True),                # three blocks of staged tokens
 ]
 
 
@@ -73,6 +74,9 @@ def test_decode_multi_matches_oracle(dtype, B, K, H, n_tok, update):
 
 
 def test_decode_multi_one_token_equals_decode_step():
+    """K = 1 is one decode step: the two kernels sum the state's columns in a
+    different order (the multi-token kernel keeps them inside a wavefront),
+    so they agree to rounding, not bit for bit."""
     kda = need_gpu()
     B, H = 16, 96
     case(f"decode_multi K=1 vs decode_step B={B} H={H}")
@@ -82,7 +86,8 @@ def test_decode_multi_one_token_equals_decode_step():
     o2 = kda.kda_decode_multi(*[dd[x].unsqueeze(1) for x in ("q", "k", "v", "log_alpha",
                                                               "beta")], S2)
     torch.cuda.synchronize()
-    assert torch.equal(o1, o2[:, 0]) and torch.equal(S1, S2)
+    check("o: multi-token K=1 vs decode step", np_(o2[:, 0]), np_(o1).astype(np.float64), 1e-2)
+    check("S: multi-token K=1 vs decode step", np_(S2), np_(S1).astype(np.float64), 1e-5)
 
 
 def test_decode_multi_agrees_with_the_chunk_path():
