@@ -93,7 +93,7 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
                           kda_dtype dt, void* o, float* h_T, void* workspace,
                           size_t workspace_bytes, int32_t chunk, int32_t dv_split,
                           const SnapReq& sr, int32_t flags, hipStream_t stream,
-                          bool check_only = false) {
+                          bool check_only = false, float* h_T2 = nullptr) {
     if (!valid_dtype(dt)) return KDA_ERR_BAD_DTYPE;
     if (N < 1 || T_total < 0 || H < 1 || H > KDA_MAX_HEADS || Dk != kda::kHeadDim ||
         Dv != kda::kHeadDim)
@@ -157,6 +157,9 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
     // bf16 snapshots exist in the pipelined bf16 kernel only (chunk 16, split 1 or 2)
     if ((flags & kda::kChunkSnapBf16) && !(dt == KDA_BF16 && c == 16 && s <= 2))
         return KDA_ERR_BAD_SHAPE;
+    // both summary passes in one launch: the bf16 pipelined kernel at split 2
+    if ((flags & kda::kChunkDualBM) && !(dt == KDA_BF16 && c == 16 && s == 2 && sr.n_snap == 0))
+        return KDA_ERR_BAD_SHAPE;
     if (check_only) return KDA_OK;
 
     kda::ChunkArgs a;
@@ -177,6 +180,7 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
     a.snap.n_snap = sr.n_snap;
     a.snap.every_chunks = sr.interval > 0 ? sr.interval / kda::kSnapUnit : 1;
     a.flags = flags;
+    a.h_T2 = h_T2;
     if (kda::launch_chunk(a, (int)dt, c, s, stream) != hipSuccess) return KDA_ERR_DEVICE;
     return KDA_OK;
 }
@@ -271,19 +275,32 @@ kda_status kda_segment_summary(const void* q, const void* k, const void* v,
     // are validated before either is launched.
     const int32_t fB = kda::kChunkNoOutput;
     const int32_t fM = kda::kChunkNoOutput | kda::kChunkVZero | kda::kChunkH0Identity;
-    for (int launch = 0; launch < 2; ++launch) {
-        kda_status st = KDA_OK;
-        if (B)
-            st = chunk_fwd_impl(q, k, v, log_alpha, beta, nullptr, cu_seqlens, N, T_total, H, Dk,
-                                Dv, dt, nullptr, B, workspace, workspace_bytes, 0, 0, SnapReq{},
-                                fB, stream, !launch);
-        if (st == KDA_OK && M)
-            st = chunk_fwd_impl(q, k, v, log_alpha, beta, nullptr, cu_seqlens, N, T_total, H, Dk,
-                                Dv, dt, nullptr, M, workspace, workspace_bytes, 0, 0, SnapReq{},
-                                fM, stream, !launch);
-        if (st != KDA_OK) return st;
-    }
-    return KDA_OK;
+    kda_status st = KDA_OK;
+    if (B)
+        st = chunk_fwd_impl(q, k, v, log_alpha, beta, nullptr, cu_seqlens, N, T_total, H, Dk, Dv,
+                            dt, nullptr, B, workspace, workspace_bytes, 0, 0, SnapReq{}, fB,
+                            stream, true);
+    if (st == KDA_OK && M)
+        st = chunk_fwd_impl(q, k, v, log_alpha, beta, nullptr, cu_seqlens, N, T_total, H, Dk, Dv,
+                            dt, nullptr, M, workspace, workspace_bytes, 0, 0, SnapReq{}, fM,
+                            stream, true);
+    if (st != KDA_OK) return st;
+    // bf16 with both: one launch whose state waves run both passes over the
+    // operands its prep waves form once (the B pass's arguments, validated
+    // above, carry the M states as a second output)
+    if (M && B && dt == KDA_BF16)
+        return chunk_fwd_impl(q, k, v, log_alpha, beta, nullptr, cu_seqlens, N, T_total, H, Dk,
+                              Dv, dt, nullptr, B, workspace, workspace_bytes, 16, 2, SnapReq{},
+                              fB | kda::kChunkDualBM, stream, false, M);
+    if (B)
+        st = chunk_fwd_impl(q, k, v, log_alpha, beta, nullptr, cu_seqlens, N, T_total, H, Dk, Dv,
+                            dt, nullptr, B, workspace, workspace_bytes, 0, 0, SnapReq{}, fB,
+                            stream);
+    if (st == KDA_OK && M)
+        st = chunk_fwd_impl(q, k, v, log_alpha, beta, nullptr, cu_seqlens, N, T_total, H, Dk, Dv,
+                            dt, nullptr, M, workspace, workspace_bytes, 0, 0, SnapReq{}, fM,
+                            stream);
+    return st;
 }
 
 kda_status kda_segment_scan(const float* M, const float* B, const float* h0, int32_t R,

@@ -54,11 +54,12 @@ constexpr float kLog2e = 1.4426950408889634f;
 // 2^x on the transcendental unit (v_exp_f32); |x| stays far inside its range here
 __device__ __forceinline__ float exp2f_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <int NCT, int NSW_, int PD, bool DEEP>
+template <int NCT, int NSW_, int PD, bool DEEP, bool DUAL>
 struct WsCfg {
-    static constexpr int NSW = NSW_;             // state waves
+    static constexpr int NSW = NSW_;             // state waves per pass
+    static constexpr int NSA = DUAL ? 2 * NSW : NSW;   // state waves in all
     static constexpr int NPW = 8;                // prep waves
-    static constexpr int NT = 64 * (NSW + NPW);  // threads
+    static constexpr int NT = 64 * (NSA + NPW);  // threads
     static constexpr int DV = 16 * NCT * NSW;    // value columns per workgroup
     static constexpr int KP = kHeadDim + 8;      // bf16 stride of [token][channel]
     static constexpr int TP = kWsC + 8;          // bf16 stride of [.][token]
@@ -89,14 +90,14 @@ struct WsCfg {
     static_assert(kWsC == kSnapUnit, "snapshots fall on chunk ends");
 };
 
-template <int NCT, int NSW, int PD, bool DEEP>
-__global__ __launch_bounds__((WsCfg<NCT, NSW, PD, DEEP>::NT)) void chunk_ws_kernel(
+template <int NCT, int NSW, int PD, bool DEEP, bool DUAL>
+__global__ __launch_bounds__((WsCfg<NCT, NSW, PD, DEEP, DUAL>::NT)) void chunk_ws_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ log_alpha, const bf16* __restrict__ beta,
     const float* __restrict__ h0, const int32_t* __restrict__ cu_seqlens, int64_t T_total,
     int32_t H, int32_t split, int32_t units, bf16* __restrict__ o, float* __restrict__ h_T,
-    SnapArgs snap, int32_t flags) {
-    typedef WsCfg<NCT, NSW, PD, DEEP> K;
+    float* __restrict__ h_T2, SnapArgs snap, int32_t flags) {
+    typedef WsCfg<NCT, NSW, PD, DEEP, DUAL> K;
     constexpr int GD = DEEP ? 1 : 0;   // extra pipeline depth of the split Gram tiles
     constexpr int KP = K::KP, TP = K::TP, AP = K::AP, DV = K::DV;
 
@@ -153,20 +154,24 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD, DEEP>::NT)) void chunk_ws_kern
     // input pointer is touched (they may be null when T_total is 0).  The
     // branch is uniform over the workgroup, so no barrier is skipped.
     if (nch == 0) {
-        if (wave < K::NSW && h_T) {
-            const float* src = h0 ? h0 + ((size_t)n * (size_t)H + h) * (kHeadDim * kHeadDim) : nullptr;
-            float* dst = h_T + ((size_t)n * (size_t)H + h) * (kHeadDim * kHeadDim);
+        // (with DUAL, state waves NSW .. 2 NSW - 1 write the identity into h_T2)
+        const bool mp = DUAL && wave >= NSW;
+        float* hT = mp ? h_T2 : h_T;
+        if (wave < K::NSA && hT) {
+            const float* src = (h0 && !mp) ? h0 + ((size_t)n * (size_t)H + h) * (kHeadDim * kHeadDim) : nullptr;
+            const bool ident = mp || (flags & kChunkH0Identity);
+            const int sw = mp ? wave - NSW : wave;
+            float* dst = hT + ((size_t)n * (size_t)H + h) * (kHeadDim * kHeadDim);
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
-                const int j = col0 + 16 * (NCT * wave + ct) + l16;
+                const int j = col0 + 16 * (NCT * sw + ct) + l16;
 #pragma unroll
                 for (int it = 0; it < 8; ++it)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int row = 16 * it + 4 * g + e;
                         const int idx = row * kHeadDim + j;
-                        dst[idx] = src ? src[idx]
-                                       : ((flags & kChunkH0Identity) && row == j ? 1.f : 0.f);
+                        dst[idx] = src ? src[idx] : (ident && row == j ? 1.f : 0.f);
                     }
             }
         }
@@ -204,14 +209,21 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD, DEEP>::NT)) void chunk_ws_kern
         }
     };
 
-    if (wave < K::NSW) {
+    if (wave < K::NSA) {
         // ======================= state waves =======================
+        // With DUAL the workgroup runs two passes over the same operands
+        // (segment summaries): waves 0 .. NSW-1 the B pass (zero start, V,
+        // h_T), waves NSW .. 2 NSW - 1 the M pass (identity start, V = 0,
+        // h_T2); sw is the wave's index within its pass.
+        const bool mpass = DUAL && wave >= NSW;
+        const int sw = mpass ? wave - NSW : wave;
         floatx4 S[NCT][8];
         {
-            const float* src = h0 ? h0 + ((size_t)n * (size_t)H + h) * (kHeadDim * kHeadDim) : nullptr;
+            const float* src = (h0 && !mpass) ? h0 + ((size_t)n * (size_t)H + h) * (kHeadDim * kHeadDim)
+                                              : nullptr;
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
-                const int j = col0 + 16 * (NCT * wave + ct) + l16;
+                const int j = col0 + 16 * (NCT * sw + ct) + l16;
 #pragma unroll
                 for (int it = 0; it < 8; ++it)
 #pragma unroll
@@ -220,10 +232,10 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD, DEEP>::NT)) void chunk_ws_kern
             }
             // h0 = I (a separate uniform branch: folded into the loads above,
             // the selects cost registers across the whole chunk loop)
-            if (!src && (flags & kChunkH0Identity)) {
+            if (!src && (mpass || (flags & kChunkH0Identity))) {
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) {
-                    const int j = col0 + 16 * (NCT * wave + ct) + l16;
+                    const int j = col0 + 16 * (NCT * sw + ct) + l16;
 #pragma unroll
                     for (int it = 0; it < 8; ++it)
 #pragma unroll
@@ -235,7 +247,7 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD, DEEP>::NT)) void chunk_ws_kern
         // V arrives in, and O leaves through, LDS tiles of the workgroup's
         // DV columns (the prep waves move them between LDS and memory), so
         // the state waves issue no global memory operations per chunk.
-        const int colw0 = col0 + 16 * NCT * wave + l16;  // this lane's first column
+        const int colw0 = col0 + 16 * NCT * sw + l16;  // this lane's first column
         const int64_t snap_base = (flags & kChunkSnapSlots) ? chunk_slot(bos, n)
                                   : snap.snap_cu ? (int64_t)snap.snap_cu[n] : 0;
         const uint32_t snap_lane = (uint32_t)((4 * g * kHeadDim + colw0) * 4);
@@ -252,10 +264,15 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD, DEEP>::NT)) void chunk_ws_kern
                 floatx4 X[NCT], Ov[NCT], U[NCT];
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) {
-                    // rows 4g..4g+3 of this lane's column (transposed read)
-                    const bf16x4 v4 = lds_col4(vt_s(c) + 4 * g * VP + 16 * (NCT * wave + ct), VP, l16);
+                    // rows 4g..4g+3 of this lane's column (transposed read);
+                    // the M pass takes V as zero
+                    if (mpass) {
+                        X[ct] = zero4();
+                    } else {
+                        const bf16x4 v4 = lds_col4(vt_s(c) + 4 * g * VP + 16 * (NCT * sw + ct), VP, l16);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) X[ct][e] = (float)v4[e];
+                        for (int e = 0; e < 4; ++e) X[ct][e] = (float)v4[e];
+                    }
                     Ov[ct] = zero4();
                 }
                 // X = V - Ktil S, O = Qtil S
@@ -285,7 +302,7 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD, DEEP>::NT)) void chunk_ws_kern
                     for (int e = 0; e < 4; ++e)
 #pragma unroll
                         for (int ct = 0; ct < NCT; ++ct)
-                            ot_s(c)[(4 * g + e) * VP + 16 * (NCT * wave + ct) + l16] = (bf16)Ov[ct][e];
+                            ot_s(c)[(4 * g + e) * VP + 16 * (NCT * sw + ct) + l16] = (bf16)Ov[ct][e];
                 }
                 // S <- Diag(Gamma) S + Kvec^T U
                 const bf16* Kv = kv_s(c);
@@ -314,7 +331,7 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD, DEEP>::NT)) void chunk_ws_kern
 #pragma unroll
                             for (int ct = 0; ct < NCT; ++ct)
                                 store_tile_t(S[ct], tile, rs,
-                                             (uint32_t)((col0 + 16 * (NCT * wave + ct)) * kHeadDim * 2),
+                                             (uint32_t)((col0 + 16 * (NCT * sw + ct)) * kHeadDim * 2),
                                              lane);
                         } else {
                             const rsrc_t rs = make_rsrc(snap.snap + eo, kHeadDim * kHeadDim * 4);
@@ -349,11 +366,12 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD, DEEP>::NT)) void chunk_ws_kern
             state_iter(c + 2);
             state_iter(c + 3);
         }
-        if (h_T) {
-            float* dst = h_T + ((size_t)n * (size_t)H + h) * (kHeadDim * kHeadDim);
+        float* hT = mpass ? h_T2 : h_T;
+        if (hT) {
+            float* dst = hT + ((size_t)n * (size_t)H + h) * (kHeadDim * kHeadDim);
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
-                const int j = col0 + 16 * (NCT * wave + ct) + l16;
+                const int j = col0 + 16 * (NCT * sw + ct) + l16;
 #pragma unroll
                 for (int it = 0; it < 8; ++it)
 #pragma unroll
@@ -365,7 +383,7 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD, DEEP>::NT)) void chunk_ws_kern
     }
 
     // ========================= prep waves =========================
-    const int pw = wave - K::NSW;   // 0..7
+    const int pw = wave - K::NSA;   // 0..7
     const int r = l16;              // token of the chunk
     const int ch0 = 16 * pw + 4 * g;  // first of this lane's 4 key channels
     // register slots of in-flight loads: chunk y lives in slot y % PD.  The
@@ -511,12 +529,12 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD, DEEP>::NT)) void chunk_ws_kern
     if (io_wave && write_o) store_o(nch - 1);
 }
 
-template <int NCT, int NSW, int PD, bool DEEP>
+template <int NCT, int NSW, int PD, bool DEEP, bool DUAL>
 hipError_t launch_ws_t(const ChunkArgs& a, hipStream_t stream) {
-    typedef WsCfg<NCT, NSW, PD, DEEP> K;
+    typedef WsCfg<NCT, NSW, PD, DEEP, DUAL> K;
     static_assert(PD % 2 == 0, "the state waves step two chunks per trip");
     const int split = kHeadDim / K::DV;
-    auto kern = chunk_ws_kernel<NCT, NSW, PD, DEEP>;
+    auto kern = chunk_ws_kernel<NCT, NSW, PD, DEEP, DUAL>;
     hipError_t e = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)K::bytes);
     if (e != hipSuccess) return e;
@@ -526,7 +544,7 @@ hipError_t launch_ws_t(const ChunkArgs& a, hipStream_t stream) {
     kern<<<dim3((unsigned)nwg), dim3(K::NT), K::bytes, stream>>>(
         (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.log_alpha,
         (const bf16*)a.beta, a.h0, a.cu_seqlens, a.T_total, a.H, split, (int32_t)units,
-        (bf16*)a.o, a.h_T, a.snap, a.flags);
+        (bf16*)a.o, a.h_T, a.h_T2, a.snap, a.flags);
     return hipGetLastError();
 }
 
@@ -536,11 +554,18 @@ hipError_t launch_chunk_ws(const ChunkArgs& a, int split, hipStream_t stream) {
     // the deeper pipeline costs one more iteration per sequence and saves a
     // few percent per iteration: used from 512 tokens per sequence on average
     const bool deep = a.N > 0 && a.T_total >= 512 * (int64_t)a.N;
+    if (a.flags & kChunkDualBM) {   // 16 waves: 4 + 4 state waves of 64 columns
+        if (split != 2) return hipErrorInvalidValue;
+        return deep ? launch_ws_t<1, 4, 4, true, true>(a, stream)
+                    : launch_ws_t<1, 4, 4, false, true>(a, stream);
+    }
     switch (split) {
         case 1:   // 16 waves, 128 columns
-            return deep ? launch_ws_t<1, 8, 4, true>(a, stream) : launch_ws_t<1, 8, 4, false>(a, stream);
+            return deep ? launch_ws_t<1, 8, 4, true, false>(a, stream)
+                        : launch_ws_t<1, 8, 4, false, false>(a, stream);
         case 2:   // 12 waves, 64 columns
-            return deep ? launch_ws_t<1, 4, 4, true>(a, stream) : launch_ws_t<1, 4, 4, false>(a, stream);
+            return deep ? launch_ws_t<1, 4, 4, true, false>(a, stream)
+                        : launch_ws_t<1, 4, 4, false, false>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -36,6 +36,10 @@ enum ChunkFlags : int32_t {
                             // of one column an MFMA lane holds go out as one 8-byte
                             // store (the bf16 pipelined kernel only; read by the
                             // backward's per-chunk gradient kernel)
+    kChunkDualBM = 32,      // both segment-summary passes in one launch over shared
+                            // operands: B (zero start, V) into h_T and M (identity
+                            // start, V = 0) into h_T2; no outputs or snapshots (the
+                            // bf16 pipelined kernel, split 2 only)
     kChunkSnapSlots = 8,    // snapshot j of sequence n goes to entry chunk_slot(n) + j
                             // (with a snapshot after every chunk: the per-chunk
                             // state store of the backward pass)
@@ -66,6 +70,7 @@ struct ChunkArgs {
     float* h_T;               // may be null
     SnapArgs snap;            // snap.snap == nullptr: no snapshots
     int32_t flags;            // ChunkFlags
+    float* h_T2 = nullptr;    // kChunkDualBM: the M pass's final states
 };
 
 struct DecodeArgs {
