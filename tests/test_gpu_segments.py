@@ -86,10 +86,12 @@ def test_summary_matches_oracle_transition_and_offset(dtype, lengths, H):
                 check(f"B seg {n} (len {L}) head {hh}", gB[n, hh], B_ref[n, hh], TOL[dtype])
 
 
-def test_summary_parts_alone_equal_the_pair():
-    """Asking for M or B alone gives the same bits as asking for both."""
+@pytest.mark.parametrize("lengths", [[200, 45], [1500, 3, 700]])
+def test_summary_parts_alone_equal_the_pair(lengths):
+    """Asking for M or B alone gives the same bits as asking for both (bf16:
+    one launch for the pair; both pipeline schedules)."""
     kda = need_gpu()
-    lengths, H = [200, 45], 2
+    H = 2
     case(f"segment summary parts lengths={lengths} H={H}")
     d = kda_inputs.prefill_inputs(sum(lengths), H, dtype="bf16", device="cuda", seed=5)
     args = (d["q"], d["k"], d["v"], d["log_alpha"], d["beta"])
