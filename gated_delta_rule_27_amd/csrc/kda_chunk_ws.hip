@@ -23,17 +23,24 @@
 // wavefronts (12 for a 64-column slice, 16 for all 128 columns):
 //   waves 0..NSW-1 (state): each owns 16 * NCT value columns of the 128 x 128
 //     state in MFMA accumulators for the whole sequence and runs the state
-//     chain of chunk c; its V values arrive by its own register prefetch;
-//     state waves 0 and 1 then form the Gram tiles of chunk c+2 (A and P);
+//     chain of chunk c with no global memory operation of its own (V comes
+//     from an LDS ring, O goes to an LDS tile); state waves 0 and 1 then form
+//     the Gram tiles of chunk c+2 (A and P);
 //   the next 8 waves (prep), lane = (token r, 4 key channels): load q, k, log_alpha
 //     of chunk c+3 straight into the lanes that use them (PD chunks ahead),
 //     take the cumulative log-decay over the chunk's 16 tokens as a DPP scan
-//     across the 16 lanes of a row and write the decay-scaled operands;
-//     prep waves 0-3 also run the triangular solve of chunk c+1 (lane = one
-//     element of the 16 x 16 inverse).
+//     across the 16 lanes of a row and write the decay-scaled operands in
+//     token rows; prep waves 0-3 also run the triangular solve of chunk c+1
+//     (lane = one element of the 16 x 16 inverse), and two of them move V in
+//     and O out as 16-byte row pieces.
 // Every stage reads only what an earlier iteration wrote, so one barrier per
 // chunk is the only synchronisation.  LDS holds ring buffers indexed by
-// chunk, each as deep as its value lives (77 KB in all).
+// chunk, each at least as deep as its value lives.
+// Two variants, chosen at launch: DEEP (sequences of 512 tokens and more on
+// average) splits each Gram tile over two iterations and all four state
+// waves, one pipeline stage deeper (the state then runs chunk c-1, the solve
+// chunk c); DUAL (segment summaries) runs two groups of NSW state waves, one
+// per summary pass, over the operands the prep waves form once.
 //
 // Workgroup order is XCD-aware: the `split` workgroups that share one
 // (sequence, head) get ids with the same residue mod 8, i.e. the same XCD
