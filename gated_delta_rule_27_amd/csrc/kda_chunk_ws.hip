@@ -91,13 +91,17 @@ struct WsCfg {
     static constexpr size_t VT0 = T0 + 2 * szTile;          //  V of the workgroup's columns, 5 slots
     static constexpr size_t OT0 = VT0 + 5 * szVO;           //  O of the workgroup's columns, 2 slots
     static constexpr size_t TILE0 = OT0 + 2 * szVO;         //  per state wave: bf16 snapshot staging
-    static constexpr size_t bytes = TILE0 + NSW * kWsC * kTileTP * 2;
+    static constexpr size_t szTiles = NSW * kWsC * kTileTP * 2;
+    // bf16 snapshots: with room for two slots, the state waves only write
+    // their tiles to LDS and the prep waves store them an iteration later
+    static constexpr bool SNAP_PREP = TILE0 + 2 * szTiles <= 160 * 1024;
+    static constexpr size_t bytes = TILE0 + (SNAP_PREP ? 2 : 1) * szTiles;
 
     static_assert(bytes <= 160 * 1024, "LDS budget");
     static_assert(kWsC == kSnapUnit, "snapshots fall on chunk ends");
 };
 
-template <int NCT, int NSW, int PD, bool DEEP, bool DUAL>
+template <int NCT, int NSW, int PD, bool DEEP, bool DUAL, bool SP>
 __global__ __launch_bounds__((WsCfg<NCT, NSW, PD, DEEP, DUAL>::NT)) void chunk_ws_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ log_alpha, const bf16* __restrict__ beta,
@@ -328,7 +332,15 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD, DEEP, DUAL>::NT)) void chunk_w
                     const int64_t idx = snap_base + (c + 1) / snap.every_chunks - 1;
                     if (idx < snap.n_snap) {
                         const size_t eo = ((size_t)idx * (size_t)H + h) * (kHeadDim * kHeadDim);
-                        if (flags & kChunkSnapBf16) {
+                        if (SP) {
+                            // transposed tile into slot c & 1; the prep waves
+                            // store the workgroup's tiles next iteration
+                            bf16* tile = reinterpret_cast<bf16*>(smem + K::TILE0 + (c & 1) * K::szTiles) +
+                                         (size_t)wave * NCT * kWsC * kTileTP;
+#pragma unroll
+                            for (int ct = 0; ct < NCT; ++ct)
+                                tile_to_lds(S[ct], tile + ct * kWsC * kTileTP, lane);
+                        } else if (flags & kChunkSnapBf16) {
                             // transposed entry: this wave's 16 columns are 16
                             // contiguous rows of 128
                             const rsrc_t rs = make_rsrc(reinterpret_cast<bf16*>(snap.snap) + eo,
@@ -431,6 +443,27 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD, DEEP, DUAL>::NT)) void chunk_w
         buf_store_b128(*reinterpret_cast<const bf16x8*>(ot_s(y) + io_row * VP + io_col),
                        make_rsrc_u32(o_seq + (size_t)y * cstride, chunk_rows(y) * row_bytes), io_off, 0);
     };
+    // bf16 snapshot of chunk y from the state waves' LDS tiles (slot y & 1):
+    // the workgroup's DV columns are DV contiguous rows of 128 in the
+    // transposed entry; 512 prep lanes store 16-byte pieces
+    const bool snap_prep = SP && snap.snap;
+    const int64_t snap_base_p = (flags & kChunkSnapSlots) ? chunk_slot(bos, n)
+                                : snap.snap_cu ? (int64_t)snap.snap_cu[n] : 0;
+    auto store_snap = [&](int y) {
+        if (!((y + 1) % snap.every_chunks == 0 && (int64_t)kWsC * (y + 1) <= seqlen)) return;
+        const int64_t idx = snap_base_p + (y + 1) / snap.every_chunks - 1;
+        if (idx >= snap.n_snap) return;
+        const size_t eo = ((size_t)idx * (size_t)H + h) * (kHeadDim * kHeadDim);
+        const rsrc_t rs = make_rsrc(reinterpret_cast<bf16*>(snap.snap) + eo, kHeadDim * kHeadDim * 2);
+        const bf16* tiles = reinterpret_cast<const bf16*>(smem + K::TILE0 + (y & 1) * K::szTiles);
+        const int pl = (wave - K::NSA) * 64 + lane;   // 0..511
+#pragma unroll
+        for (int m = 0; m < DV * 16 / 512; ++m) {
+            const int p = m * 512 + pl, row = p >> 4, col8 = (p & 15) * 8;   // row: column of the state
+            const bf16x8 x = *reinterpret_cast<const bf16x8*>(tiles + (size_t)row * kTileTP + col8);
+            buf_store_b128(x, rs, (uint32_t)(((size_t)(col0 + row) * kHeadDim + col8) * 2), 0);
+        }
+    };
     const uint32_t qo_lane = (uint32_t)(((size_t)r * rowstride + headoff + ch0) * 2);
     const uint32_t bo_lane = (uint32_t)(((size_t)r * H + h) * 2);
     auto load_chunk = [&](auto slot_c, int yc) {
@@ -488,6 +521,7 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD, DEEP, DUAL>::NT)) void chunk_w
             if (io_wave) *reinterpret_cast<bf16x8*>(vt_s(yc) + io_row * VP + io_col) = rv[s];
         }
         if (io_wave && write_o && c - 1 - GD >= 0 && c - 1 - GD < nch) store_o(c - 1 - GD);
+        if (snap_prep && c - 1 - GD >= 0 && c - 1 - GD < nch) store_snap(c - 1 - GD);
         load_chunk(slot_c, yc + PD);
         // (3) UT transform of chunk c+1-GD on prep waves 0-3: lane = (row
         // l16, column 4 * pw + g) of X = (I + A)^{-1}; forward elimination
@@ -532,16 +566,18 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD, DEEP, DUAL>::NT)) void chunk_w
         if constexpr (PD > 2) prep_iter(std::integral_constant<int, 2 % PD>{}, c + 2);
         if constexpr (PD > 3) prep_iter(std::integral_constant<int, 3 % PD>{}, c + 3);
     }
-    // O of the last chunk (its tile was written before the final barrier)
+    // O (and the snapshot) of the last chunk (written before the final barrier)
     if (io_wave && write_o) store_o(nch - 1);
+    if (snap_prep) store_snap(nch - 1);
 }
 
-template <int NCT, int NSW, int PD, bool DEEP, bool DUAL>
+template <int NCT, int NSW, int PD, bool DEEP, bool DUAL, bool SP = false>
 hipError_t launch_ws_t(const ChunkArgs& a, hipStream_t stream) {
     typedef WsCfg<NCT, NSW, PD, DEEP, DUAL> K;
     static_assert(PD % 2 == 0, "the state waves step two chunks per trip");
+    static_assert(!SP || K::SNAP_PREP, "no room for two snapshot tile slots");
     const int split = kHeadDim / K::DV;
-    auto kern = chunk_ws_kernel<NCT, NSW, PD, DEEP, DUAL>;
+    auto kern = chunk_ws_kernel<NCT, NSW, PD, DEEP, DUAL, SP>;
     hipError_t e = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)K::bytes);
     if (e != hipSuccess) return e;
@@ -570,7 +606,10 @@ hipError_t launch_chunk_ws(const ChunkArgs& a, int split, hipStream_t stream) {
         case 1:   // 16 waves, 128 columns
             return deep ? launch_ws_t<1, 8, 4, true, false>(a, stream)
                         : launch_ws_t<1, 8, 4, false, false>(a, stream);
-        case 2:   // 12 waves, 64 columns
+        case 2:   // 12 waves, 64 columns; bf16 snapshots staged for the prep waves
+            if (a.snap.snap && (a.flags & kChunkSnapBf16))
+                return deep ? launch_ws_t<1, 4, 4, true, false, true>(a, stream)
+                            : launch_ws_t<1, 4, 4, false, false, true>(a, stream);
             return deep ? launch_ws_t<1, 4, 4, true, false>(a, stream)
                         : launch_ws_t<1, 4, 4, false, false>(a, stream);
         default: return hipErrorInvalidValue;

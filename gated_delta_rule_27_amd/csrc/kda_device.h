@@ -258,6 +258,16 @@ __device__ __forceinline__ void buf_store_f32(float x, rsrc_t r, uint32_t voff, 
 // first byte.  Only this wave touches `tile`; its LDS operations execute in
 // order, and the fence keeps the compiler from moving them across.
 constexpr int kTileTP = 128 + 8;   // a 128-channel row plus 16 bytes of padding
+// The first half of store_tile_t: the transposed tile into LDS only (16 rows
+// of kTileTP bf16), for other waves to store after a barrier.
+__device__ __forceinline__ void tile_to_lds(const floatx4 (&T)[8], bf16* tile, int lane) {
+    const int l16 = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        *reinterpret_cast<bf16x4*>(tile + l16 * kTileTP + 16 * it + 4 * g) = acc_frag_k16(T[it]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
 __device__ __forceinline__ void store_tile_t(const floatx4 (&T)[8], bf16* tile, rsrc_t r,
                                              uint32_t voff0, int lane) {
     const int l16 = lane & 15, g = lane >> 4;
