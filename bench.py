@@ -428,8 +428,8 @@ def backward(torch, kda, kda_inputs, dev, stream, steps, warmup, fwd_ms):
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--chunk", type=int, default=0, help="override the chunk length")
     ap.add_argument("--split", type=int, default=0, help="override the column split")
     ap.add_argument("--no-cpu-baseline", action="store_true")
