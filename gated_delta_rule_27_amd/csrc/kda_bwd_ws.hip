@@ -372,8 +372,8 @@ hipError_t launch_rws(const BwdArgs& a, hipStream_t stream) {
     typedef RwsCfg<NSW> K;
     const int split = kHeadDim / K::DV;
     auto kern = bwd_dh_ws_kernel<NSW>;
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)K::bytes);
+    static std::atomic<uint64_t> lds_set{0};
+    hipError_t e = raise_lds_limit_once((const void*)kern, (int)K::bytes, lds_set);
     if (e != hipSuccess) return e;
     const int64_t units = (int64_t)a.N * a.H;
     if (units == 0) return hipSuccess;

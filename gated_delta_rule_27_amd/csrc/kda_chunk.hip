@@ -573,8 +573,8 @@ hipError_t launch(const ChunkArgs& a, hipStream_t stream) {
     typedef ChunkCfg<TIn, C, NW, NCT> K;
     const int split = kHeadDim / K::DV;
     auto kern = chunk_kernel<TIn, C, NW, NCT>;
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)K::bytes);
+    static std::atomic<uint64_t> lds_set{0};
+    hipError_t e = raise_lds_limit_once((const void*)kern, (int)K::bytes, lds_set);
     if (e != hipSuccess) return e;
     const int64_t nwg = (int64_t)a.N * a.H * split;
     if (nwg == 0) return hipSuccess;

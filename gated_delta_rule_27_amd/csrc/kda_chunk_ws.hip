@@ -578,8 +578,8 @@ hipError_t launch_ws_t(const ChunkArgs& a, hipStream_t stream) {
     static_assert(!SP || K::SNAP_PREP, "no room for two snapshot tile slots");
     const int split = kHeadDim / K::DV;
     auto kern = chunk_ws_kernel<NCT, NSW, PD, DEEP, DUAL, SP>;
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)K::bytes);
+    static std::atomic<uint64_t> lds_set{0};
+    hipError_t e = raise_lds_limit_once((const void*)kern, (int)K::bytes, lds_set);
     if (e != hipSuccess) return e;
     const int64_t units = (int64_t)a.N * a.H;
     if (units == 0) return hipSuccess;

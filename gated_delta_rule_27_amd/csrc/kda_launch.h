@@ -6,7 +6,25 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace kda {
+
+// Raises a kernel's dynamic LDS limit once per device (64 devices at most
+// are remembered; past that the attribute is set on every launch).  The
+// attribute belongs to the function, not to stream work, so later launches,
+// including launches recorded into a HIP graph, make no attribute calls.
+// `done` is one flag word per kernel instantiation.
+inline hipError_t raise_lds_limit_once(const void* kern, int bytes, std::atomic<uint64_t>& done) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t)1 << dev : 0;
+    if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
+    return e;
+}
 
 constexpr int kHeadDim = 128;  // d_k = d_v of the K3 KDA head
 constexpr int kSnapUnit = 16;  // prefix-snapshot intervals are multiples of this
