@@ -131,7 +131,8 @@ __global__ __launch_bounds__((RwsCfg<NSW>::NT)) void bwd_dh_ws_kernel(BwdArgs a,
     }
 
     // Gram tiles of step zy: acc(s, r) = sum_i Khat_s[i] X_r[i] with X = -Kt
-    // (A[r][s] = beta_r Kt_r . Khat_s, strictly lower) or Qt (P[r][s], s <= r,
+    // (A[r][s] = beta_r Kt_r . Khat_s, strictly lower, stored negated for the
+    // solve to add) or Qt (P[r][s], s <= r,
     // stored transposed as P^T[s][r])
     auto gram_tile = [&](bool isP, int zy) {
         const bf16* arow = kh_s(zy) + l16 * KP;
@@ -144,7 +145,7 @@ __global__ __launch_bounds__((RwsCfg<NSW>::NT)) void bwd_dh_ws_kernel(BwdArgs a,
             const float br = beta_s(zy)[l16];
             floatx4 out;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) out[e] = (4 * g + e >= l16) ? 0.f : -acc[e] * br;
+            for (int e = 0; e < 4; ++e) out[e] = (4 * g + e >= l16) ? 0.f : acc[e] * br;
             *reinterpret_cast<floatx4*>(a_s(zy) + l16 * AP + 4 * g) = out;
         } else {
             bf16* pt = pt_s(zy);
@@ -339,22 +340,22 @@ __global__ __launch_bounds__((RwsCfg<NSW>::NT)) void bwd_dh_ws_kernel(BwdArgs a,
                 for (int e = 0; e < 4; ++e) av[4 * q4 + e] = v4[e];
             }
             const int col = 4 * pw + g;
-            float xv = (l16 == col) ? 1.f : 0.f;
-            xv -= av[0] * row_bcast<0>(xv);
-            xv -= av[1] * row_bcast<1>(xv);
-            xv -= av[2] * row_bcast<2>(xv);
-            xv -= av[3] * row_bcast<3>(xv);
-            xv -= av[4] * row_bcast<4>(xv);
-            xv -= av[5] * row_bcast<5>(xv);
-            xv -= av[6] * row_bcast<6>(xv);
-            xv -= av[7] * row_bcast<7>(xv);
-            xv -= av[8] * row_bcast<8>(xv);
-            xv -= av[9] * row_bcast<9>(xv);
-            xv -= av[10] * row_bcast<10>(xv);
-            xv -= av[11] * row_bcast<11>(xv);
-            xv -= av[12] * row_bcast<12>(xv);
-            xv -= av[13] * row_bcast<13>(xv);
-            xv -= av[14] * row_bcast<14>(xv);
+            float xv = (l16 == col) ? 1.f : 0.f;   // av = -A
+            xv += row_bcast<0>(xv) * av[0];
+            xv += row_bcast<1>(xv) * av[1];
+            xv += row_bcast<2>(xv) * av[2];
+            xv += row_bcast<3>(xv) * av[3];
+            xv += row_bcast<4>(xv) * av[4];
+            xv += row_bcast<5>(xv) * av[5];
+            xv += row_bcast<6>(xv) * av[6];
+            xv += row_bcast<7>(xv) * av[7];
+            xv += row_bcast<8>(xv) * av[8];
+            xv += row_bcast<9>(xv) * av[9];
+            xv += row_bcast<10>(xv) * av[10];
+            xv += row_bcast<11>(xv) * av[11];
+            xv += row_bcast<12>(xv) * av[12];
+            xv += row_bcast<13>(xv) * av[13];
+            xv += row_bcast<14>(xv) * av[14];
             tt_s(wy)[col * TP + l16] = (bf16)(xv * beta_s(wy)[col]);
         }
         __syncthreads();

@@ -190,7 +190,8 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD, DEEP, DUAL>::NT)) void chunk_w
     }
 
     // Gram tiles of chunk zc, on MFMA (transposed products: acc(s, r)):
-    // A[r][s] = beta_r (Ktil_r . Khat_s), strictly lower (Kn = -Ktil), or
+    // A[r][s] = beta_r (Ktil_r . Khat_s), strictly lower and stored negated
+    // (Kn = -Ktil; the solve then adds, one fused DPP multiply-add a step), or
     // P[r][s] = Qtil_r . Khat_s for s <= r.  Without DEEP, state waves 0 (A)
     // and 1 (P) form whole tiles (nk = 128 key channels from k0 = 0).  With
     // DEEP a tile is summed over two iterations by one state wave, half of
@@ -210,7 +211,7 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD, DEEP, DUAL>::NT)) void chunk_w
             const float br = beta_s(zc)[l16];
             floatx4 out;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) out[e] = (4 * g + e >= l16) ? 0.f : -acc[e] * br;
+            for (int e = 0; e < 4; ++e) out[e] = (4 * g + e >= l16) ? 0.f : acc[e] * br;
             *reinterpret_cast<floatx4*>(a_s(zc) + l16 * AP + 4 * g) = out;
         } else {
             bf16x4 out;
@@ -539,22 +540,23 @@ __global__ __launch_bounds__((WsCfg<NCT, NSW, PD, DEEP, DUAL>::NT)) void chunk_w
             }
             const int col = 4 * pw + g;
             float xv = (l16 == col) ? 1.f : 0.f;
-            // A[r][sc] = 0 for sc >= r, so lanes above the pivot are unchanged
-            xv -= a[0] * row_bcast<0>(xv);
-            xv -= a[1] * row_bcast<1>(xv);
-            xv -= a[2] * row_bcast<2>(xv);
-            xv -= a[3] * row_bcast<3>(xv);
-            xv -= a[4] * row_bcast<4>(xv);
-            xv -= a[5] * row_bcast<5>(xv);
-            xv -= a[6] * row_bcast<6>(xv);
-            xv -= a[7] * row_bcast<7>(xv);
-            xv -= a[8] * row_bcast<8>(xv);
-            xv -= a[9] * row_bcast<9>(xv);
-            xv -= a[10] * row_bcast<10>(xv);
-            xv -= a[11] * row_bcast<11>(xv);
-            xv -= a[12] * row_bcast<12>(xv);
-            xv -= a[13] * row_bcast<13>(xv);
-            xv -= a[14] * row_bcast<14>(xv);
+            // a = -A; A[r][sc] = 0 for sc >= r, so lanes above the pivot
+            // are unchanged
+            xv += row_bcast<0>(xv) * a[0];
+            xv += row_bcast<1>(xv) * a[1];
+            xv += row_bcast<2>(xv) * a[2];
+            xv += row_bcast<3>(xv) * a[3];
+            xv += row_bcast<4>(xv) * a[4];
+            xv += row_bcast<5>(xv) * a[5];
+            xv += row_bcast<6>(xv) * a[6];
+            xv += row_bcast<7>(xv) * a[7];
+            xv += row_bcast<8>(xv) * a[8];
+            xv += row_bcast<9>(xv) * a[9];
+            xv += row_bcast<10>(xv) * a[10];
+            xv += row_bcast<11>(xv) * a[11];
+            xv += row_bcast<12>(xv) * a[12];
+            xv += row_bcast<13>(xv) * a[13];
+            xv += row_bcast<14>(xv) * a[14];
             t_s(wc)[l16 * TP + col] = (bf16)(xv * beta_s(wc)[col]);
         }
         __syncthreads();

@@ -136,11 +136,13 @@ __device__ __forceinline__ float row_shl(float src, float fill) {
 }
 
 // Lane N of each row of 16 lanes, broadcast to the whole row (row_newbcast).
+// Every lane reads a valid source, so no "old" value is passed: the result
+// needs no copy of x in its register, and the compiler may fold the
+// broadcast into the consuming VALU instruction.
 template <int N>
 __device__ __forceinline__ float row_bcast(float x) {
     return __builtin_bit_cast(
-        float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x),
-                                           0x150 + N, 0xF, 0xF, false));
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + N, 0xF, 0xF, true));
 }
 
 // Shift with zero fill (lanes whose source is outside the row read 0); the
