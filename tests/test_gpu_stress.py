@@ -3,7 +3,7 @@ decay (mean log alpha about -2.5) the state forgets within a few tokens, so
 a kernel that mishandles the carried state can still pass them.  These
 cases use slow decay (log alpha = -5 sigmoid(N(mu, 1)), mu = -4 or -8),
 no decay at all, beta at its endpoints, one-hot keys and random h0, at fp32
-and the 1e-4 bar."""
+and the 1e-4 bar, and the bf16 path (and the backward) at the decay bound."""
 import numpy as np
 import pytest
 import torch
@@ -107,3 +107,55 @@ def test_long_slow_decay_fp32_sampled():
     ro, rh = oracle_prefill(d)
     check("o", np_(o), ro, TOL["f32"])
     check("h_T", np_(hT), rh, TOL["f32"])
+
+
+@pytest.mark.parametrize("split", [1, 2])
+def test_decay_at_bound_bf16(split):
+    """The pipelined bf16 kernel with log alpha = -5 everywhere: its bf16
+    Gram operands carry factors up to e^80 (inside bf16's range), and the
+    masked products above the diagonal must not leak into A or P."""
+    kda = need_gpu()
+    case(f"log_alpha = -5 everywhere bf16 T=200 H=2 lengths=[150, 50] split={split}")
+    d = kda_inputs.prefill_inputs(200, 2, dtype="bf16", device="cuda", seed=26, lengths=[150, 50],
+                                  h0_std=0.5)
+    d["log_alpha"].fill_(-5.0)
+    o, hT = gpu_prefill(kda, d, 16, split)
+    ro, rh = oracle_prefill(d)
+    check("o", np_(o), ro, TOL["bf16"])
+    check("h_T", np_(hT), rh, TOL["bf16"])
+
+
+@pytest.mark.parametrize("beta", [0.0, 1.0])
+def test_beta_endpoints_bf16(beta):
+    kda = need_gpu()
+    case(f"beta = {beta} bf16 T=300 H=2 slow decay")
+    d = kda_inputs.prefill_inputs(300, 2, dtype="bf16", device="cuda", seed=27,
+                                  decay_mu=-4.0, beta_const=beta, h0_std=0.5)
+    o, hT = gpu_prefill(kda, d)
+    ro, rh = oracle_prefill(d)
+    check("o", np_(o), ro, TOL["bf16"])
+    check("h_T", np_(hT), rh, TOL["bf16"])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_decay_at_bound(dtype):
+    """Gradients with log alpha = -5 everywhere: the gradient kernel divides
+    by decay factors down to e^-80 within a chunk."""
+    from oracle import backward as obwd
+    kda = need_gpu()
+    T, H, lengths = 120, 2, [70, 50]
+    case(f"backward log_alpha = -5 everywhere {dtype} T={T} H={H} lengths={lengths}")
+    d = kda_inputs.prefill_inputs(T, H, dtype=dtype, device="cuda", seed=28, lengths=lengths,
+                                  h0_std=0.1)
+    d["log_alpha"].fill_(-5.0)
+    g = torch.Generator(device="cuda").manual_seed(28)
+    do = torch.randn((T, H, 128), generator=g, device="cuda").to(d["q"].dtype)
+    dhT = torch.randn((len(lengths), H, 128, 128), generator=g, device="cuda") * 0.1
+    got = kda.kda_chunk_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], do, h0=d["h0"],
+                            cu_seqlens=d["cu_seqlens"], dhT=dhT)
+    torch.cuda.synchronize()
+    cu = d["cu_seqlens"].cpu().numpy().astype(np.int64)
+    ref = obwd.bwd(np_(d["q"]), np_(d["k"]), np_(d["v"]), np_(d["log_alpha"]), np_(d["beta"]),
+                   np_(do), dhT=np_(dhT), h0=np_(d["h0"]), cu_seqlens=cu)
+    for name, gv, r in zip(("dq", "dk", "dv", "dlog_alpha", "dbeta", "dh0"), got, ref):
+        check(name, np_(gv), r, TOL[dtype])
