@@ -9,9 +9,11 @@ resident in HBM before timing; two input sets alternate so that consecutive
 steps do not hit in the 256 MiB Infinity Cache.  The decode half of the
 metric (decode state GB/s) is measured in the same run on the batched
 decode workload (256 sequences x 96 heads, one token each, state updated in
-place) and reported under "decode".  The 16-document varlen prefill is timed
-too (under "other_workloads"; `--long` adds the 1M-token sequence), and a
-1 GiB device copy gives the measured streaming ceiling beside the 8 TB/s peak.
+place) and reported under "decode".  The other three workloads -- the tiny
+fp32 prefill, the 16-document varlen prefill and the 1M-token sequence (a
+few steps) -- are timed too, under "other_workloads", each with the CPU
+oracle's rate beside it, and a 1 GiB device copy gives the measured
+streaming ceiling beside the 8 TB/s peak.
 
 Prints ONE JSON line.  `--gpus N` with N > 1 exits: this build is single-GPU.
 """
@@ -22,12 +24,17 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "KDA prefill tokens/s @H=96,d=128 (% MFMA peak); decode state GB/s (% HBM)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA (2.5 PFLOP/s)
+FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 (vector / MFMA)
+MFMA_TARGET = 0.40             # the prefill target: >= 40% of bf16 MFMA peak
+RUN_CHUNK = 16                 # tokens per chunk of the default bf16 prefill kernel
 D = 128
 
 
@@ -207,29 +214,103 @@ def copy_bandwidth(torch, dev, stream):
     return round(gbps, 1)
 
 
-def extra_prefill(torch, kda, kda_inputs, dev, stream, cfg_id, steps, warmup):
+def mfma_fracs(T, H, ms, chunk_run=RUN_CHUNK, peak_tflops=BF16_PEAK_TFLOPS):
+    """%MFMA of a prefill taking `ms`: at the chunk length the kernel runs
+    (the flops it executes) and, labelled, at F(64) (the survey's fixed
+    yardstick, which counts more chunk-local work than a 16-token kernel
+    does)."""
+    f_run = T * H * flops_per_head_token(chunk_run)
+    f64 = T * H * flops_per_head_token(64)
+    s = ms * 1e-3 * peak_tflops * 1e12
+    return {"chunk_run": chunk_run, "mfma_frac_at_run_chunk": round(f_run / s, 4),
+            "mfma_frac_F64": round(f64 / s, 4)}
+
+
+def oracle_rate_prefill(d, heads=None, dv_block=0):
+    """The fp32 CPU oracle on a prefill workload (all heads, or the listed
+    heads of a one-sequence workload), one run, on this host's cores:
+    returns (seconds, head-tokens processed, threads)."""
+    import kda_inputs
+    import oracle
+    n = kda_inputs.to_numpy
+    names = ("q", "k", "v", "log_alpha", "beta")
+    if heads is None:
+        args = [n(d[x]) for x in names]
+        cu = None if d["cu_seqlens"] is None else d["cu_seqlens"].cpu().numpy()
+        h0 = n(d["h0"]) if d["h0"] is not None else None
+    else:
+        args = [n(d[x][:, heads].contiguous()) for x in names]
+        cu, h0 = None, None
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    oracle.fwd(*args, h0=h0, cu_seqlens=cu, precision="f32", nthreads=threads,
+               dv_block=dv_block, store_state=True)
+    dt = time.perf_counter() - t0
+    return dt, args[0].shape[0] * args[0].shape[1], threads
+
+
+def extra_prefill(torch, kda, kda_inputs, dev, stream, cfg_id, steps, warmup, cpu=True):
     """Timing line of another prefill workload (same kernel path, its default
-    configuration): tokens/s, HBM fraction and %MFMA at F(64)."""
+    configuration, or the chunk length the workload fixes): tokens/s, HBM
+    fraction, %MFMA, and the CPU oracle beside it (the whole workload, or the
+    1M-token workload's four sampled heads with the per-head rate and a
+    labelled whole-workload extrapolation)."""
+    cfg = kda_inputs.CONFIGS[cfg_id]
+    print(f"[bench] {cfg['name']}: generating inputs", file=sys.stderr, flush=True)
     d = kda_inputs.config_inputs(cfg_id, device=dev)
     T, H = d["q"].shape[0], d["q"].shape[1]
     N = 1 if d["cu_seqlens"] is None else d["cu_seqlens"].numel() - 1
     o = torch.empty_like(d["v"])
     hT = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
+    chunk = cfg.get("chunk") or 0
+    esize = d["q"].element_size()
 
     def step(i):
         kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], h0=d["h0"],
-                          cu_seqlens=d["cu_seqlens"], o=o, h_T=hT)
+                          cu_seqlens=d["cu_seqlens"], o=o, h_T=hT, chunk=chunk)
 
+    print(f"[bench] {cfg['name']}: timing", file=sys.stderr, flush=True)
     wall, ms = time_launches(step, steps, warmup, stream)
     avg = sum(ms) / len(ms)
-    nbytes = prefill_bytes(T, H, N, h0=d["h0"] is not None)
-    flops = T * H * flops_per_head_token(64)
-    out = {"workload": kda_inputs.CONFIGS[cfg_id]["name"], "T": T, "H": H, "sequences": N,
+    nbytes = prefill_bytes(T, H, N, esize=esize, h0=d["h0"] is not None)
+    out = {"workload": cfg["name"], "T": T, "H": H, "sequences": N, "dtype": cfg["dtype"],
+           "steps": steps, "warmup": warmup,
            "tokens_per_s": round(T * steps / wall, 1), "kernel_ms": round(avg, 4),
            "kernel_ms_median": round(median(ms), 4),
            "hbm_frac": round(nbytes / (avg * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
-           "mfma_frac_F64": round(flops / (avg * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4),
            "algorithmic_bytes": nbytes}
+    if cfg["dtype"] == "bf16":
+        out.update(mfma_fracs(T, H, avg))
+    else:   # fp32 operands run on the fp32 MFMA
+        out.update(mfma_fracs(T, H, avg, chunk_run=chunk or RUN_CHUNK,
+                              peak_tflops=FP32_PEAK_TFLOPS))
+        out["mfma_peak"] = "fp32 157.3 TFLOP/s"
+    if cpu:
+        print(f"[bench] {cfg['name']}: CPU oracle", file=sys.stderr, flush=True)
+        if cfg_id == 4:
+            rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([1004, 98])))
+            heads = [0, 95] + [int(x) for x in rng.choice(np.arange(1, 95), size=2,
+                                                           replace=False)]
+            secs, ht, thr = oracle_rate_prefill(d, heads=heads, dv_block=32)
+            per_head = ht / secs
+            out["cpu_oracle"] = {
+                "value": round(per_head, 1), "unit": "head-tokens/s", "cores": thr,
+                "kind": "oracle",
+                "sample": f"heads {heads} x all {T} tokens, fp32 C oracle, one run "
+                          f"{secs:.2f} s wall (value-column blocks of 32 as units)",
+                "extrapolated_tokens_per_s_all_96_heads": round(per_head / H, 2),
+                "extrapolation": "per-head rate / 96 heads, assuming the same rate per head"}
+        else:
+            runs = 3 if T * H < 100000 else 1
+            best = []
+            for _ in range(runs):
+                secs, ht, thr = oracle_rate_prefill(d)
+                best.append(secs)
+            secs = sorted(best)[len(best) // 2]
+            out["cpu_oracle"] = {
+                "value": round(T / secs, 1), "unit": "tokens/s", "cores": thr, "kind": "oracle",
+                "sample": f"whole workload (T={T}, H={H}, {N} sequences), fp32 C oracle, "
+                          f"{'median of 3 runs' if runs == 3 else 'one run'} {secs:.3f} s wall"}
     del d, o, hT
     torch.cuda.empty_cache()
     return out
@@ -425,6 +506,38 @@ def backward(torch, kda, kda_inputs, dev, stream, steps, warmup, fwd_ms):
     return out
 
 
+def decode_section(torch, kda, kda_inputs, dev, stream, steps, warmup, H=96):
+    """The batched decode workload: 256 x 96 fp32 states, one bf16 token
+    each, the state updated in place (the decode half of the metric)."""
+    B = 256
+    dd = kda_inputs.decode_inputs(B, H, dtype="bf16", device=dev, seed=1002)
+    od = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
+
+    def dstep(i):
+        kda.kda_decode_step(dd["q"], dd["k"], dd["v"], dd["log_alpha"], dd["beta"],
+                            dd["S"], o=od)
+
+    _, dms = time_launches(dstep, steps, warmup, stream)
+    davg = sum(dms) / len(dms)
+    state_bytes = B * H * D * D * 4 * 2
+    total_bytes = B * H * (D * D * 4 * 2 + 2 * (4 * D + 1 + D))
+    del dd
+    torch.cuda.empty_cache()
+    return {
+        "workload": "kda_decode_B256_H96_d128_bf16", "steps": steps, "warmup": warmup,
+        "state_GBps": round(state_bytes / (davg * 1e-3) / 1e9, 1),
+        "total_GBps": round(total_bytes / (davg * 1e-3) / 1e9, 1),
+        "ms_per_step": round(davg, 5),
+        "roofline": {"bound": "hbm",
+                     "achieved": round(total_bytes / (davg * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(total_bytes / (davg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": read_traffic("decode_B256_H96_bf16", kernel_source_hash()),
+                     "kernel": "kda::decode_kernel",
+                     "kernel_ms_median": round(median(dms), 5)},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -438,11 +551,14 @@ def main():
                     help="also run a plain 1 GiB device copy three times, as the "
                          "reference kernel for scaling HBM byte counters")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the 16-document varlen prefill line")
-    ap.add_argument("--long", action="store_true",
-                    help="also time the 1M-token single-sequence prefill (129 GB of HBM)")
+                    help="skip everything but the headline prefill and decode lines")
+    ap.add_argument("--skip-long", action="store_true",
+                    help="skip the 1M-token single-sequence prefill (129 GB of HBM)")
+    ap.add_argument("--long-steps", type=int, default=3,
+                    help="timed steps of the 1M-token prefill (one untimed step first)")
     ap.add_argument("--section", default=None,
-                    choices=["backward", "layer", "context_parallel", "verify_replay"],
+                    choices=["prefill", "long", "varlen", "tiny", "decode", "backward", "layer",
+                             "context_parallel", "verify_replay"],
                     help="time only this section (one JSON object), e.g. under a profiler")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -461,9 +577,38 @@ def main():
         from gated_delta_rule_27_amd import build
         build.build()
     dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    T, H, N = 4096, 96, 1
+
+    def headline_inputs():
+        return [kda_inputs.prefill_inputs(T, H, dtype="bf16", device=dev, seed=s)
+                for s in (1001, 1101)]
+
     if args.section:
-        stream = torch.cuda.current_stream(dev)
-        if args.section == "backward":
+        if args.section == "prefill":
+            sets = headline_inputs()
+            o = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+
+            def pstep(i):
+                d = sets[i % 2]
+                kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"],
+                                  chunk=args.chunk, dv_split=args.split, o=o, store_state=True)
+
+            _, ms = time_launches(pstep, args.steps, args.warmup, stream)
+            avg = sum(ms) / len(ms)
+            res = {"workload": "kda_prefill_T4096_H96_d128_bf16", "kernel_ms": round(avg, 5),
+                   "hbm_frac": round(prefill_bytes(T, H, N) / (avg * 1e-3)
+                                     / (HBM_PEAK_GBS * 1e9), 4)}
+            res.update(mfma_fracs(T, H, avg))
+        elif args.section in ("long", "varlen", "tiny"):
+            cid = {"tiny": 0, "varlen": 3, "long": 4}[args.section]
+            st = args.long_steps if cid == 4 else args.steps
+            res = extra_prefill(torch, kda, kda_inputs, dev, stream, cid, st,
+                                1 if cid == 4 else args.warmup, cpu=False)
+        elif args.section == "decode":
+            res = decode_section(torch, kda, kda_inputs, dev, stream, args.steps, args.warmup)
+        elif args.section == "backward":
             res = backward(torch, kda, kda_inputs, dev, stream, args.steps, args.warmup, 1.0)
             res.pop("vs_forward")
         elif args.section == "layer":
@@ -473,15 +618,18 @@ def main():
             res = context_parallel(torch, kda, kda_inputs, dev, stream, args.steps, args.warmup)
         else:
             res = verify_replay(torch, kda, kda_inputs, dev, stream, args.steps, args.warmup)
-        print(json.dumps({"section": args.section, **res}), flush=True)
+        print(json.dumps({"section": args.section, "kernel_source_hash": kernel_source_hash(),
+                          **res}), flush=True)
         return
-    torch.cuda.set_device(dev)
-    stream = torch.cuda.current_stream(dev)
+
+    # Decode is timed first: it is half of the metric, and it also brings the
+    # GPU to its working clocks before the prefill's own warm-up steps.
+    sets = headline_inputs()
+    decode_out = None
+    if not args.no_decode:
+        decode_out = decode_section(torch, kda, kda_inputs, dev, stream, args.steps, args.warmup)
 
     # ---------------- prefill: T=4096, H=96, bf16 ----------------
-    T, H, N = 4096, 96, 1
-    sets = [kda_inputs.prefill_inputs(T, H, dtype="bf16", device=dev, seed=s)
-            for s in (1001, 1101)]
     o = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
     hT = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
 
@@ -498,8 +646,7 @@ def main():
     achieved = nbytes / (avg_ms * 1e-3) / 1e9
     src_hash = kernel_source_hash()
     traffic = read_traffic("chunk_fwd_T4096_H96_bf16", src_hash)
-    flops = T * H * flops_per_head_token(64)
-    mfma_frac = flops / (avg_ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)
+    fr = mfma_fracs(T, H, avg_ms, chunk_run=args.chunk or RUN_CHUNK)
 
     out = {
         "metric": METRIC,
@@ -522,10 +669,19 @@ def main():
                      "traffic": traffic, "kernel": "kda::chunk_ws_kernel",
                      "kernel_ms": round(avg_ms, 5), "kernel_ms_median": round(median(ms), 5),
                      "algorithmic_bytes": nbytes},
-        "mfma": {"flops_per_step": flops, "counted_at_chunk": 64,
-                 "frac_of_bf16_peak": round(mfma_frac, 4)},
+        "mfma": {"chunk_run": fr["chunk_run"],
+                 "flops_per_step_at_run_chunk": T * H * flops_per_head_token(fr["chunk_run"]),
+                 "frac_of_bf16_peak": fr["mfma_frac_at_run_chunk"],
+                 "flops_per_step_F64": T * H * flops_per_head_token(64),
+                 "frac_of_bf16_peak_F64": fr["mfma_frac_F64"],
+                 "target_frac": MFMA_TARGET,
+                 "gap_to_target": round(MFMA_TARGET - fr["mfma_frac_at_run_chunk"], 4),
+                 "note": "HBM-bound: at the HBM roofline %MFMA would be ~0.27 at the run chunk "
+                         "(0.35 at F(64)), below the 0.40 target"},
         "kernel_source_hash": src_hash,
     }
+    if decode_out is not None:
+        out["decode"] = decode_out
     # ---------------- prefix snapshots every 512 tokens (same workload) ----------------
     if not args.no_extra:
         snap_cu, n_snap = kda.snapshot_index(None, T, 512)
@@ -545,43 +701,13 @@ def main():
                             "algorithmic_bytes": sbytes,
                             "hbm_frac": round(sbytes / (savg * 1e-3) / (HBM_PEAK_GBS * 1e9), 4)}
         del snap
-    del sets
+    del sets, o, hT
     torch.cuda.empty_cache()
 
     # ---------------- speculative verify + replay, 256 requests ----------------
     if not args.no_extra and not args.no_decode:
         out["verify_replay"] = verify_replay(torch, kda, kda_inputs, dev, stream, args.steps,
                                              args.warmup)
-
-    # ---------------- decode: 256 x 96 states, one token ----------------
-    if not args.no_decode:
-        B = 256
-        dd = kda_inputs.decode_inputs(B, H, dtype="bf16", device=dev, seed=1002)
-        od = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
-
-        def dstep(i):
-            kda.kda_decode_step(dd["q"], dd["k"], dd["v"], dd["log_alpha"], dd["beta"],
-                                dd["S"], o=od)
-
-        dwall, dms = time_launches(dstep, args.steps, args.warmup, stream)
-        davg = sum(dms) / len(dms)
-        state_bytes = B * H * D * D * 4 * 2
-        total_bytes = B * H * (D * D * 4 * 2 + 2 * (4 * D + 1 + D))
-        out["decode"] = {
-            "workload": "kda_decode_B256_H96_d128_bf16",
-            "state_GBps": round(state_bytes / (davg * 1e-3) / 1e9, 1),
-            "total_GBps": round(total_bytes / (davg * 1e-3) / 1e9, 1),
-            "ms_per_step": round(davg, 5),
-            "roofline": {"bound": "hbm",
-                         "achieved": round(total_bytes / (davg * 1e-3) / 1e9, 1),
-                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(total_bytes / (davg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                         "traffic": read_traffic("decode_B256_H96_bf16", src_hash),
-                         "kernel": "kda::decode_kernel",
-                         "kernel_ms_median": round(median(dms), 5)},
-        }
-        del dd
-        torch.cuda.empty_cache()
 
     if not args.no_extra:
         out["backward"] = backward(torch, kda, kda_inputs, dev, stream, args.steps, args.warmup,
@@ -603,15 +729,18 @@ def main():
         out["decode"]["roofline"]["frac_of_copy"] = round(
             out["decode"]["roofline"]["achieved"] / cbw, 4)
 
-    extra = []
+    # every other workload, each with the CPU oracle beside it
+    cpu = not args.no_cpu_baseline
     if not args.no_extra:
-        extra.append(extra_prefill(torch, kda, kda_inputs, dev, stream, 3, args.steps, args.warmup))
-    if args.long:
-        extra.append(extra_prefill(torch, kda, kda_inputs, dev, stream, 4, 3, 1))
-    if not args.no_extra:
+        extra = [extra_prefill(torch, kda, kda_inputs, dev, stream, 0, args.steps, args.warmup,
+                               cpu=cpu),
+                 extra_prefill(torch, kda, kda_inputs, dev, stream, 3, args.steps, args.warmup,
+                               cpu=cpu)]
         out["context_parallel"] = context_parallel(torch, kda, kda_inputs, dev, stream,
                                                    min(args.steps, 5), 1)
-    if extra:
+        if not args.skip_long:
+            extra.append(extra_prefill(torch, kda, kda_inputs, dev, stream, 4,
+                                       args.long_steps, 1, cpu=cpu))
         out["other_workloads"] = extra
 
     if args.copy_calibration:
@@ -623,7 +752,7 @@ def main():
         out["copy_calibration_bytes"] = {"read": src.numel() * 4, "write": dst.numel() * 4}
         del src, dst
 
-    if not args.no_cpu_baseline:
+    if cpu:
         out["cpu_baseline"] = cpu_baseline(T, H)
         # the oracle beside the other rows, on bounded samples
         if "decode" in out:

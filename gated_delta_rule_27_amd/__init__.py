@@ -145,6 +145,30 @@ def _dev(t, name, dtype=None):
     return t
 
 
+def _tensors(**named):
+    """Every argument given must be a torch.Tensor (None = not given)."""
+    torch = _torch()
+    for name, t in named.items():
+        if t is not None and not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+
+
+def _shape(t, name, shape):
+    """Shape check of a caller-supplied tensor (None = not given).  The C ABI
+    receives bare pointers, so a buffer that is too small would be written
+    past its end: every output and optional input is checked here, before
+    any device work."""
+    shape = tuple(int(x) for x in shape)
+    if t is not None and tuple(t.shape) != shape:
+        raise ValueError(f"{name} must have shape {shape} (got {tuple(t.shape)})")
+
+
+def _same_device(dev, **named):
+    for name, t in named.items():
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} must be on {dev} like q (got {t.device})")
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -152,6 +176,38 @@ def _ptr(t):
 def _stream(device):
     torch = _torch()
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _prefill_shapes(q, k, v, log_alpha, beta, h0, cu_seqlens, need_v=True):
+    """Shape checks shared by the prefill-family calls; returns (T, H, Dk,
+    Dv, N)."""
+    _tensors(q=q, k=k, v=v, log_alpha=log_alpha, beta=beta, h0=h0, cu_seqlens=cu_seqlens)
+    if q is None or k is None or log_alpha is None or beta is None or (need_v and v is None):
+        raise TypeError("q, k, log_alpha, beta (and v) are required tensors")
+    if q.dim() != 3:
+        raise ValueError("q must be [T, H, D]")
+    T, H, Dk = q.shape
+    Dv = v.shape[-1] if v is not None else Dk
+    if k.shape != q.shape or log_alpha.shape != q.shape or tuple(beta.shape) != (T, H) \
+            or (v is not None and (v.dim() != 3 or tuple(v.shape[:2]) != (T, H))):
+        raise ValueError("inconsistent shapes")
+    N = 1
+    if cu_seqlens is not None:
+        if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+            raise ValueError("cu_seqlens must be [N + 1] with N >= 1")
+        N = cu_seqlens.numel() - 1
+    _shape(h0, "h0", (N, H, Dk, Dv))
+    return T, H, Dk, Dv, N
+
+
+def _prefill_devices(q, k, v, log_alpha, beta, h0, cu_seqlens):
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("beta", beta)):
+        _dev(t, name, q.dtype)
+    _dev(cu_seqlens, "cu_seqlens", torch.int32)
+    _dev(h0, "h0", torch.float32)
+    _same_device(q.device, k=k, v=v, log_alpha=log_alpha, beta=beta, h0=h0,
+                 cu_seqlens=cu_seqlens)
 
 
 def kda_chunk_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, chunk=0,
@@ -166,32 +222,21 @@ def kda_chunk_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, chunk=0
     library's tuning choice (0 = automatic).
     """
     torch = _torch()
-    for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("beta", beta)):
-        _dev(t, name, q.dtype)
+    T, H, Dk, Dv, N = _prefill_shapes(q, k, v, log_alpha, beta, h0, cu_seqlens)
+    _tensors(o=o, h_T=h_T)
+    _shape(o, "o", (T, H, Dv))
+    _shape(h_T, "h_T", (N, H, Dk, Dv))
+    _prefill_devices(q, k, v, log_alpha, beta, h0, cu_seqlens)
+    _dev(o, "o", q.dtype)
+    _dev(h_T, "h_T", torch.float32)
+    _same_device(q.device, o=o, h_T=h_T)
     dt = _dtype_code(q)
-    if q.dim() != 3:
-        raise ValueError("q must be [T, H, D]")
-    T, H, Dk = q.shape
-    Dv = v.shape[-1]
-    if k.shape != q.shape or log_alpha.shape != q.shape or v.shape[:2] != (T, H) \
-            or tuple(beta.shape) != (T, H):
-        raise ValueError("inconsistent shapes")
-    if cu_seqlens is not None:
-        _dev(cu_seqlens, "cu_seqlens", torch.int32)
-        N = cu_seqlens.numel() - 1
-    else:
-        N = 1
-    _dev(h0, "h0", torch.float32)
-    if h0 is not None and tuple(h0.shape) != (N, H, Dk, Dv):
-        raise ValueError("h0 must be [N, H, Dk, Dv]")
     if o is None:
         o = torch.empty((T, H, Dv), dtype=q.dtype, device=q.device)
-    _dev(o, "o", q.dtype)
     if store_state and h_T is None:
         h_T = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device)
     if not store_state:
         h_T = None
-    _dev(h_T, "h_T", torch.float32)
     ws_bytes = kda_chunk_fwd_workspace_size(T, N, H, Dk, Dv, dt)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
     _check(lib().kda_chunk_fwd_ex(
@@ -229,35 +274,36 @@ def kda_chunk_fwd_snap(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, in
     [n_snap, H, 128, 128] fp32, laid out as snapshot_index describes.
     Returns (o, h_T, snap, snap_cu)."""
     torch = _torch()
-    for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("beta", beta)):
-        _dev(t, name, q.dtype)
+    T, H, Dk, Dv, N = _prefill_shapes(q, k, v, log_alpha, beta, h0, cu_seqlens)
+    _tensors(o=o, h_T=h_T, snap=snap, snap_cu=snap_cu)
+    _shape(o, "o", (T, H, Dv))
+    _shape(h_T, "h_T", (N, H, Dk, Dv))
+    if (snap_cu is None) != (n_snap is None) and N > 1:
+        raise ValueError("give snap_cu and n_snap together (snapshot_index computes both)")
+    if n_snap is not None:
+        n_snap = int(n_snap)
+        if n_snap < 0:
+            raise ValueError("n_snap must be >= 0")
+        _shape(snap_cu, "snap_cu", (N + 1,))
+        _shape(snap, "snap", (n_snap, H, Dk, Dv))
+    _prefill_devices(q, k, v, log_alpha, beta, h0, cu_seqlens)
+    _dev(o, "o", q.dtype)
+    _dev(h_T, "h_T", torch.float32)
+    _dev(snap, "snap", torch.float32)
+    _dev(snap_cu, "snap_cu", torch.int32)
+    _same_device(q.device, o=o, h_T=h_T, snap=snap, snap_cu=snap_cu)
     dt = _dtype_code(q)
-    T, H, Dk = q.shape
-    Dv = v.shape[-1]
-    if k.shape != q.shape or log_alpha.shape != q.shape or v.shape[:2] != (T, H) \
-            or tuple(beta.shape) != (T, H):
-        raise ValueError("inconsistent shapes")
-    N = 1
-    if cu_seqlens is not None:
-        _dev(cu_seqlens, "cu_seqlens", torch.int32)
-        N = cu_seqlens.numel() - 1
-    _dev(h0, "h0", torch.float32)
-    if h0 is not None and tuple(h0.shape) != (N, H, Dk, Dv):
-        raise ValueError("h0 must be [N, H, Dk, Dv]")
     if n_snap is None:
         snap_cu, n_snap = snapshot_index(cu_seqlens, T, interval)
-    _dev(snap_cu, "snap_cu", torch.int32)
+        _shape(snap, "snap", (n_snap, H, Dk, Dv))
     if snap is None:
         snap = torch.empty((n_snap, H, Dk, Dv), dtype=torch.float32, device=q.device)
-    _dev(snap, "snap", torch.float32)
     if o is None:
         o = torch.empty((T, H, Dv), dtype=q.dtype, device=q.device)
-    _dev(o, "o", q.dtype)
     if store_state and h_T is None:
         h_T = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device)
     if not store_state:
         h_T = None
-    _dev(h_T, "h_T", torch.float32)
     ws_bytes = kda_chunk_fwd_workspace_size(T, N, H, Dk, Dv, dt)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
     _check(lib().kda_chunk_fwd_snap(
@@ -272,18 +318,24 @@ def kda_decode_step(q, k, v, log_alpha, beta, S, *, o=None):
     updated in place.  q, k, log_alpha, v: [B, H, 128]; beta: [B, H].
     Returns o [B, H, 128] in the input dtype."""
     torch = _torch()
+    _tensors(q=q, k=k, v=v, log_alpha=log_alpha, beta=beta, S=S, o=o)
+    if q.dim() != 3:
+        raise ValueError("q must be [B, H, D]")
+    B, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if k.shape != q.shape or log_alpha.shape != q.shape or v.dim() != 3 \
+            or tuple(v.shape[:2]) != (B, H) or tuple(beta.shape) != (B, H):
+        raise ValueError("inconsistent shapes")
+    _shape(S, "S", (B, H, Dk, Dv))
+    _shape(o, "o", (B, H, Dv))
     for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("beta", beta)):
         _dev(t, name, q.dtype)
     _dev(S, "S", torch.float32)
+    _dev(o, "o", q.dtype)
+    _same_device(q.device, k=k, v=v, log_alpha=log_alpha, beta=beta, S=S, o=o)
     dt = _dtype_code(q)
-    B, H, Dk = q.shape
-    Dv = v.shape[-1]
-    if k.shape != q.shape or log_alpha.shape != q.shape or v.shape[:2] != (B, H) \
-            or tuple(beta.shape) != (B, H) or tuple(S.shape) != (B, H, Dk, Dv):
-        raise ValueError("inconsistent shapes")
     if o is None:
         o = torch.empty((B, H, Dv), dtype=q.dtype, device=q.device)
-    _dev(o, "o", q.dtype)
     _check(lib().kda_decode_step(
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S), B, H, Dk, Dv, dt,
         _ptr(o), _stream(q.device)))
@@ -296,16 +348,14 @@ def kda_segment_summary(q, k, v, log_alpha, beta, cu_seqlens=None, *, want_M=Tru
     cu_seqlens (packed as for kda_chunk_fwd).  Returns (M, B), each
     [N, H, 128, 128] fp32 or None when not asked for."""
     torch = _torch()
-    for name, t in (("q", q), ("k", k), ("log_alpha", log_alpha), ("beta", beta)):
-        _dev(t, name, q.dtype)
-    if want_B:
-        _dev(v, "v", q.dtype)
+    if not want_B:
+        v = None
+    T, H, Dk, _, N = _prefill_shapes(q, k, v, log_alpha, beta, None, cu_seqlens,
+                                     need_v=want_B)
+    if v is not None and v.shape[-1] != Dk:
+        raise ValueError("v must be [T, H, 128]")
+    _prefill_devices(q, k, v, log_alpha, beta, None, cu_seqlens)
     dt = _dtype_code(q)
-    T, H, Dk = q.shape
-    N = 1
-    if cu_seqlens is not None:
-        _dev(cu_seqlens, "cu_seqlens", torch.int32)
-        N = cu_seqlens.numel() - 1
     M = torch.empty((N, H, Dk, Dk), dtype=torch.float32, device=q.device) if want_M else None
     B = torch.empty((N, H, Dk, Dk), dtype=torch.float32, device=q.device) if want_B else None
     ws_bytes = kda_chunk_fwd_workspace_size(T, N, H, Dk, Dk, dt)
@@ -322,14 +372,19 @@ def kda_segment_scan(M, B, h0=None):
     [H, 128, 128] or [1, H, 128, 128].  Returns (S_in [R, H, 128, 128],
     S_final [H, 128, 128])."""
     torch = _torch()
+    _tensors(M=M, B=B, h0=h0)
+    if M.dim() != 4:
+        raise ValueError("M must be [R, H, 128, 128]")
+    R, H, Dk, Dv = M.shape
+    _shape(B, "B", (R, H, Dk, Dv))
+    if h0 is not None:
+        if h0.numel() != H * Dk * Dv:
+            raise ValueError(f"h0 must be [H, Dk, Dv] or [1, H, Dk, Dv] (got {tuple(h0.shape)})")
+        h0 = h0.reshape(H, Dk, Dv)
     _dev(M, "M", torch.float32)
     _dev(B, "B", torch.float32)
-    R, H, Dk, Dv = M.shape
-    if tuple(B.shape) != (R, H, Dk, Dv):
-        raise ValueError("M and B must have the same shape")
-    if h0 is not None:
-        h0 = h0.reshape(H, Dk, Dv)
     _dev(h0, "h0", torch.float32)
+    _same_device(M.device, B=B, h0=h0)
     S_in = torch.empty_like(M)
     S_final = torch.empty((H, Dk, Dv), dtype=torch.float32, device=M.device)
     _check(lib().kda_segment_scan(_ptr(M), _ptr(B), _ptr(h0), R, H, Dk, Dv, _ptr(S_in),
@@ -350,18 +405,16 @@ def kda_chunk_bwd(q, k, v, log_alpha, beta, do, h0=None, cu_seqlens=None, dhT=No
     [N, H, 128, 128] fp32 or None.  Returns (dq, dk, dv, dlog_alpha, dbeta,
     dh0 or None); token gradients in the input dtype, dh0 fp32."""
     torch = _torch()
-    for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("beta", beta),
-                    ("do", do)):
-        _dev(t, name, q.dtype)
-    dt = _dtype_code(q)
-    T, H, Dk = q.shape
-    Dv = v.shape[2]
-    N = 1
-    if cu_seqlens is not None:
-        _dev(cu_seqlens, "cu_seqlens", torch.int32)
-        N = cu_seqlens.numel() - 1
-    _dev(h0, "h0", torch.float32)
+    T, H, Dk, Dv, N = _prefill_shapes(q, k, v, log_alpha, beta, h0, cu_seqlens)
+    _tensors(do=do, dhT=dhT, workspace=workspace)
+    _shape(do, "do", (T, H, Dv))
+    _shape(dhT, "dhT", (N, H, Dk, Dv))
+    _prefill_devices(q, k, v, log_alpha, beta, h0, cu_seqlens)
+    _dev(do, "do", q.dtype)
     _dev(dhT, "dhT", torch.float32)
+    _dev(workspace, "workspace")
+    _same_device(q.device, do=do, dhT=dhT, workspace=workspace)
+    dt = _dtype_code(q)
     dq, dk, dv, dg = (torch.empty_like(x) for x in (q, k, v, log_alpha))
     db = torch.empty_like(beta)
     dh0 = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device) if want_dh0 else None
@@ -371,7 +424,8 @@ def kda_chunk_bwd(q, k, v, log_alpha, beta, do, h0=None, cu_seqlens=None, dhT=No
     _check(lib().kda_chunk_bwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0), _ptr(cu_seqlens), N,
         T, H, Dk, Dv, dt, _ptr(do), _ptr(dhT), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(db),
-        _ptr(dh0), _ptr(workspace), workspace.numel(), _stream(q.device)))
+        _ptr(dh0), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(q.device)))
     return dq, dk, dv, dg, db, dh0
 
 
@@ -386,25 +440,41 @@ def kda_prologue(xq, xk, xv, a_raw, b_raw, conv_w, a_bias, cu_seqlens=None, conv
     [N, 3, 3, H, 128] in the input dtype or None (zero history).  Returns
     (q, k, v, log_alpha, beta, conv_state_out or None)."""
     torch = _torch()
+    _tensors(xq=xq, xk=xk, xv=xv, a_raw=a_raw, b_raw=b_raw, conv_w=conv_w, a_bias=a_bias,
+             cu_seqlens=cu_seqlens, conv_state=conv_state, state_out=state_out)
+    if xq.dim() != 3:
+        raise ValueError("xq must be [T, H, D]")
     dt_t = xq.dtype
+    T, H, D = xq.shape
+    for name, t in (("xk", xk), ("xv", xv), ("a_raw", a_raw)):
+        _shape(t, name, (T, H, D))
+    _shape(b_raw, "b_raw", (T, H))
+    _shape(conv_w, "conv_w", (3, H, D, 4))
+    _shape(a_bias, "a_bias", (H, D))
+    N = 1
+    if cu_seqlens is not None:
+        if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+            raise ValueError("cu_seqlens must be [N + 1] with N >= 1")
+        N = cu_seqlens.numel() - 1
+    _shape(conv_state, "conv_state", (N, 3, 3, H, D))
+    _shape(state_out, "state_out", (N, 3, 3, H, D))
     for name, t in (("xq", xq), ("xk", xk), ("xv", xv), ("a_raw", a_raw), ("b_raw", b_raw)):
         _dev(t, name, dt_t)
     _dev(conv_w, "conv_w", torch.float32)
     _dev(a_bias, "a_bias", torch.float32)
-    dt = _dtype_code(xq)
-    T, H, D = xq.shape
-    N = 1
-    if cu_seqlens is not None:
-        _dev(cu_seqlens, "cu_seqlens", torch.int32)
-        N = cu_seqlens.numel() - 1
+    _dev(cu_seqlens, "cu_seqlens", torch.int32)
     _dev(conv_state, "conv_state", dt_t)
+    _dev(state_out, "state_out", dt_t)
+    _same_device(xq.device, xk=xk, xv=xv, a_raw=a_raw, b_raw=b_raw, conv_w=conv_w,
+                 a_bias=a_bias, cu_seqlens=cu_seqlens, conv_state=conv_state,
+                 state_out=state_out)
+    dt = _dtype_code(xq)
     q, k, v, la = (torch.empty_like(xq) for _ in range(4))
     beta = torch.empty_like(b_raw)
     so = None
     if store_state:
         so = state_out if state_out is not None else torch.empty(
             (N, 3, 3, H, D), dtype=dt_t, device=xq.device)
-        _dev(so, "state_out", dt_t)
     _check(lib().kda_prologue(
         _ptr(xq), _ptr(xk), _ptr(xv), _ptr(a_raw), _ptr(b_raw), _ptr(conv_w), _ptr(a_bias),
         _ptr(cu_seqlens), N, T, H, D, dt, _ptr(conv_state), _ptr(so), float(l2_eps), _ptr(q),
@@ -416,13 +486,20 @@ def kda_epilogue(o, g, norm_w, *, eps=1e-5, y=None):
     """y = RMSNorm_head(o) * norm_w * sigmoid(g).  o, g: [T, H, 128]
     (bf16 or fp32); norm_w: [H, 128] fp32.  y may be o or g (in place)."""
     torch = _torch()
+    _tensors(o=o, g=g, norm_w=norm_w, y=y)
+    if o.dim() != 3:
+        raise ValueError("o must be [T, H, D]")
+    T, H, D = o.shape
+    _shape(g, "g", (T, H, D))
+    _shape(norm_w, "norm_w", (H, D))
+    _shape(y, "y", (T, H, D))
     _dev(o, "o", o.dtype)
     _dev(g, "g", o.dtype)
     _dev(norm_w, "norm_w", torch.float32)
-    T, H, D = o.shape
+    _dev(y, "y", o.dtype)
+    _same_device(o.device, g=g, norm_w=norm_w, y=y)
     if y is None:
         y = torch.empty_like(o)
-    _dev(y, "y", o.dtype)
     _check(lib().kda_epilogue(_ptr(o), _ptr(g), _ptr(norm_w), T, H, D, _dtype_code(o),
                               float(eps), _ptr(y), _stream(o.device)))
     return y
@@ -435,23 +512,26 @@ def kda_decode_multi(q, k, v, log_alpha, beta, S, n_tok=None, *, update_state=Tr
     int32 [B] device (tokens applied per sequence, clamped to [0, K]) or
     None (all K).  Returns o [B, K, H, 128] (rows past n_tok[b] untouched)."""
     torch = _torch()
-    for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("beta", beta)):
-        _dev(t, name, q.dtype)
-    _dev(S, "S", torch.float32)
-    _dev(n_tok, "n_tok", torch.int32)
-    dt = _dtype_code(q)
+    _tensors(q=q, k=k, v=v, log_alpha=log_alpha, beta=beta, S=S, n_tok=n_tok, o=o)
     if q.dim() != 4:
         raise ValueError("q must be [B, K, H, D]")
     B, K, H, Dk = q.shape
     Dv = v.shape[-1]
-    if k.shape != q.shape or log_alpha.shape != q.shape or v.shape[:3] != (B, K, H) \
-            or tuple(beta.shape) != (B, K, H) or tuple(S.shape) != (B, H, Dk, Dv):
+    if k.shape != q.shape or log_alpha.shape != q.shape or v.dim() != 4 \
+            or tuple(v.shape[:3]) != (B, K, H) or tuple(beta.shape) != (B, K, H):
         raise ValueError("inconsistent shapes")
-    if n_tok is not None and tuple(n_tok.shape) != (B,):
-        raise ValueError("n_tok must be [B]")
+    _shape(S, "S", (B, H, Dk, Dv))
+    _shape(n_tok, "n_tok", (B,))
+    _shape(o, "o", (B, K, H, Dv))
+    for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("beta", beta)):
+        _dev(t, name, q.dtype)
+    _dev(S, "S", torch.float32)
+    _dev(n_tok, "n_tok", torch.int32)
+    _dev(o, "o", q.dtype)
+    _same_device(q.device, k=k, v=v, log_alpha=log_alpha, beta=beta, S=S, n_tok=n_tok, o=o)
+    dt = _dtype_code(q)
     if o is None:
         o = torch.empty((B, K, H, Dv), dtype=q.dtype, device=q.device)
-    _dev(o, "o", q.dtype)
     _check(lib().kda_decode_multi(
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S), _ptr(n_tok),
         B, K, H, Dk, Dv, dt, 1 if update_state else 0, _ptr(o), _stream(q.device)))

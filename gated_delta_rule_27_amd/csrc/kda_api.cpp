@@ -134,12 +134,12 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
     const Span sq = span(q, nTok * es), sk = span(k, nTok * es), sv = span(v, nTok * es),
                sg = span(log_alpha, nTok * es), sb = span(beta, (uint64_t)T_total * H * es),
                sh0 = span(h0, h0 ? nState * 4 : 0),
-               scu = span(cu_seqlens, cu_seqlens ? (uint64_t)(N + 1) * 4 : 0),
+               scu = span(cu_seqlens, cu_seqlens ? ((uint64_t)N + 1) * 4 : 0),
                so = span(o, nTok * es), shT = span(h_T, h_T ? nState * 4 : 0),
                sws = span(workspace, workspace_bytes);
     const uint64_t snap_es = (flags & kda::kChunkSnapBf16) ? 2 : 4;
     const Span ssn = span(sr.snap, sr.snap ? (uint64_t)sr.n_snap * (nState / N) * snap_es : 0),
-               sscu = span(sr.snap_cu, sr.snap_cu ? (uint64_t)(N + 1) * 4 : 0);
+               sscu = span(sr.snap_cu, sr.snap_cu ? ((uint64_t)N + 1) * 4 : 0);
     if (overlaps_any(so, {sq, sk, sv, sg, sb, sh0, scu, sws, sscu})) return KDA_ERR_ALIAS;
     if (overlaps_any(shT, {sq, sk, sv, sg, sb, sh0, scu, so, sws, sscu})) return KDA_ERR_ALIAS;
     if (overlaps_any(ssn, {sq, sk, sv, sg, sb, sh0, scu, so, shT, sws, sscu}))
@@ -228,7 +228,8 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const vo
                            const void* beta, float* S, int32_t B, int32_t H, int32_t Dk,
                            int32_t Dv, kda_dtype dt, void* o, hipStream_t stream) {
     if (!valid_dtype(dt)) return KDA_ERR_BAD_DTYPE;
-    if (B < 0 || H < 1 || Dk != kda::kHeadDim || Dv != kda::kHeadDim) return KDA_ERR_BAD_SHAPE;
+    if (B < 0 || H < 1 || H > KDA_MAX_HEADS || Dk != kda::kHeadDim || Dv != kda::kHeadDim)
+        return KDA_ERR_BAD_SHAPE;
     if ((uint64_t)B * (uint64_t)H > (uint64_t)std::numeric_limits<int32_t>::max())
         return KDA_ERR_BAD_SHAPE;
     if (B > 0 && (!q || !k || !v || !log_alpha || !beta || !S || !o)) return KDA_ERR_NULL_ARG;
@@ -382,12 +383,20 @@ size_t kda_chunk_bwd_workspace_size(int64_t T_total, int32_t N, int32_t H, int32
            kda::kHeadDim * esize(dt);
 }
 
-kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void* log_alpha,
-                         const void* beta, const float* h0, const int32_t* cu_seqlens,
-                         int32_t N, int64_t T_total, int32_t H, int32_t Dk, int32_t Dv,
-                         kda_dtype dt, const void* dout, const float* dhT, void* dq, void* dk,
-                         void* dv, void* dlog_alpha, void* dbeta, float* dh0, void* workspace,
-                         size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// kda_chunk_bwd's validation and launches.  no_workspace: validate every
+// argument except the workspace (which the caller supplies afterwards);
+// check_only: return after validation, before any HIP call.
+kda_status chunk_bwd_impl(const void* q, const void* k, const void* v, const void* log_alpha,
+                          const void* beta, const float* h0, const int32_t* cu_seqlens,
+                          int32_t N, int64_t T_total, int32_t H, int32_t Dk, int32_t Dv,
+                          kda_dtype dt, const void* dout, const float* dhT, void* dq, void* dk,
+                          void* dv, void* dlog_alpha, void* dbeta, float* dh0, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream, bool check_only,
+                          bool no_workspace) {
     if (!valid_dtype(dt)) return KDA_ERR_BAD_DTYPE;
     if (N < 1 || T_total < 0 || H < 1 || H > KDA_MAX_HEADS || Dk != kda::kHeadDim ||
         Dv != kda::kHeadDim)
@@ -407,9 +416,11 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void
         if (p && !aligned(p, 16)) return KDA_ERR_MISALIGNED;
     if (dbeta && !aligned(dbeta, esize(dt))) return KDA_ERR_MISALIGNED;
     const size_t need = kda_chunk_bwd_workspace_size(T_total, N, H, Dk, Dv, dt);
-    if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE;
+    if (!no_workspace && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
     void* states = workspace;
-    void* dstates = static_cast<unsigned char*>(workspace) + (size_t)n_slots * per * esize(dt);
+    void* dstates =
+        workspace ? static_cast<unsigned char*>(workspace) + (size_t)n_slots * per * esize(dt)
+                  : nullptr;
 
     // the forward pass again, keeping the state after every chunk (validates
     // the forward arguments and the state table against them)
@@ -419,8 +430,13 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void
     sr.snap = static_cast<float*>(states);
     const int32_t fflags = kda::kChunkNoOutput | kda::kChunkSnapSlots |
                            (dt == KDA_BF16 ? kda::kChunkSnapBf16 : 0);
+    SnapReq sr_check = sr;
+    if (no_workspace) {   // (the state table is checked once it is known)
+        sr_check.n_snap = 0;
+        sr_check.snap = nullptr;
+    }
     kda_status st = chunk_fwd_impl(q, k, v, log_alpha, beta, h0, cu_seqlens, N, T_total, H, Dk,
-                                   Dv, dt, nullptr, nullptr, nullptr, 0, kda::kChunk, 0, sr,
+                                   Dv, dt, nullptr, nullptr, nullptr, 0, kda::kChunk, 0, sr_check,
                                    fflags, stream, true);
     if (st != KDA_OK) return st;
 
@@ -430,11 +446,11 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void
     const Span sq = span(q, nTok), sk = span(k, nTok), sv = span(v, nTok),
                sg = span(log_alpha, nTok), sb = span(beta, nB),
                sh0 = span(h0, h0 ? nState : 0),
-               scu = span(cu_seqlens, cu_seqlens ? (uint64_t)(N + 1) * 4 : 0),
+               scu = span(cu_seqlens, cu_seqlens ? ((uint64_t)N + 1) * 4 : 0),
                sdo = span(dout, nTok), sdhT = span(dhT, dhT ? nState : 0),
-               sws = span(workspace, need), sdq = span(dq, nTok), sdk = span(dk, nTok),
-               sdv = span(dv, nTok), sdg = span(dlog_alpha, nTok), sdb = span(dbeta, nB),
-               sdh0 = span(dh0, dh0 ? nState : 0);
+               sws = span(workspace, no_workspace ? 0 : need), sdq = span(dq, nTok),
+               sdk = span(dk, nTok), sdv = span(dv, nTok), sdg = span(dlog_alpha, nTok),
+               sdb = span(dbeta, nB), sdh0 = span(dh0, dh0 ? nState : 0);
     const Span outs[] = {sdq, sdk, sdv, sdg, sdb, sdh0};
     for (int i = 0; i < 6; ++i) {
         if (overlaps_any(outs[i], {sq, sk, sv, sg, sb, sh0, scu, sdo, sdhT, sws}))
@@ -443,6 +459,7 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void
             if (overlaps(outs[i], outs[j])) return KDA_ERR_ALIAS;
     }
     if (overlaps_any(sws, {sdo, sdhT})) return KDA_ERR_ALIAS;
+    if (check_only) return KDA_OK;
 
     st = chunk_fwd_impl(q, k, v, log_alpha, beta, h0, cu_seqlens, N, T_total, H, Dk, Dv, dt,
                         nullptr, nullptr, nullptr, 0, kda::kChunk, 0, sr, fflags, stream);
@@ -471,6 +488,21 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void
     a.n_slots = n_slots;
     if (kda::launch_bwd(a, (int)dt, stream) != hipSuccess) return KDA_ERR_DEVICE;
     return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void* log_alpha,
+                         const void* beta, const float* h0, const int32_t* cu_seqlens,
+                         int32_t N, int64_t T_total, int32_t H, int32_t Dk, int32_t Dv,
+                         kda_dtype dt, const void* dout, const float* dhT, void* dq, void* dk,
+                         void* dv, void* dlog_alpha, void* dbeta, float* dh0, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+    return chunk_bwd_impl(q, k, v, log_alpha, beta, h0, cu_seqlens, N, T_total, H, Dk, Dv, dt,
+                          dout, dhT, dq, dk, dv, dlog_alpha, dbeta, dh0, workspace,
+                          workspace_bytes, stream, false, false);
 }
 
 kda_status kda_prologue(const void* xq, const void* xk, const void* xv, const void* a_raw,
@@ -505,7 +537,7 @@ kda_status kda_prologue(const void* xq, const void* xk, const void* xv, const vo
                sa = span(a_raw, nTok), sbr = span(b_raw, nB),
                sw = span(conv_w, T_total > 0 ? 3 * row * 4 * 4 : 0),
                sbias = span(a_bias, T_total > 0 ? row * 4 : 0),
-               scu = span(cu_seqlens, cu_seqlens ? (uint64_t)(N + 1) * 4 : 0),
+               scu = span(cu_seqlens, cu_seqlens ? ((uint64_t)N + 1) * 4 : 0),
                ssi = span(conv_state_in, conv_state_in ? nState : 0),
                sso = span(conv_state_out, conv_state_out ? nState : 0), sq = span(q, nTok),
                sk = span(k, nTok), sv = span(v, nTok), sla = span(log_alpha, nTok),

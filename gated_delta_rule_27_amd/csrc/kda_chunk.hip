@@ -23,11 +23,11 @@
 // Decay-factor range.  Exponents are never formed from the chunk start when
 // they could overflow: the Gram products use, for row tile R (16 tokens),
 // the reference point just before R, so left factors are <= 1 and right
-// factors are <= 1 except on the diagonal tile, where they are bounded by
-// e^80 because log alpha >= -5 ("From GPT-2 to Kimi K3", ch. 5 "K3's
-// lower-bounded decay": a 16-token tile's reciprocal cumulative decay stays
-// below e^80, inside the BF16 range).  So both diagonal and off-diagonal
-// tiles are plain dense MFMA products.
+// factors are <= 1 except on the diagonal tile.  There, log alpha >= -5
+// bounds the log-decay summed over 16 tokens by -80, so a right factor is
+// at most e^80 = 5.5e34, which bf16 (max 3.4e38) still represents ("From
+// GPT-2 to Kimi K3", ch. 5 "K3's lower-bounded decay").  Every tile, on the
+// diagonal or off it, is therefore an ordinary MFMA product.
 //
 // Kernel structure (one launch does the whole prefill).  One workgroup owns
 // one (sequence, head, value-column slice) chain and walks that sequence's
@@ -597,24 +597,6 @@ hipError_t launch_split(const ChunkArgs& a, int split, hipStream_t stream) {
 }
 
 }  // namespace
-
-bool chunk_config_supported(int dtype, int chunk, int split) {
-    (void)dtype;
-    return (chunk == 16 || chunk == 32) && (split == 1 || split == 2 || split == 4);
-}
-
-void chunk_default_config(int dtype, int64_t T_total, int32_t N, int32_t H, int* chunk,
-                          int* split) {
-    (void)T_total;
-    const int64_t chains = (int64_t)N * H;
-    if (dtype == 0) {
-        *chunk = 16;
-        *split = chains >= 512 ? 1 : (chains >= 256 ? 2 : 4);
-    } else {
-        *chunk = 16;
-        *split = chains >= 256 ? 1 : 2;
-    }
-}
 
 hipError_t launch_chunk(const ChunkArgs& a, int dtype, int chunk, int split,
                         hipStream_t stream) {

@@ -123,10 +123,25 @@ struct DecodeMultiArgs {
 // bf16 with chunk 16 and split 1 or 2 runs the wave-specialised pipelined
 // kernel (kda_chunk_ws.hip); every other combination runs the phase-serial
 // kernel (kda_chunk.hip).
-bool chunk_config_supported(int dtype, int chunk, int split);
+// (host-only choices, inline so that the C ABI's validation builds without
+// the kernels, e.g. for the host sanitizer tests)
+inline bool chunk_config_supported(int dtype, int chunk, int split) {
+    (void)dtype;
+    return (chunk == 16 || chunk == 32) && (split == 1 || split == 2 || split == 4);
+}
+inline void chunk_default_config(int dtype, int64_t T_total, int32_t N, int32_t H, int* chunk,
+                                 int* split) {
+    (void)T_total;
+    const int64_t chains = (int64_t)N * H;
+    if (dtype == 0) {
+        *chunk = 16;
+        *split = chains >= 512 ? 1 : (chains >= 256 ? 2 : 4);
+    } else {
+        *chunk = 16;
+        *split = chains >= 256 ? 1 : 2;
+    }
+}
 hipError_t launch_chunk_ws(const ChunkArgs& a, int split, hipStream_t stream);
-void chunk_default_config(int dtype, int64_t T_total, int32_t N, int32_t H,
-                          int* chunk, int* split);
 hipError_t launch_chunk(const ChunkArgs& a, int dtype, int chunk, int split,
                         hipStream_t stream);
 
@@ -195,7 +210,17 @@ hipError_t launch_bwd(const BwdArgs& a, int dtype, hipStream_t stream);
 // the reverse recursion for bf16 inputs, pipelined (kda_bwd_ws.hip)
 hipError_t launch_bwd_dh_ws(const BwdArgs& a, hipStream_t stream);
 
-int32_t prologue_tokens_per_wave(int64_t T_total, int32_t H);
+constexpr int kPrologueLookahead = 8;   // tokens the prologue loads ahead per lane
+
+// Tokens per prologue wave: enough waves to cover the chip several times,
+// blocks long enough that the three rows of history per block stay a small
+// overhead.
+inline int32_t prologue_tokens_per_wave(int64_t T_total, int32_t H) {
+    const int64_t nslice = (H + 3) / 4;
+    int32_t tb = 32;
+    while (tb > kPrologueLookahead && 4 * nslice * ((T_total + tb - 1) / tb) < 8192) tb /= 2;
+    return tb;
+}
 hipError_t launch_prologue(const PrologueArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_epilogue(const EpilogueArgs& a, int dtype, hipStream_t stream);
 

@@ -32,7 +32,7 @@ namespace {
 
 constexpr int kConvW = 4;            // short-convolution width
 constexpr int kHist = kConvW - 1;    // inputs of history per sequence
-constexpr int kPU = 8;               // tokens loaded ahead per lane
+constexpr int kPU = kPrologueLookahead;   // tokens loaded ahead per lane
 
 __device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
     const floatx4 a = *reinterpret_cast<const floatx4*>(p);
@@ -331,15 +331,6 @@ hipError_t launch_epilogue_t(const EpilogueArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
-
-int32_t prologue_tokens_per_wave(int64_t T_total, int32_t H) {
-    // enough waves to cover the chip several times, long enough blocks that
-    // the three rows of history per block stay a small overhead
-    const int64_t nslice = (H + 3) / 4;
-    int32_t tb = 32;
-    while (tb > kPU && 4 * nslice * ((T_total + tb - 1) / tb) < 8192) tb /= 2;
-    return tb;
-}
 
 hipError_t launch_prologue(const PrologueArgs& a, int dtype, hipStream_t stream) {
     return dtype == 0 ? launch_prologue_t<float>(a, stream) : launch_prologue_t<bf16>(a, stream);

@@ -42,8 +42,8 @@
  *   - Input contract (not checked, never clamped): log_alpha in [-5, 0]
  *     (the K3 lower-bounded log-decay, "From GPT-2 to Kimi K3", ch. 5
  *     "K3's lower-bounded decay"), beta in [0, 1].  Inside the contract the
- *     chunk kernels' decay factors stay finite (a 16-token tile's reciprocal
- *     cumulative decay is below e^80).
+ *     chunk kernels' decay factors stay finite: 16 tokens at log_alpha >= -5
+ *     give a log-decay >= -80, so no factor exceeds e^80.
  */
 #ifndef KDA_H
 #define KDA_H

@@ -383,6 +383,7 @@ def test_chunk_error_precedence(L):
     (dict(B=-1), BAD_SHAPE),
     (dict(H=0), BAD_SHAPE),
     (dict(Dk=32), BAD_SHAPE),
+    (dict(H=65537), BAD_SHAPE),          # above KDA_MAX_HEADS, as for every entry point
     (dict(S=None), NULL_ARG),
     (dict(o=None), NULL_ARG),
     (dict(q=None), NULL_ARG),
@@ -405,3 +406,101 @@ def test_binding_refuses_host_tensors():
     x = torch.zeros(4, 2, D, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="ROCm device"):
         kda.kda_chunk_fwd(x, x, x, x, torch.zeros(4, 2, dtype=torch.bfloat16))
+
+
+# ---- the binding checks the shape of every caller-supplied buffer ------------
+# The C ABI receives bare pointers, so a buffer that is too small would be
+# written past its end.  These checks run before any device check, so host
+# tensors reach them here.
+
+def _t(*shape, dtype=None):
+    torch = pytest.importorskip("torch")
+    return torch.zeros(shape, dtype=dtype or torch.bfloat16)
+
+
+def _prefill(T=8, H=2):
+    x = _t(T, H, D)
+    return dict(q=x, k=x, v=x, log_alpha=x, beta=_t(T, H))
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(o=(7, 2, D)), "o must have shape"),
+    (dict(o=(8, 2, D - 8)), "o must have shape"),
+    (dict(h_T=(1, 2, D, D - 1)), "h_T must have shape"),
+    (dict(h_T=(2, 2, D, D)), "h_T must have shape"),
+    (dict(h0=(1, 3, D, D)), "h0 must have shape"),
+])
+def test_binding_chunk_fwd_checks_buffer_shapes(kw, msg):
+    torch = pytest.importorskip("torch")
+    a = _prefill()
+    extra = {n: _t(*s, dtype=torch.float32 if n != "o" else None) for n, s in kw.items()}
+    with pytest.raises(ValueError, match=msg):
+        kda.kda_chunk_fwd(**a, **extra)
+
+
+def test_binding_snap_checks_buffer_shapes():
+    torch = pytest.importorskip("torch")
+    a = _prefill(T=64)
+    with pytest.raises(ValueError, match="snap must have shape"):
+        kda.kda_chunk_fwd_snap(**a, interval=16, n_snap=4,
+                               snap=_t(3, 2, D, D, dtype=torch.float32))
+    with pytest.raises(ValueError, match="o must have shape"):
+        kda.kda_chunk_fwd_snap(**a, interval=16, o=_t(63, 2, D))
+    with pytest.raises(ValueError, match="h_T must have shape"):
+        kda.kda_chunk_fwd_snap(**a, interval=16, h_T=_t(1, 1, D, D, dtype=torch.float32))
+    cu = torch.tensor([0, 32, 64], dtype=torch.int32)
+    with pytest.raises(ValueError, match="snap_cu must have shape"):
+        kda.kda_chunk_fwd_snap(**a, cu_seqlens=cu, interval=16, n_snap=4,
+                               snap_cu=torch.zeros(2, dtype=torch.int32))
+    with pytest.raises(ValueError, match="n_snap must be"):
+        kda.kda_chunk_fwd_snap(**a, interval=16, n_snap=-1)
+
+
+def test_binding_decode_checks_buffer_shapes():
+    torch = pytest.importorskip("torch")
+    B, H = 4, 2
+    x = _t(B, H, D)
+    S = _t(B, H, D, D, dtype=torch.float32)
+    with pytest.raises(ValueError, match="o must have shape"):
+        kda.kda_decode_step(x, x, x, x, _t(B, H), S, o=_t(B - 1, H, D))
+    with pytest.raises(ValueError, match="S must have shape"):
+        kda.kda_decode_step(x, x, x, x, _t(B, H), _t(B, H, D, D - 4, dtype=torch.float32))
+    K = 3
+    xm = _t(B, K, H, D)
+    with pytest.raises(ValueError, match="o must have shape"):
+        kda.kda_decode_multi(xm, xm, xm, xm, _t(B, K, H), S, o=_t(B, K - 1, H, D))
+    with pytest.raises(ValueError, match="n_tok must have shape"):
+        kda.kda_decode_multi(xm, xm, xm, xm, _t(B, K, H), S,
+                             n_tok=torch.zeros(B + 1, dtype=torch.int32))
+
+
+def test_binding_other_calls_check_buffer_shapes():
+    torch = pytest.importorskip("torch")
+    a = _prefill()
+    with pytest.raises(ValueError, match="do must have shape"):
+        kda.kda_chunk_bwd(**a, do=_t(8, 2, D - 8))
+    with pytest.raises(ValueError, match="dhT must have shape"):
+        kda.kda_chunk_bwd(**a, do=_t(8, 2, D), dhT=_t(2, 2, D, D, dtype=torch.float32))
+    o = _t(8, 2, D)
+    with pytest.raises(ValueError, match="y must have shape"):
+        kda.kda_epilogue(o, o, _t(2, D, dtype=torch.float32), y=_t(8, 1, D))
+    with pytest.raises(ValueError, match="norm_w must have shape"):
+        kda.kda_epilogue(o, o, _t(3, D, dtype=torch.float32))
+    M = _t(2, 2, D, D, dtype=torch.float32)
+    with pytest.raises(ValueError, match="B must have shape"):
+        kda.kda_segment_scan(M, _t(1, 2, D, D, dtype=torch.float32))
+    x, b = _t(8, 2, D), _t(8, 2)
+    w, bias = _t(3, 2, D, 4, dtype=torch.float32), _t(2, D, dtype=torch.float32)
+    with pytest.raises(ValueError, match="state_out must have shape"):
+        kda.kda_prologue(x, x, x, x, b, w, bias, state_out=_t(1, 3, 2, 2, D))
+    with pytest.raises(ValueError, match="conv_w must have shape"):
+        kda.kda_prologue(x, x, x, x, b, _t(3, 2, D, 3, dtype=torch.float32), bias)
+
+
+def test_binding_refuses_mixed_devices():
+    # one host tensor among the arguments: refused before any device work
+    torch = pytest.importorskip("torch")
+    a = _prefill()
+    with pytest.raises(ValueError, match="ROCm device"):
+        kda.kda_chunk_fwd(**a, o=_t(8, 2, D))
+

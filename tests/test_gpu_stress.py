@@ -159,3 +159,38 @@ def test_backward_decay_at_bound(dtype):
                    np_(do), dhT=np_(dhT), h0=np_(d["h0"]), cu_seqlens=cu)
     for name, gv, r in zip(("dq", "dk", "dv", "dlog_alpha", "dbeta", "dh0"), got, ref):
         check(name, np_(gv), r, TOL[dtype])
+
+
+@pytest.mark.parametrize("dtype,mu", [("f32", -4.0), ("bf16", -4.0)])
+def test_million_tokens_slow_decay(dtype, mu):
+    """The long-memory run: one sequence of 1,048,576 tokens (the K3 context
+    length, "An infra-oriented diagram of Kimi K3", KDA card) with slow decay
+    (mu = -4: per-channel memories of tens to hundreds of tokens) and a
+    random h0, on 2 heads, every token of both compared with the fp64 oracle
+    -- fp32 inputs at 1e-4, bf16 (the pipelined kernel) at 2e-2.  The error
+    is also taken per window of 65,536 tokens, so that drift late in the
+    chain cannot hide behind the whole run's largest outputs."""
+    import oracle
+    kda = need_gpu()
+    T, H = 1 << 20, 2
+    case(f"1M-token slow decay mu={mu} {dtype} T={T} H={H} random h0: generating inputs")
+    d = kda_inputs.prefill_inputs(T, H, dtype=dtype, device="cuda", seed=29, decay_mu=mu,
+                                  h0_std=0.5 if dtype == "f32" else 0.02)
+    case(f"1M-token slow decay mu={mu} {dtype}: GPU run")
+    o, hT = gpu_prefill(kda, d)
+    case(f"1M-token slow decay mu={mu} {dtype}: fp64 oracle")
+    ro, rh = oracle.fwd(np_(d["q"]), np_(d["k"]), np_(d["v"]), np_(d["log_alpha"]),
+                        np_(d["beta"]), h0=np_(d["h0"]), dv_block=16)
+    go, gh = np_(o), np_(hT)
+    tol = TOL[dtype]
+    for h in range(H):
+        check(f"o head {h}", go[:, h], ro[:, h], tol)
+        check(f"h_T head {h}", gh[:, h], rh[:, h], tol)
+        worst = 0.0
+        for w0 in range(0, T, 1 << 16):
+            w = slice(w0, w0 + (1 << 16))
+            den = np.abs(ro[w, h]).max()
+            e = float(np.abs(go[w, h] - ro[w, h]).max() / den)
+            worst = max(worst, e)
+            assert e <= tol, f"head {h} tokens {w0}..: normwise error {e:.3e} > {tol:.0e}"
+        print(f"    head {h}: worst 65,536-token window {worst:.3e}", flush=True)
