@@ -163,6 +163,16 @@ def _shape(t, name, shape):
         raise ValueError(f"{name} must have shape {shape} (got {tuple(t.shape)})")
 
 
+def _shape_at_least(t, name, n0, rest):
+    """A buffer of at least n0 entries of shape `rest` (None = not given):
+    the C call writes entries below n0 only."""
+    rest = tuple(int(x) for x in rest)
+    if t is not None and (t.dim() != 1 + len(rest) or tuple(t.shape[1:]) != rest
+                          or t.shape[0] < int(n0)):
+        raise ValueError(f"{name} must have shape (>= {int(n0)},) + {rest} "
+                         f"(got {tuple(t.shape)})")
+
+
 def _same_device(dev, **named):
     for name, t in named.items():
         if t is not None and t.device != dev:
@@ -271,7 +281,8 @@ def kda_chunk_fwd_snap(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, in
                        store_state=True):
     """kda_chunk_fwd that also writes the state of every sequence after each
     multiple of `interval` tokens (a multiple of 16) to `snap`
-    [n_snap, H, 128, 128] fp32, laid out as snapshot_index describes.
+    [n_snap, H, 128, 128] fp32 (a longer buffer is allowed: entries at or
+    past n_snap are never written), laid out as snapshot_index describes.
     Returns (o, h_T, snap, snap_cu)."""
     torch = _torch()
     T, H, Dk, Dv, N = _prefill_shapes(q, k, v, log_alpha, beta, h0, cu_seqlens)
@@ -285,7 +296,7 @@ def kda_chunk_fwd_snap(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, in
         if n_snap < 0:
             raise ValueError("n_snap must be >= 0")
         _shape(snap_cu, "snap_cu", (N + 1,))
-        _shape(snap, "snap", (n_snap, H, Dk, Dv))
+        _shape_at_least(snap, "snap", n_snap, (H, Dk, Dv))
     _prefill_devices(q, k, v, log_alpha, beta, h0, cu_seqlens)
     _dev(o, "o", q.dtype)
     _dev(h_T, "h_T", torch.float32)
@@ -295,7 +306,7 @@ def kda_chunk_fwd_snap(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, in
     dt = _dtype_code(q)
     if n_snap is None:
         snap_cu, n_snap = snapshot_index(cu_seqlens, T, interval)
-        _shape(snap, "snap", (n_snap, H, Dk, Dv))
+        _shape_at_least(snap, "snap", n_snap, (H, Dk, Dv))
     if snap is None:
         snap = torch.empty((n_snap, H, Dk, Dv), dtype=torch.float32, device=q.device)
     if o is None:

@@ -429,7 +429,9 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) float sdW[C * FP];
     __shared__ __attribute__((aligned(16))) float sdWt[C * FP];
     __shared__ float sGam[kHeadDim];
-    __shared__ float sDG[kHeadDim];   // row sums of D o S
+    // row sums of D o S: one partial per wave (16 columns each), summed in
+    // wave order by the reader, so the result does not depend on timing
+    __shared__ float sDG[8][kHeadDim];
     __shared__ float sBeta[C];
 
     const TIn* q = static_cast<const TIn*>(a.q);
@@ -492,7 +494,6 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdArgs a) {
                            E);
         const float gam = E[C - 1];
         sGam[i] = gam;
-        sDG[i] = 0.f;
 #pragma unroll
         for (int r = 0; r < C; ++r) {
             const float inv = 1.f / E[r];
@@ -593,7 +594,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdArgs a) {
                 s += __shfl_xor(s, 4, 16);
                 s += __shfl_xor(s, 2, 16);
                 s += __shfl_xor(s, 1, 16);
-                if (l16 == 0) atomicAdd(&sDG[16 * it + 4 * g + e], s);
+                if (l16 == 0) sDG[wave][16 * it + 4 * g + e] = s;
             }
     }
     __syncthreads();
@@ -710,7 +711,12 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(BwdArgs a) {
         // the chunk-total decay Gamma = exp(G_15)
         kvk += __shfl_xor(kvk, 16, 64);
         kvk += __shfl_xor(kvk, 32, 64);
-        if (g == 3) dG[3] += gam * sDG[i] + kvk;
+        if (g == 3) {
+            float ds = sDG[0][i];
+#pragma unroll
+            for (int w = 1; w < 8; ++w) ds += sDG[w][i];
+            dG[3] += gam * ds + kvk;
+        }
         // dlog_alpha_s = sum_{r >= s} dG_r: suffix over the lane's rows, then
         // over the lane groups above it
         float suf[4];

@@ -444,6 +444,13 @@ def test_binding_snap_checks_buffer_shapes():
     with pytest.raises(ValueError, match="snap must have shape"):
         kda.kda_chunk_fwd_snap(**a, interval=16, n_snap=4,
                                snap=_t(3, 2, D, D, dtype=torch.float32))
+    with pytest.raises(ValueError, match="snap must have shape"):
+        kda.kda_chunk_fwd_snap(**a, interval=16, n_snap=4,
+                               snap=_t(5, 2, D, D - 1, dtype=torch.float32))
+    # a longer buffer passes the shape check (then needs a device)
+    with pytest.raises(ValueError, match="ROCm device"):
+        kda.kda_chunk_fwd_snap(**a, interval=16, n_snap=4,
+                               snap=_t(6, 2, D, D, dtype=torch.float32))
     with pytest.raises(ValueError, match="o must have shape"):
         kda.kda_chunk_fwd_snap(**a, interval=16, o=_t(63, 2, D))
     with pytest.raises(ValueError, match="h_T must have shape"):

@@ -137,3 +137,43 @@ def test_backward_single_token_and_empty():
     got = _gpu(kda, e)
     # no tokens: dh0 is dhT itself
     assert torch.equal(got[5], e["dhT"])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_bitwise_reproducible_over_any_workspace(dtype):
+    """Gradients are a deterministic function of the inputs: bit for bit the
+    same on every run (no floating-point atomics in any reduction), and
+    whatever the workspace held before the call (zeros, all-ones bytes --
+    NaN in both table dtypes -- or random bytes), so no table entry is read
+    before this call has written it.  Packed sequences with a one-token
+    last chunk, a partial one, an empty sequence and a long one."""
+    kda = need_gpu()
+    lengths = [17, 23, 0, 70]
+    T, H = sum(lengths), 3
+    case(f"backward determinism {dtype} T={T} H={H} lengths={lengths}")
+    d = kda_inputs.prefill_inputs(T, H, dtype=dtype, device="cuda", seed=81, lengths=lengths,
+                                  h0_std=0.1)
+    g = torch.Generator(device="cuda").manual_seed(81)
+    do = torch.randn((T, H, 128), generator=g, device="cuda").to(d["q"].dtype)
+    dhT = torch.randn((len(lengths), H, 128, 128), generator=g, device="cuda") * 0.1
+    nbytes = kda.kda_chunk_bwd_workspace_size(T, len(lengths), H,
+                                              dtype=kda.KDA_BF16 if dtype == "bf16" else kda.KDA_F32)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    runs = []
+    for fill in ("zeros", "ones", "random"):
+        if fill == "zeros":
+            ws.zero_()
+        elif fill == "ones":
+            ws.fill_(0xFF)
+        else:
+            ws.copy_(torch.randint(0, 256, (nbytes,), generator=g, device="cuda",
+                                   dtype=torch.int32).to(torch.uint8))
+        runs.append(kda.kda_chunk_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], do,
+                                      h0=d["h0"], cu_seqlens=d["cu_seqlens"], dhT=dhT,
+                                      workspace=ws))
+        torch.cuda.synchronize()
+    names = ("dq", "dk", "dv", "dlog_alpha", "dbeta", "dh0")
+    for r in runs[1:]:
+        for name, a, b in zip(names, r, runs[0]):
+            assert torch.isfinite(a.float()).all(), f"{name}: non-finite"
+            assert torch.equal(a, b), f"{name} differs between runs"
