@@ -21,7 +21,9 @@ Functions (same names as the C entry points):
   S_final)``  the affine summaries of sequence segments and the scan that
   chains them (context parallelism);
 * ``kda_chunk_bwd`` -> ``(dq, dk, dv, dlog_alpha, dbeta, dh0)``  the
-  backward (training) pass of the chunkwise forward;
+  backward (training) pass of the chunkwise forward, and
+  ``kda_chunk_bwd_noalloc``, the same without a workspace (for callers that
+  cannot allocate: the tables live in the library's static device scratch);
 * ``kda_prologue`` and ``kda_epilogue``  the elementwise work of a KDA layer
   around the core (short convolution, Swish, norms, gates);
 * ``kda_chunk_fwd_workspace_size``, ``kda_status_str``, ``kda_abi_version``.
@@ -94,6 +96,10 @@ def lib():
         L.kda_chunk_bwd.restype = ctypes.c_int
         L.kda_chunk_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
                                     ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.kda_chunk_bwd_noalloc.restype = ctypes.c_int
+        L.kda_chunk_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32,
+                                            i32, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp,
+                                            vp]
         _lib = L
     return _lib
 
@@ -440,6 +446,56 @@ def kda_chunk_bwd(q, k, v, log_alpha, beta, do, h0=None, cu_seqlens=None, dhT=No
     return dq, dk, dv, dg, db, dh0
 
 
+# KDA_BWD_NOALLOC_MAX_BYTES of include/kda.h: the largest backward workspace
+# kda_chunk_bwd_noalloc serves from the library's own device scratch
+BWD_NOALLOC_MAX_BYTES = 256 << 20
+
+
+def kda_chunk_bwd_noalloc(q, k, v, log_alpha, beta, do, h0=None, cu_seqlens=None, dhT=None, *,
+                          want_dh0=True, grads=None):
+    """kda_chunk_bwd without a workspace argument: the per-chunk tables live
+    in the library's static device scratch (at most BWD_NOALLOC_MAX_BYTES of
+    workspace, i.e. kda_chunk_bwd_workspace_size must not exceed it).  The C
+    call allocates nothing; `grads` may supply the six output tensors
+    (dq, dk, dv, dlog_alpha, dbeta, dh0-or-None) so that this function
+    allocates nothing either.  Calls that overlap on one GPU share the
+    scratch: keep them on one stream.  Returns the six gradients."""
+    torch = _torch()
+    T, H, Dk, Dv, N = _prefill_shapes(q, k, v, log_alpha, beta, h0, cu_seqlens)
+    _tensors(do=do, dhT=dhT)
+    _shape(do, "do", (T, H, Dv))
+    _shape(dhT, "dhT", (N, H, Dk, Dv))
+    if grads is not None:
+        if len(grads) != 6:
+            raise ValueError("grads must be (dq, dk, dv, dlog_alpha, dbeta, dh0 or None)")
+        _tensors(**dict(zip(("dq", "dk", "dv", "dlog_alpha", "dbeta", "dh0"), grads)))
+        for name, t, shape in zip(("dq", "dk", "dv", "dlog_alpha", "dbeta", "dh0"), grads,
+                                  ((T, H, Dk), (T, H, Dk), (T, H, Dv), (T, H, Dk), (T, H),
+                                   (N, H, Dk, Dv))):
+            _shape(t, name, shape)
+    _prefill_devices(q, k, v, log_alpha, beta, h0, cu_seqlens)
+    _dev(do, "do", q.dtype)
+    _dev(dhT, "dhT", torch.float32)
+    _same_device(q.device, do=do, dhT=dhT)
+    dt = _dtype_code(q)
+    if grads is None:
+        dq, dk, dv, dg = (torch.empty_like(x) for x in (q, k, v, log_alpha))
+        db = torch.empty_like(beta)
+        dh0 = (torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device)
+               if want_dh0 else None)
+    else:
+        dq, dk, dv, dg, db, dh0 = grads
+        for name, t in zip(("dq", "dk", "dv", "dlog_alpha", "dbeta"), (dq, dk, dv, dg, db)):
+            _dev(t, name, q.dtype)
+        _dev(dh0, "dh0", torch.float32)
+        _same_device(q.device, dq=dq, dk=dk, dv=dv, dlog_alpha=dg, dbeta=db, dh0=dh0)
+    _check(lib().kda_chunk_bwd_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0), _ptr(cu_seqlens), N,
+        T, H, Dk, Dv, dt, _ptr(do), _ptr(dhT), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(db),
+        _ptr(dh0), _stream(q.device)))
+    return dq, dk, dv, dg, db, dh0
+
+
 def kda_prologue(xq, xk, xv, a_raw, b_raw, conv_w, a_bias, cu_seqlens=None, conv_state=None,
                  *, l2_eps=1e-6, store_state=True, state_out=None):
     """Prologue of a KDA layer: Swish(short conv) for q, k, v (q, k then
@@ -552,5 +608,6 @@ def kda_decode_multi(q, k, v, log_alpha, beta, S, n_tok=None, *, update_state=Tr
 __all__ = ["kda_chunk_fwd", "kda_chunk_fwd_snap", "snapshot_index", "kda_decode_step",
            "kda_decode_multi", "kda_segment_summary", "kda_segment_scan", "kda_prologue",
            "kda_epilogue", "kda_chunk_bwd", "kda_chunk_bwd_workspace_size",
+           "kda_chunk_bwd_noalloc", "BWD_NOALLOC_MAX_BYTES",
            "kda_chunk_fwd_workspace_size", "kda_status_str", "kda_abi_version", "KDAError",
            "lib", "LIB_PATH"]

@@ -18,7 +18,7 @@ LIB = os.path.join(HERE, "libkda.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = ["kda_api.cpp", "kda_chunk.hip", "kda_chunk_ws.hip", "kda_decode.hip",
            "kda_segment.hip", "kda_layer.hip", "kda_bwd.hip",
-           "kda_bwd_ws.hip"]
+           "kda_bwd_ws.hip", "kda_noalloc.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -505,6 +505,28 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void
                           workspace_bytes, stream, false, false);
 }
 
+kda_status kda_chunk_bwd_noalloc(const void* q, const void* k, const void* v,
+                                 const void* log_alpha, const void* beta, const float* h0,
+                                 const int32_t* cu_seqlens, int32_t N, int64_t T_total,
+                                 int32_t H, int32_t Dk, int32_t Dv, kda_dtype dt,
+                                 const void* dout, const float* dhT, void* dq, void* dk,
+                                 void* dv, void* dlog_alpha, void* dbeta, float* dh0,
+                                 hipStream_t stream) {
+    // every argument first, on the host; then the size limit; only then the
+    // one HIP call that finds this device's copy of the library's scratch
+    kda_status st = chunk_bwd_impl(q, k, v, log_alpha, beta, h0, cu_seqlens, N, T_total, H, Dk,
+                                   Dv, dt, dout, dhT, dq, dk, dv, dlog_alpha, dbeta, dh0, nullptr,
+                                   0, stream, true, true);
+    if (st != KDA_OK) return st;
+    if (kda_chunk_bwd_workspace_size(T_total, N, H, Dk, Dv, dt) > KDA_BWD_NOALLOC_MAX_BYTES)
+        return KDA_ERR_WORKSPACE;
+    void* scratch = nullptr;
+    if (kda::noalloc_scratch(&scratch) != hipSuccess || !scratch) return KDA_ERR_DEVICE;
+    return chunk_bwd_impl(q, k, v, log_alpha, beta, h0, cu_seqlens, N, T_total, H, Dk, Dv, dt,
+                          dout, dhT, dq, dk, dv, dlog_alpha, dbeta, dh0, scratch,
+                          KDA_BWD_NOALLOC_MAX_BYTES, stream, false, false);
+}
+
 kda_status kda_prologue(const void* xq, const void* xk, const void* xv, const void* a_raw,
                         const void* b_raw, const float* conv_w, const float* a_bias,
                         const int32_t* cu_seqlens, int32_t N, int64_t T_total, int32_t H,

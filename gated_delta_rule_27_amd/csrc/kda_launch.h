@@ -207,6 +207,9 @@ struct BwdArgs {
 };
 
 hipError_t launch_bwd(const BwdArgs& a, int dtype, hipStream_t stream);
+// The current device's address of the library's static scratch array of
+// KDA_BWD_NOALLOC_MAX_BYTES (kda_noalloc.hip), looked up once per device.
+hipError_t noalloc_scratch(void** ptr);
 // the reverse recursion for bf16 inputs, pipelined (kda_bwd_ws.hip)
 hipError_t launch_bwd_dh_ws(const BwdArgs& a, hipStream_t stream);
 

@@ -259,6 +259,40 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v,
                          size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * kda_chunk_bwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving or training loops, harnesses that forbid
+ * hipMalloc): the same computation, the same kernels and the same arguments
+ * minus the workspace.  The per-chunk tables live instead in a scratch array
+ * of KDA_BWD_NOALLOC_MAX_BYTES that the library holds in device memory, one
+ * copy per GPU it runs on, from this call's first use on that GPU until the
+ * process ends.  The call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine); its first call on a device looks the array
+ * up once (hipGetSymbolAddress), after all arguments are validated.
+ *
+ * Limit: kda_chunk_bwd_workspace_size(T_total, N, H, 128, 128, dt) must not
+ * exceed KDA_BWD_NOALLOC_MAX_BYTES (256 MiB: for bf16, (T_total / 16 + N +
+ * 1) * H <= 4096, e.g. 1,024 tokens of 48 heads or 512 tokens of 96 heads);
+ * larger problems return KDA_ERR_WORKSPACE before any HIP call.  Other
+ * errors as kda_chunk_bwd (KDA_ERR_DEVICE also when the scratch array cannot
+ * be found on the current device).
+ *
+ * Every call on one GPU uses that GPU's one array, which keeps whatever the
+ * last call left there (no call needs it cleared).  Calls that overlap on
+ * one GPU -- on different streams, or from different threads -- race on
+ * it: serialise them (one stream, or events).
+ */
+#define KDA_BWD_NOALLOC_MAX_BYTES ((size_t)256 << 20)
+
+kda_status kda_chunk_bwd_noalloc(const void* q, const void* k, const void* v,
+                                 const void* log_alpha, const void* beta,
+                                 const float* h0, const int32_t* cu_seqlens,
+                                 int32_t N, int64_t T_total, int32_t H,
+                                 int32_t Dk, int32_t Dv, kda_dtype dt,
+                                 const void* dout, const float* dhT, void* dq,
+                                 void* dk, void* dv, void* dlog_alpha,
+                                 void* dbeta, float* dh0, hipStream_t stream);
+
+/*
  * Prologue of a KDA layer: from the outputs of its input projections to the
  * inputs of kda_chunk_fwd / kda_decode_step ("From GPT-2 to Kimi K3", ch. 6,
  * "Where q, k, v, alpha, and beta come from"; "An infra-oriented diagram of

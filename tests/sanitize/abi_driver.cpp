@@ -258,6 +258,31 @@ int main() {
     case_<BwdA>("bwd two gradients", KDA_ERR_ALIAS, [](BwdA& a) { a.dk = P(8); });
     case_<BwdA>("bwd workspace over q", KDA_ERR_ALIAS, [](BwdA& a) { a.ws = P(0); });
 
+    // the allocation-free backward: same validation, then its size limit
+    {
+        BwdA a;
+        expect("noalloc valid", kda_chunk_bwd_noalloc(a.q, a.k, a.v, a.g, a.b, a.h0, a.cu, a.N, a.T,
+                                                      a.H, a.Dk, a.Dv, KDA_BF16, a.dout, a.dhT,
+                                                      a.dq, a.dk, a.dv, a.dg, a.db, a.dh0,
+                                                      nullptr),
+               KDA_ERR_DEVICE);
+        expect("noalloc oversize", kda_chunk_bwd_noalloc(a.q, a.k, a.v, a.g, a.b, a.h0, a.cu, a.N,
+                                                         4096, 96, a.Dk, a.Dv, KDA_BF16, a.dout,
+                                                         a.dhT, a.dq, a.dk, a.dv, a.dg, a.db,
+                                                         a.dh0, nullptr),
+               KDA_ERR_WORKSPACE);
+        expect("noalloc alias", kda_chunk_bwd_noalloc(a.q, a.k, a.v, a.g, a.b, a.h0, a.cu, a.N, a.T,
+                                                      a.H, a.Dk, a.Dv, KDA_BF16, a.dout, a.dhT,
+                                                      a.dq, a.dq, a.dv, a.dg, a.db, a.dh0,
+                                                      nullptr),
+               KDA_ERR_ALIAS);
+        for (int64_t T : kLongs)
+            expect_valid("noalloc T", kda_chunk_bwd_noalloc(a.q, a.k, a.v, a.g, a.b, a.h0, a.cu,
+                                                            a.N, T, a.H, a.Dk, a.Dv, KDA_BF16,
+                                                            a.dout, a.dhT, a.dq, a.dk, a.dv, a.dg,
+                                                            a.db, a.dh0, nullptr));
+    }
+
     expect("valid summary", SegA().call(), KDA_ERR_DEVICE);
     case_<SegA>("summary none", KDA_ERR_NULL_ARG, [](SegA& a) { a.M = a.B = nullptr; });
     case_<SegA>("summary M on B", KDA_ERR_ALIAS, [](SegA& a) { a.M = F(8); });

@@ -23,5 +23,9 @@ hipError_t launch_prologue(const PrologueArgs&, int, hipStream_t) { return hipEr
 hipError_t launch_epilogue(const EpilogueArgs&, int, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_bwd(const BwdArgs&, int, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_bwd_dh_ws(const BwdArgs&, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t noalloc_scratch(void** ptr) {
+    *ptr = nullptr;
+    return hipErrorInvalidValue;
+}
 
 }  // namespace kda

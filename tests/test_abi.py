@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(L):
             "kda_chunk_fwd_workspace_size", "kda_status_str", "kda_abi_version",
             "kda_chunk_fwd_snap", "kda_decode_multi", "kda_segment_summary",
             "kda_segment_scan", "kda_prologue", "kda_epilogue", "kda_chunk_bwd",
-            "kda_chunk_bwd_workspace_size"} <= set(names)
+            "kda_chunk_bwd_workspace_size", "kda_chunk_bwd_noalloc"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -511,3 +511,47 @@ def test_binding_refuses_mixed_devices():
     with pytest.raises(ValueError, match="ROCm device"):
         kda.kda_chunk_fwd(**a, o=_t(8, 2, D))
 
+
+def bwd_noalloc(L, **kw):
+    a = dict(q=P(0), k=P(1), v=P(2), g=P(3), b=P(4), h0=P(5), cu=None, N=1, T=64, H=2, Dk=D,
+             Dv=D, dt=BF16, do=P(6), dhT=P(7), dq=P(8), dk=P(9), dv=P(10), dg=P(11), db=P(12),
+             dh0=P(13), stream=None)
+    a.update(kw)
+    return L.kda_chunk_bwd_noalloc(a["q"], a["k"], a["v"], a["g"], a["b"], a["h0"], a["cu"],
+                                   a["N"], a["T"], a["H"], a["Dk"], a["Dv"], a["dt"], a["do"],
+                                   a["dhT"], a["dq"], a["dk"], a["dv"], a["dg"], a["db"],
+                                   a["dh0"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=9), BAD_DTYPE),
+    (dict(Dk=64), BAD_SHAPE),
+    (dict(H=65537), BAD_SHAPE),
+    (dict(N=2, cu=None), BAD_SHAPE),
+    (dict(do=None), NULL_ARG),
+    (dict(q=None), NULL_ARG),
+    (dict(dq=P(8, 4)), MISALIGNED),
+    (dict(dq=P(0)), ALIAS),                 # gradient over an input
+    (dict(dk=P(8)), ALIAS),                 # two gradients
+    # beyond the scratch: (T/16 + N + 1) * H * 2 * 32 KiB > 256 MiB (bf16)
+    (dict(T=4096, H=96), WORKSPACE),
+    (dict(T=16 * 4095, H=1), WORKSPACE),
+    (dict(T=16 * 2047, H=1, dt=F32), WORKSPACE),
+])
+def test_bwd_noalloc_argument_errors(L, kw, code):
+    assert bwd_noalloc(L, **kw) == code
+
+
+def test_bwd_noalloc_limit_is_the_documented_size(L):
+    # the largest problems inside the limit pass validation (the scratch
+    # lookup is what fails without a GPU); one more chunk does not
+    lim = kda.BWD_NOALLOC_MAX_BYTES
+    assert lim == 256 << 20
+    assert L.kda_chunk_bwd_workspace_size(16 * 4094, 1, 1, D, D, BF16) == lim
+    assert bwd_noalloc(L, T=16 * 4094, H=1) == DEVICE
+    assert bwd_noalloc(L, T=16 * 4094 + 16, H=1) == WORKSPACE
+    assert L.kda_chunk_bwd_workspace_size(16 * 2046, 1, 1, D, D, F32) == lim
+    assert bwd_noalloc(L, T=16 * 2046, H=1, dt=F32) == DEVICE
+    assert bwd_noalloc(L, T=512, H=96) == DEVICE          # (32 + 2) * 96 = 3264 entries
+    assert bwd_noalloc(L, T=0, N=3, H=2, cu=P(14), q=None, k=None, v=None, g=None, b=None,
+                       do=None, dq=None, dk=None, dv=None, dg=None, db=None) == DEVICE
