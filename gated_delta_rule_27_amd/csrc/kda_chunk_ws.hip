@@ -68,7 +68,12 @@ struct WsCfg {
     static constexpr int NPW = 8;                // prep waves
     static constexpr int NT = 64 * (NSA + NPW);  // threads
     static constexpr int DV = 16 * NCT * NSW;    // value columns per workgroup
-    static constexpr int KP = kHeadDim + 8;      // bf16 stride of [token][channel]
+    // bf16 stride of [token][channel] rows: 280 bytes.  Consecutive rows then
+    // start 6 banks apart, which keeps the 8-byte row reads of the MFMA
+    // operands (16 rows at once), the transposed column reads and the prep
+    // waves' 8-byte row writes free of bank conflicts; the 272-byte stride
+    // (4 banks) made every operand row read a two-way conflict.
+    static constexpr int KP = kHeadDim + 12;
     static constexpr int TP = kWsC + 8;          // bf16 stride of [.][token]
     static constexpr int AP = 20;                // fp32 stride of the A tile
 
@@ -596,6 +601,7 @@ hipError_t launch_ws_t(const ChunkArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_chunk_ws(const ChunkArgs& a, int split, hipStream_t stream) {
+    if (chunk_ws2_supports(a, split)) return launch_chunk_ws2(a, split, stream);
     // the deeper pipeline costs one more iteration per sequence and saves a
     // few percent per iteration: used from 512 tokens per sequence on average
     const bool deep = a.N > 0 && a.T_total >= 512 * (int64_t)a.N;

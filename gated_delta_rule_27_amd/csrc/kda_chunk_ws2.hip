@@ -1,0 +1,441 @@
+// kda_chunk_ws2.hip -- the wave-specialised bf16 prefill of kda_chunk_ws.hip,
+// cut down to the instructions the plain prefill needs (gfx950).
+//
+// Same mathematics and wave roles as kda_chunk_ws.hip (see its header): per
+// 16-token chunk with incoming state S0,
+//   Ktil = K o E, Qtil = Q o E, Khat = K / E, Kvec = K o Gamma / E,
+//   A = strict_lower(diag(beta) Ktil Khat^T), P = lower_incl(Qtil Khat^T),
+//   T = (I + A)^{-1} diag(beta), U = T (V - Ktil S0),
+//   O = Qtil S0 + P U,  S_C = Diag(Gamma) S0 + Kvec^T U,
+// with the decay reference at the chunk start, so every factor is <= e^80
+// ("From GPT-2 to Kimi K3", ch. 5 "K3's lower-bounded decay").
+//
+// A wavefront issues about one instruction every eight cycles whatever its
+// type (measured on MI355X: scalar, vector and LDS instructions alike), and
+// the per-chunk iteration of the pipelined kernel is set by how many
+// instructions its busiest wavefronts issue.  This version removes the
+// per-iteration bookkeeping of the general kernel:
+//   * every ring buffer holds 2 or 4 chunks and the loop is unrolled four
+//     times, so each ring slot is a compile-time constant (no modular
+//     arithmetic on the scalar unit);
+//   * no stage tests whether its chunk exists.  The rings start out holding
+//     the identity chunk (Gamma = 1, everything else 0: the state passes
+//     through unchanged), and chunks past the end of a sequence read zeros
+//     through their buffer resources (log alpha = 0, beta = 0, V = 0), which
+//     is again the identity; their outputs fall outside the resources and
+//     are dropped.
+// Pipeline: iteration c forms the scaled operands of chunk c+3 (prep waves),
+// the Gram tiles of chunk c+2 (state waves 0 and 1), the UT solve of chunk
+// c+1 (prep waves 0-3) and the state update of chunk c (state waves); one
+// barrier per iteration.
+#include <type_traits>
+
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int kC2 = 16;       // tokens per chunk
+constexpr int kXcd2 = 8;      // MI355X accelerator complex dies
+constexpr float kLog2e2 = 1.4426950408889634f;
+
+template <int NSW_>
+struct Ws2Cfg {
+    static constexpr int NSW = NSW_;             // state waves (16 value columns each)
+    static constexpr int NPW = 8;                // prep waves
+    static constexpr int NT = 64 * (NSW + NPW);  // threads
+    static constexpr int DV = 16 * NSW;          // value columns per workgroup
+    // bf16 stride of [token][channel] rows: 280 bytes, 6 banks apart, which
+    // keeps 8-byte row reads, transposed column reads and 8-byte row writes
+    // of 16 rows free of bank conflicts
+    static constexpr int KP = kHeadDim + 12;
+    static constexpr int TP = kC2 + 8;           // bf16 stride of [.][token]
+    static constexpr int AP = 20;                // fp32 stride of the A tile
+    static constexpr int VP = DV + 8;            // bf16 stride of the V / O tiles
+
+    static constexpr size_t szTok = kC2 * KP * 2;
+    static constexpr size_t szTile = kC2 * TP * 2;
+    static constexpr size_t szA = kC2 * AP * 4;
+    static constexpr size_t szVO = kC2 * VP * 2;
+    static constexpr size_t KN0 = 0;                        // -Ktil, 4 slots
+    static constexpr size_t QS0 = KN0 + 4 * szTok;          //  Qtil, 4 slots
+    static constexpr size_t KV0 = QS0 + 4 * szTok;          //  Kvec rows, 4 slots
+    static constexpr size_t KH0 = KV0 + 4 * szTok;          //  Khat, 2 slots
+    static constexpr size_t GAM0 = KH0 + 2 * szTok;         //  Gamma, 4 slots
+    static constexpr size_t BETA0 = GAM0 + 4 * 512;         //  beta, 4 slots
+    static constexpr size_t A0 = BETA0 + 4 * 64;            //  A, 2 slots
+    static constexpr size_t P0 = A0 + 2 * szA;              //  P, 4 slots
+    static constexpr size_t T0 = P0 + 4 * szTile;           //  T, 2 slots
+    static constexpr size_t VT0 = T0 + 2 * szTile;          //  V, 4 slots
+    static constexpr size_t OT0 = VT0 + 4 * szVO;           //  O, 2 slots
+    static constexpr size_t bytes = OT0 + 2 * szVO;
+    static_assert(bytes <= 160 * 1024, "LDS budget");
+    static_assert(bytes % 16 == 0, "16-byte initialisation");
+};
+
+// Ring slot of chunk c0 + 4j + K + OFF for a loop that starts at c0 = -3.
+template <int K, int OFF>
+constexpr int slot4() { return (K + OFF + 1) & 3; }
+template <int K, int OFF>
+constexpr int slot2() { return (K + OFF + 1) & 1; }
+
+template <int NSW>
+__global__ __launch_bounds__((Ws2Cfg<NSW>::NT)) void chunk_ws2_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ log_alpha, const bf16* __restrict__ beta,
+    const float* __restrict__ h0, const int32_t* __restrict__ cu_seqlens, int64_t T_total,
+    int32_t H, int32_t split, int32_t units, bf16* __restrict__ o, float* __restrict__ h_T,
+    int32_t flags) {
+    typedef Ws2Cfg<NSW> K;
+    constexpr int KP = K::KP, TP = K::TP, AP = K::AP, DV = K::DV, VP = K::VP;
+
+    // XCD-aware id: the column slices of one (sequence, head) share the
+    // id's residue mod 8, i.e. one XCD and its L2
+    const int x = blockIdx.x;
+    const int xcd = x % kXcd2;
+    const int qd = x / kXcd2;
+    const int slice = qd % split;
+    const int unit = (qd / split) * kXcd2 + xcd;
+    if (unit >= units) return;
+    const int n = unit / H;
+    const int h = unit % H;
+
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    auto kn_s = [&](int s) { return reinterpret_cast<bf16*>(smem + K::KN0 + s * K::szTok); };
+    auto qs_s = [&](int s) { return reinterpret_cast<bf16*>(smem + K::QS0 + s * K::szTok); };
+    auto kv_s = [&](int s) { return reinterpret_cast<bf16*>(smem + K::KV0 + s * K::szTok); };
+    auto kh_s = [&](int s) { return reinterpret_cast<bf16*>(smem + K::KH0 + s * K::szTok); };
+    auto gam_s = [&](int s) { return reinterpret_cast<float*>(smem + K::GAM0 + s * 512); };
+    auto beta_s = [&](int s) { return reinterpret_cast<float*>(smem + K::BETA0 + s * 64); };
+    auto a_s = [&](int s) { return reinterpret_cast<float*>(smem + K::A0 + s * K::szA); };
+    auto p_s = [&](int s) { return reinterpret_cast<bf16*>(smem + K::P0 + s * K::szTile); };
+    auto t_s = [&](int s) { return reinterpret_cast<bf16*>(smem + K::T0 + s * K::szTile); };
+    auto vt_s = [&](int s) { return reinterpret_cast<bf16*>(smem + K::VT0 + s * K::szVO); };
+    auto ot_s = [&](int s) { return reinterpret_cast<bf16*>(smem + K::OT0 + s * K::szVO); };
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15;
+    const int g = lane >> 4;
+
+    const int64_t bos = cu_seqlens ? (int64_t)cu_seqlens[n] : 0;
+    const int64_t eos = cu_seqlens ? (int64_t)cu_seqlens[n + 1] : T_total;
+    const int64_t seqlen = eos - bos;
+    const int nch = (int)((seqlen + kC2 - 1) / kC2);
+    const size_t rowstride = (size_t)H * kHeadDim;
+    const size_t headoff = (size_t)h * kHeadDim;
+    const int col0 = slice * DV;
+    // iterations c = -3 .. nch (the last one stores the outputs of chunk
+    // nch - 1), rounded up to whole trips of four
+    const int trips = (nch + 4 + 3) / 4;
+
+    if (nch == 0) {   // empty sequence: h_T = h0 (or zero / identity)
+        if (wave < NSW && h_T) {
+            const float* src = h0 ? h0 + ((size_t)n * (size_t)H + h) * (kHeadDim * kHeadDim) : nullptr;
+            const bool ident = flags & kChunkH0Identity;
+            float* dst = h_T + ((size_t)n * (size_t)H + h) * (kHeadDim * kHeadDim);
+            const int j = col0 + 16 * wave + l16;
+#pragma unroll
+            for (int it = 0; it < 8; ++it)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int row = 16 * it + 4 * g + e;
+                    const int idx = row * kHeadDim + j;
+                    dst[idx] = src ? src[idx] : (ident && row == j ? 1.f : 0.f);
+                }
+        }
+        return;
+    }
+
+    // The rings start out holding the identity chunk: zeros, Gamma = 1.
+    {
+        typedef unsigned int uintx4_t __attribute__((ext_vector_type(4)));
+        for (size_t b = (size_t)tid * 16; b < K::bytes; b += (size_t)K::NT * 16)
+            *reinterpret_cast<uintx4_t*>(smem + b) = uintx4_t{0u, 0u, 0u, 0u};
+        __syncthreads();
+        for (int i = tid; i < 4 * kHeadDim; i += K::NT) gam_s(0)[i] = 1.f;
+        __syncthreads();
+    }
+
+    if (wave < NSW) {
+        // ======================= state waves =======================
+        floatx4 S[8];
+        {
+            const float* src = h0 ? h0 + ((size_t)n * (size_t)H + h) * (kHeadDim * kHeadDim) : nullptr;
+            const int j = col0 + 16 * wave + l16;
+#pragma unroll
+            for (int it = 0; it < 8; ++it)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    S[it][e] = src ? src[(16 * it + 4 * g + e) * kHeadDim + j] : 0.f;
+            if (!src && (flags & kChunkH0Identity)) {
+#pragma unroll
+                for (int it = 0; it < 8; ++it)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (16 * it + 4 * g + e == j) S[it][e] = 1.f;
+            }
+        }
+        const bool write_o = !(flags & kChunkNoOutput);
+        const bool v_zero = flags & kChunkVZero;
+        const bf16 z = (bf16)0.f;
+
+        auto state_iter = [&](auto kc) {
+            constexpr int KK = decltype(kc)::value;
+            constexpr int sc = slot4<KK, 0>();      // chunk c
+            constexpr int sc2 = slot2<KK, 0>();
+            const bf16* Kn = kn_s(sc) + l16 * KP;
+            const bf16* Qs = qs_s(sc) + l16 * KP;
+            floatx4 X, Ov = zero4();
+            if (v_zero) {
+                X = zero4();
+            } else {
+                const bf16x4 v4 = lds_col4(vt_s(sc) + 4 * g * VP + 16 * wave, VP, l16);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) X[e] = (float)v4[e];
+            }
+            // X = V - Ktil S, O = Qtil S
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const bf16x8 sb = acc_frag_k32(S[2 * b], S[2 * b + 1]);
+                X = mma_bf16_k32(frag_k32(Kn, 32 * b, g), sb, X);
+                Ov = mma_bf16_k32(frag_k32(Qs, 32 * b, g), sb, Ov);
+            }
+            // U = T X, O += P U (as the k = 32 product with a zero upper half,
+            // the same opcode as the Qtil S chain on this accumulator)
+            const bf16x4 at = frag_k16(t_s(sc2) + l16 * TP, 0, g);
+            const bf16x4 ap = frag_k16(p_s(sc) + l16 * TP, 0, g);
+            const floatx4 U = mma_bf16_k16(at, acc_frag_k16(X), zero4());
+            const bf16x4 ub = acc_frag_k16(U);
+            Ov = mma_bf16_k32(bf16x8{ap[0], ap[1], ap[2], ap[3], z, z, z, z},
+                              bf16x8{ub[0], ub[1], ub[2], ub[3], z, z, z, z}, Ov);
+            if (write_o) {
+                bf16* ot = ot_s(sc2) + 16 * wave + l16;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ot[(4 * g + e) * VP] = (bf16)Ov[e];
+            }
+            // S <- Diag(Gamma) S + Kvec^T U
+            const float* Gm = gam_s(sc);
+            const bf16* Kv = kv_s(sc);
+#pragma unroll
+            for (int it = 0; it < 8; ++it) {
+                const floatx4 gm = *reinterpret_cast<const floatx4*>(Gm + 16 * it + 4 * g);
+                const bf16x4 a = lds_col4(Kv + 4 * g * KP + 16 * it, KP, l16);
+                S[it] = mma_bf16_k16(a, ub, S[it] * gm);
+            }
+            // Gram tiles of chunk c+2: wave 0 A (stored negated), wave 1 P
+            if (wave < 2) {
+                constexpr int sg = slot4<KK, 2>();
+                constexpr int sgh = slot2<KK, 2>();
+                const bool isP = wave == 1;
+                const bf16* arow = kh_s(sgh) + l16 * KP;
+                const bf16* brow = (isP ? qs_s(sg) : kn_s(sg)) + l16 * KP;
+                floatx4 acc = zero4();
+#pragma unroll
+                for (int kb = 0; kb < kHeadDim; kb += 32)
+                    acc = mma_bf16_k32(frag_k32(arow, kb, g), frag_k32(brow, kb, g), acc);
+                if (!isP) {
+                    const float br = beta_s(sg)[l16];
+                    floatx4 out;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) out[e] = (4 * g + e >= l16) ? 0.f : acc[e] * br;
+                    *reinterpret_cast<floatx4*>(a_s(sgh) + l16 * AP + 4 * g) = out;
+                } else {
+                    bf16x4 out;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) out[e] = (bf16)((4 * g + e > l16) ? 0.f : acc[e]);
+                    *reinterpret_cast<bf16x4*>(p_s(sg) + l16 * TP + 4 * g) = out;
+                }
+            }
+            __syncthreads();
+        };
+        for (int t = 0; t < trips; ++t) {
+            state_iter(std::integral_constant<int, 0>{});
+            state_iter(std::integral_constant<int, 1>{});
+            state_iter(std::integral_constant<int, 2>{});
+            state_iter(std::integral_constant<int, 3>{});
+        }
+        if (h_T) {
+            float* dst = h_T + ((size_t)n * (size_t)H + h) * (kHeadDim * kHeadDim);
+            const int j = col0 + 16 * wave + l16;
+#pragma unroll
+            for (int it = 0; it < 8; ++it)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dst[(16 * it + 4 * g + e) * kHeadDim + j] = S[it][e];
+        }
+        return;
+    }
+
+    // ========================= prep waves =========================
+    const int pw = wave - NSW;          // 0..7
+    const int r = l16;                  // token of the chunk
+    const int ch0 = 16 * pw + 4 * g;    // first of this lane's 4 key channels
+    bf16x4 rq[4], rk[4], rg[4];
+    bf16 rb[4];
+    bf16x8 rv[4];
+    static_assert(DV / 32 <= 4, "V / O waves are prep waves 0..3");
+    const bool io_wave = pw >= 4 - DV / 32 && pw < 4;
+    const int io_u = (pw - (4 - DV / 32)) * 64 + lane;
+    const int io_row = io_u / (DV / 8), io_col = (io_u % (DV / 8)) * 8;
+    const uint32_t io_off = (uint32_t)(((size_t)io_row * rowstride + headoff + col0 + io_col) * 2);
+    const bool write_o = !(flags & kChunkNoOutput);
+    // chunk y starts y * cstride elements after the sequence's first row and
+    // has chunk_rows(y) rows inside it (0 before the start or past the end)
+    const size_t cstride = (size_t)kC2 * rowstride;
+    const uint32_t last_rows = (uint32_t)(seqlen - (int64_t)kC2 * (nch - 1));
+    auto chunk_rows = [&](int y) -> uint32_t {
+        return (y < 0 || y >= nch) ? 0u : (y < nch - 1 ? (uint32_t)kC2 : last_rows);
+    };
+    const uint32_t row_bytes = (uint32_t)(rowstride * 2);
+    const size_t seq0 = (size_t)bos * rowstride;
+    const bf16 *q_seq = q + seq0, *k_seq = k + seq0, *g_seq = log_alpha + seq0, *v_seq = v + seq0;
+    bf16* o_seq = o + seq0;
+    const bf16* b_seq = beta + (size_t)bos * H;
+    const bool q_none = flags & kChunkNoOutput, v_none = flags & kChunkVZero;
+    const uint32_t qo_lane = (uint32_t)(((size_t)r * rowstride + headoff + ch0) * 2);
+    const uint32_t bo_lane = (uint32_t)(((size_t)r * H + h) * 2);
+    auto load_chunk = [&](auto slot_c, int yc) {
+        constexpr int s = decltype(slot_c)::value;
+        // (a chunk index below zero gives an empty resource: no address is formed)
+        const size_t off = yc > 0 ? (size_t)yc * cstride : 0;
+        const uint32_t rows = chunk_rows(yc), bytes = rows * row_bytes;
+        rq[s] = buf_load_bf16x4(make_rsrc_u32(q_seq + off, q_none ? 0u : bytes), qo_lane);
+        rk[s] = buf_load_bf16x4(make_rsrc_u32(k_seq + off, bytes), qo_lane);
+        rg[s] = buf_load_bf16x4(make_rsrc_u32(g_seq + off, bytes), qo_lane);
+        rb[s] = buf_load_bf16(make_rsrc_u32(b_seq + (yc > 0 ? (size_t)yc * kC2 * H : 0),
+                                            rows * (uint32_t)H * 2),
+                              bo_lane);
+        if (io_wave)
+            rv[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   make_rsrc_u32(v_seq + off, v_none ? 0u : bytes),
+                                                   (int)io_off, 0, 0));
+    };
+    load_chunk(std::integral_constant<int, 0>{}, 0);
+    load_chunk(std::integral_constant<int, 1>{}, 1);
+    load_chunk(std::integral_constant<int, 2>{}, 2);
+    load_chunk(std::integral_constant<int, 3>{}, 3);
+
+    auto prep_iter = [&](auto kc, int c) {
+        constexpr int KK = decltype(kc)::value;   // register slot of chunk c+3 = KK
+        constexpr int s3 = slot4<KK, 3>();
+        constexpr int s3h = slot2<KK, 3>();
+        // (1) decay factors and scaled operands of chunk c+3
+        {
+            float kf[4], qf[4], lg[4];
+            const float bt = (float)rb[KK];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                kf[e] = (float)rk[KK][e];
+                qf[e] = (float)rq[KK][e];
+                lg[e] = (float)rg[KK][e] * kLog2e2;
+            }
+            bf16x4 kn, qs, kh, kv;
+            floatx4 gam;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float Pr = row_prefix_sum(lg[e]);           // G_r / ln 2
+                const float E = __builtin_amdgcn_exp2f(Pr);       // exp(G_r)       <= 1
+                const float Einv = __builtin_amdgcn_exp2f(-Pr);   // exp(-G_r)      <= e^80
+                gam[e] = row_bcast<15>(E);                        // exp(G_C)
+                const float Hs = gam[e] * Einv;                   // exp(G_C - G_r) <= 1
+                kn[e] = (bf16)(-kf[e] * E);
+                qs[e] = (bf16)(qf[e] * E);
+                kh[e] = (bf16)(kf[e] * Einv);
+                kv[e] = (bf16)(kf[e] * Hs);
+            }
+            *reinterpret_cast<bf16x4*>(kv_s(s3) + r * KP + ch0) = kv;
+            *reinterpret_cast<bf16x4*>(kn_s(s3) + r * KP + ch0) = kn;
+            *reinterpret_cast<bf16x4*>(qs_s(s3) + r * KP + ch0) = qs;
+            *reinterpret_cast<bf16x4*>(kh_s(s3h) + r * KP + ch0) = kh;
+            if (r == 0) *reinterpret_cast<floatx4*>(gam_s(s3) + ch0) = gam;
+            if (pw == 0 && g == 0) beta_s(s3)[r] = bt;
+            if (io_wave) *reinterpret_cast<bf16x8*>(vt_s(s3) + io_row * VP + io_col) = rv[KK];
+        }
+        // (2) O of chunk c-1 out of its tile (dropped outside the sequence)
+        if (io_wave && write_o) {
+            constexpr int so = slot2<KK, -1>();
+            const int y = c - 1;
+            buf_store_b128(*reinterpret_cast<const bf16x8*>(ot_s(so) + io_row * VP + io_col),
+                           make_rsrc_u32(o_seq + (y > 0 ? (size_t)y * cstride : 0),
+                                         chunk_rows(y) * row_bytes),
+                           io_off, 0);
+        }
+        // loads of chunk c+7 into this register slot
+        load_chunk(kc, c + 7);
+        // (3) UT transform of chunk c+1 on prep waves 0-3: lane = element
+        // (row l16, column 4 pw + g) of (I + A)^{-1}, forward elimination with
+        // the pivot broadcast along the row of 16 lanes
+        if (pw < 4) {
+            constexpr int s1 = slot4<KK, 1>();
+            constexpr int s1h = slot2<KK, 1>();
+            const float* Arow = a_s(s1h) + l16 * AP;
+            float a[16];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const floatx4 v4 = *reinterpret_cast<const floatx4*>(Arow + 4 * q4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a[4 * q4 + e] = v4[e];
+            }
+            const int col = 4 * pw + g;
+            float xv = (l16 == col) ? 1.f : 0.f;
+            xv += row_bcast<0>(xv) * a[0];
+            xv += row_bcast<1>(xv) * a[1];
+            xv += row_bcast<2>(xv) * a[2];
+            xv += row_bcast<3>(xv) * a[3];
+            xv += row_bcast<4>(xv) * a[4];
+            xv += row_bcast<5>(xv) * a[5];
+            xv += row_bcast<6>(xv) * a[6];
+            xv += row_bcast<7>(xv) * a[7];
+            xv += row_bcast<8>(xv) * a[8];
+            xv += row_bcast<9>(xv) * a[9];
+            xv += row_bcast<10>(xv) * a[10];
+            xv += row_bcast<11>(xv) * a[11];
+            xv += row_bcast<12>(xv) * a[12];
+            xv += row_bcast<13>(xv) * a[13];
+            xv += row_bcast<14>(xv) * a[14];
+            t_s(s1h)[l16 * TP + col] = (bf16)(xv * beta_s(s1)[col]);
+        }
+        __syncthreads();
+    };
+    int c = -3;
+    for (int t = 0; t < trips; ++t, c += 4) {
+        prep_iter(std::integral_constant<int, 0>{}, c);
+        prep_iter(std::integral_constant<int, 1>{}, c + 1);
+        prep_iter(std::integral_constant<int, 2>{}, c + 2);
+        prep_iter(std::integral_constant<int, 3>{}, c + 3);
+    }
+}
+
+template <int NSW>
+hipError_t launch_ws2_t(const ChunkArgs& a, hipStream_t stream) {
+    typedef Ws2Cfg<NSW> K;
+    const int split = kHeadDim / K::DV;
+    auto kern = chunk_ws2_kernel<NSW>;
+    static std::atomic<uint64_t> lds_set{0};
+    hipError_t e = raise_lds_limit_once((const void*)kern, (int)K::bytes, lds_set);
+    if (e != hipSuccess) return e;
+    const int64_t units = (int64_t)a.N * a.H;
+    if (units == 0) return hipSuccess;
+    const int64_t nwg = (units + kXcd2 - 1) / kXcd2 * kXcd2 * split;
+    kern<<<dim3((unsigned)nwg), dim3(K::NT), K::bytes, stream>>>(
+        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.log_alpha,
+        (const bf16*)a.beta, a.h0, a.cu_seqlens, a.T_total, a.H, split, (int32_t)units,
+        (bf16*)a.o, a.h_T, a.flags);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool chunk_ws2_supports(const ChunkArgs& a, int split) {
+    return split == 2 && !a.snap.snap && !(a.flags & (kChunkDualBM | kChunkSnapBf16 | kChunkSnapSlots));
+}
+
+hipError_t launch_chunk_ws2(const ChunkArgs& a, int split, hipStream_t stream) {
+    if (!chunk_ws2_supports(a, split)) return hipErrorInvalidValue;
+    return launch_ws2_t<4>(a, stream);
+}
+
+}  // namespace kda

@@ -142,6 +142,10 @@ inline void chunk_default_config(int dtype, int64_t T_total, int32_t N, int32_t 
     }
 }
 hipError_t launch_chunk_ws(const ChunkArgs& a, int split, hipStream_t stream);
+// the plain bf16 prefill at split 2 (no snapshots, no paired summaries), with
+// compile-time ring slots and no per-stage range checks (kda_chunk_ws2.hip)
+bool chunk_ws2_supports(const ChunkArgs& a, int split);
+hipError_t launch_chunk_ws2(const ChunkArgs& a, int split, hipStream_t stream);
 hipError_t launch_chunk(const ChunkArgs& a, int dtype, int chunk, int split,
                         hipStream_t stream);
 
