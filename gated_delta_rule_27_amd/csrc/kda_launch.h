@@ -121,8 +121,9 @@ struct DecodeMultiArgs {
 // dtype: 0 = fp32, 1 = bf16 (kda_dtype values).
 // chunk in {16, 32}; split = workgroups per head (value-column slices).
 // bf16 with chunk 16 and split 1 or 2 runs the wave-specialised pipelined
-// kernel (kda_chunk_ws.hip); every other combination runs the phase-serial
-// kernel (kda_chunk.hip).
+// kernels (kda_chunk_ws.hip, kda_chunk_ws2.hip), bf16 with chunk 32 and split
+// 2 the pipelined 32-token kernel (kda_chunk_ws3.hip); every other
+// combination runs the phase-serial kernel (kda_chunk.hip).
 // (host-only choices, inline so that the C ABI's validation builds without
 // the kernels, e.g. for the host sanitizer tests)
 inline bool chunk_config_supported(int dtype, int chunk, int split) {
@@ -146,6 +147,10 @@ hipError_t launch_chunk_ws(const ChunkArgs& a, int split, hipStream_t stream);
 // compile-time ring slots and no per-stage range checks (kda_chunk_ws2.hip)
 bool chunk_ws2_supports(const ChunkArgs& a, int split);
 hipError_t launch_chunk_ws2(const ChunkArgs& a, int split, hipStream_t stream);
+// the same cases with 32-token chunks of two 16-token sub-tiles
+// (kda_chunk_ws3.hip)
+bool chunk_ws3_supports(const ChunkArgs& a, int split);
+hipError_t launch_chunk_ws3(const ChunkArgs& a, int split, hipStream_t stream);
 hipError_t launch_chunk(const ChunkArgs& a, int dtype, int chunk, int split,
                         hipStream_t stream);
 

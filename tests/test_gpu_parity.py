@@ -39,6 +39,10 @@ SMALL = [
     # (Gram tiles over two iterations), with empty and sub-chunk sequences
     ("bf16", [4000, 0, 1, 15, 16, 17], 2, 0.3, 16, 1),
     ("bf16", [4000, 0, 1, 15, 16, 17], 2, 0.3, 16, 2),
+    # the pipelined 32-token kernel (two 16-token sub-tiles): sequences
+    # ending in either sub-tile, and shorter than one sub-tile
+    ("bf16", [4000, 0, 1, 15, 16, 17], 2, 0.3, 32, 2),
+    ("bf16", [33, 47, 48, 63, 64, 65], 3, 0.3, 32, 2),
 ]
 
 
@@ -62,6 +66,7 @@ PER_CHUNK = [
     ("bf16", 16, 1, 160), ("bf16", 16, 2, 160), ("bf16", 32, 1, 160), ("bf16", 32, 4, 160),
     ("f32", 16, 1, 160), ("f32", 16, 2, 160), ("f32", 32, 4, 160),
     ("bf16", 16, 1, 640), ("bf16", 16, 2, 640),
+    ("bf16", 32, 2, 160), ("bf16", 32, 2, 640),
 ]
 
 
@@ -110,14 +115,16 @@ def test_workload_tiny_prefill():
 
 
 def test_workload_prefill_4k():
-    """Single-sequence K3-shape prefill, T=4096, H=96, bf16: every head."""
+    """Single-sequence K3-shape prefill, T=4096, H=96, bf16: every head, in
+    the default launch and with 32-token chunks."""
     kda = need_gpu()
-    case("workload prefill_T4096_H96_bf16 (default launch)")
     d = kda_inputs.config_inputs(1, device="cuda")
-    o, hT = gpu_prefill(kda, d)
     ro, rh = oracle_prefill(d)
-    check("o", np_(o), ro, TOL["bf16"])
-    check("h_T", np_(hT), rh, TOL["bf16"])
+    for chunk in (0, 32):
+        case(f"workload prefill_T4096_H96_bf16 chunk={chunk or 'default'}")
+        o, hT = gpu_prefill(kda, d, chunk)
+        check("o", np_(o), ro, TOL["bf16"])
+        check("h_T", np_(hT), rh, TOL["bf16"])
 
 
 def test_workload_decode_batch256():

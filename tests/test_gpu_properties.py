@@ -28,9 +28,11 @@ def test_chunk_and_split_invariance(dtype):
             check("h_T", np_(hT), rh, TOL[dtype])
             outs[(c, s)] = (np_(o), np_(hT))
     # within one kernel the column split changes no arithmetic: same bits.
-    # (bf16 with chunk 16 and split <= 2 runs the pipelined kernel, the other
-    # combinations the phase-serial one.)
-    same = [[(16, 1), (16, 2)], [(32, 1), (32, 2), (32, 4)]]
+    # (bf16 with chunk 16 and split <= 2 runs the pipelined 16-token kernels,
+    # chunk 32 with split 2 the pipelined 32-token kernel, whose sub-tile
+    # factorisation rounds differently; the other combinations run the
+    # phase-serial kernel.)
+    same = [[(16, 1), (16, 2)], [(32, 1), (32, 4)]]
     if dtype == "f32":
         same = [[(16, 1), (16, 2), (16, 4)], [(32, 1), (32, 2), (32, 4)]]
     for group in same:
