@@ -593,7 +593,9 @@ kda_status kda_prologue(const void* xq, const void* xk, const void* xv, const vo
     a.beta = beta;
     a.tb = kda::prologue_tokens_per_wave(T_total, H);
     a.n_tblocks = (int32_t)((T_total + a.tb - 1) / a.tb);
-    if ((uint64_t)a.n_tblocks * (uint64_t)((H + 3) / 4) * 4u + (uint64_t)N >
+    // (the prologue's grid: four waves per workgroup)
+    if ((uint64_t)(kda::prologue_conv_waves(a.n_tblocks, H, N) +
+                   kda::prologue_gate_waves(a.n_tblocks, H)) >
         (uint64_t)std::numeric_limits<int32_t>::max() * 4u)
         return KDA_ERR_BAD_SHAPE;
     if (T_total == 0 && !conv_state_out) return KDA_OK;

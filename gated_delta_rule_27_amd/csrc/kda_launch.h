@@ -233,6 +233,15 @@ inline int32_t prologue_tokens_per_wave(int64_t T_total, int32_t H) {
     while (tb > kPrologueLookahead && 4 * nslice * ((T_total + tb - 1) / tb) < 8192) tb /= 2;
     return tb;
 }
+// Waves of the prologue's convolution kernel: q, k, v x token blocks x
+// two-head slices, plus one per sequence for the history of empty ones.
+inline int64_t prologue_conv_waves(int64_t n_tblocks, int32_t H, int64_t n_hist) {
+    return 3 * n_tblocks * (int64_t)((H + 1) / 2) + n_hist;
+}
+// Waves of its gate part: token blocks x four-head slices.
+inline int64_t prologue_gate_waves(int64_t n_tblocks, int32_t H) {
+    return n_tblocks * (int64_t)((H + 3) / 4);
+}
 hipError_t launch_prologue(const PrologueArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_epilogue(const EpilogueArgs& a, int dtype, hipStream_t stream);
 

@@ -12,17 +12,20 @@
 // Epilogue ("A third gate: control what leaves the module"; "Inside a KDA
 // Layer"): y = RMSNorm_head(o) * w * sigmoid(g).
 //
-// Both are HBM-bound streams (a few flops per byte).  Mapping of the
-// prologue: one wave per (tensor, 512-channel slice of a token row = 4
-// heads, block of consecutive tokens).  Lane l holds channels 8 (l % 16) ..
-// +7 of head 4 slice + l / 16, so every wave-wide load is 1 KiB contiguous
+// Both are HBM-bound streams (a few flops per byte): what sets their speed
+// is the number of bytes each CU keeps in flight, so the kernels are shaped
+// for registers (occupancy) and long load runs.  Convolution kernel: one
+// wave per (tensor q / k / v, 256-channel slice of a token row = 2 heads,
+// block of consecutive tokens).  Lane l holds channels 4 (l % 32) .. +3 of
+// head 2 slice + l / 32, so every wave-wide load is 512 contiguous bytes
 // (bf16) and all 64 lanes sit at the same token: the sequence bookkeeping of
 // a packed batch (where a sequence starts, where it ends) is wave-uniform
 // scalar work.  Each lane walks its token block in order, keeping the last
-// three inputs in registers (the convolution window), so every input is
-// loaded once, plus three rows of history per block.  The L2 norm of a head
-// is a 16-lane butterfly.  The epilogue maps one 16-lane group per (token,
-// head) row in the same way.
+// three inputs in registers (the convolution window), with 16 tokens of
+// loads in flight, so every input is loaded once, plus three rows of history
+// per block.  The L2 norm of a head is a 32-lane butterfly.  Gate kernel
+// (decay and write gates): one wave per 4 heads of a token block, lane =
+// 8 channels.  The epilogue maps one 16-lane group per (token, head) row.
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -59,6 +62,46 @@ __device__ __forceinline__ void store8(bf16* p, const float (&x)[8]) {
     *reinterpret_cast<bf16x8*>(p) = a;
 }
 
+__device__ __forceinline__ void load4(const float* p, float (&x)[4]) {
+    const floatx4 a = *reinterpret_cast<const floatx4*>(p);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = a[e];
+}
+__device__ __forceinline__ void load4(const bf16* p, float (&x)[4]) {
+    const bf16x4 a = *reinterpret_cast<const bf16x4*>(p);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = (float)a[e];
+}
+__device__ __forceinline__ void store4(float* p, const float (&x)[4]) {
+    *reinterpret_cast<floatx4*>(p) = floatx4{x[0], x[1], x[2], x[3]};
+}
+__device__ __forceinline__ void store4(bf16* p, const float (&x)[4]) {
+    bf16x4 a;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a[e] = (bf16)x[e];  // RNE
+    *reinterpret_cast<bf16x4*>(p) = a;
+}
+
+// 4 consecutive elements as loaded (kept packed until used, so a lane can
+// hold many tokens in flight in few registers)
+template <typename T>
+struct Raw4;
+template <>
+struct Raw4<bf16> {
+    bf16x4 v;
+    __device__ __forceinline__ void load(const bf16* p) { v = *reinterpret_cast<const bf16x4*>(p); }
+    __device__ __forceinline__ float operator[](int e) const { return (float)v[e]; }
+};
+template <>
+struct Raw4<float> {
+    floatx4 v;
+    __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const floatx4*>(p); }
+    __device__ __forceinline__ float operator[](int e) const { return v[e]; }
+};
+// tokens of loads in flight per lane of the convolution kernel
+template <typename T>
+constexpr int conv_lookahead() { return sizeof(T) == 2 ? 16 : 8; }
+
 // 8 consecutive elements as loaded (kept packed until used, so a lane can
 // hold many tokens in flight in few registers)
 template <typename T>
@@ -84,26 +127,162 @@ __device__ __forceinline__ float sigmoid(float z) {
     return __builtin_amdgcn_rcpf(1.f + __expf(-z));
 }
 
-// sum over the 16 lanes of a lane's row (lanes 16r .. 16r + 15)
+// sum over the 16 lanes of a lane's row (lanes 16r .. 16r + 15), in every
+// lane of the row: a DPP prefix sum, then lane 15 broadcast along the row
 __device__ __forceinline__ float row16_sum(float s) {
-    s += __shfl_xor(s, 8, 16);
-    s += __shfl_xor(s, 4, 16);
-    s += __shfl_xor(s, 2, 16);
-    s += __shfl_xor(s, 1, 16);
-    return s;
+    s += row_shr0<1>(s);
+    s += row_shr0<2>(s);
+    s += row_shr0<4>(s);
+    s += row_shr0<8>(s);
+    return row_bcast<15>(s);
 }
 
+// sum over the 32 lanes of a lane's half-wave: the two row sums, exchanged
+// between the rows of the half by a swizzle (swap groups of 16 lanes)
+__device__ __forceinline__ float row32_sum(float s) {
+    s = row16_sum(s);
+    return s + __builtin_bit_cast(float,
+                                  __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, s), 0x401f));
+}
+
+// raw loads and stores of 4 / 8 elements through a buffer resource (32-bit
+// offsets; out-of-range loads read 0 and out-of-range stores are dropped)
+__device__ __forceinline__ Raw4<bf16> buf_raw4(rsrc_t r, uint32_t off, const bf16*) {
+    Raw4<bf16> x;
+    x.v = buf_load_bf16x4(r, off);
+    return x;
+}
+__device__ __forceinline__ Raw4<float> buf_raw4(rsrc_t r, uint32_t off, const float*) {
+    Raw4<float> x;
+    x.v = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+    return x;
+}
+__device__ __forceinline__ Raw8<bf16> buf_raw8(rsrc_t r, uint32_t off, const bf16*) {
+    Raw8<bf16> x;
+    x.v = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+    return x;
+}
+__device__ __forceinline__ Raw8<float> buf_raw8(rsrc_t r, uint32_t off, const float*) {
+    Raw8<float> x;
+    x.a = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+    x.b = __builtin_bit_cast(floatx4,
+                             __builtin_amdgcn_raw_buffer_load_b128(r, (int)off + 16, 0, 0));
+    return x;
+}
+__device__ __forceinline__ bf16 buf_elem(rsrc_t r, uint32_t off, const bf16*) {
+    return buf_load_bf16(r, off);
+}
+__device__ __forceinline__ float buf_elem(rsrc_t r, uint32_t off, const float*) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ void buf_store_elem(rsrc_t r, uint32_t off, float x, bf16*) {
+    buf_store_bf16((bf16)x, r, off);
+}
+__device__ __forceinline__ void buf_store_elem(rsrc_t r, uint32_t off, float x, float*) {
+    buf_store_f32(x, r, off, 0);
+}
+__device__ __forceinline__ void buf_store8(rsrc_t r, uint32_t off, const float (&x)[8], bf16*) {
+    bf16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (bf16)x[e];  // RNE
+    buf_store_b128(v, r, off, 0);
+}
+__device__ __forceinline__ void buf_store8(rsrc_t r, uint32_t off, const float (&x)[8], float*) {
+    typedef unsigned int uintx4_t __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(
+        __builtin_bit_cast(uintx4_t, floatx4{x[0], x[1], x[2], x[3]}), r, (int)off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(
+        __builtin_bit_cast(uintx4_t, floatx4{x[4], x[5], x[6], x[7]}), r, (int)off + 16, 0, 0);
+}
+__device__ __forceinline__ void buf_store4(rsrc_t r, uint32_t off, const float (&x)[4], bf16*) {
+    bf16x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (bf16)x[e];  // RNE
+    buf_store_bf16x4(v, r, off, 0);
+}
+__device__ __forceinline__ void buf_store4(rsrc_t r, uint32_t off, const float (&x)[4], float*) {
+    typedef unsigned int uintx4_t __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(
+        __builtin_bit_cast(uintx4_t, floatx4{x[0], x[1], x[2], x[3]}), r, (int)off, 0, 0);
+}
+
+// log alpha = -5 sigmoid(a + bias) and beta = sigmoid(b)
 template <typename TIn>
-__global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t wid = (int64_t)blockIdx.x * 4 + wave;
+__device__ __forceinline__ void prologue_gate(const PrologueArgs& a, int64_t wid, int lane) {
     const int HD = a.H * kHeadDim;
     const int nslice = (a.H + 3) / 4;
+    if (wid >= (int64_t)a.n_tblocks * nslice) return;
+    const int64_t tblock = wid / nslice;
+    const int slice = (int)(wid % nslice);
+    const int row = lane >> 4;
+    const int h = 4 * slice + row;
+    const int c8 = 8 * (lane & 15);
+    const bool live = h < a.H;
+    const int hc = live ? h * kHeadDim + c8 : c8;           // channel offset in a token row
+    const int64_t t0 = tblock * a.tb;
+    const int64_t t1 = t0 + a.tb < a.T_total ? t0 + a.tb : a.T_total;
+    const TIn* x = static_cast<const TIn*>(a.x[3]);
+    TIn* out = static_cast<TIn*>(a.out[3]);
+    float bias[8];
+    {
+        const floatx4 b0 = *reinterpret_cast<const floatx4*>(a.a_bias + hc);
+        const floatx4 b1 = *reinterpret_cast<const floatx4*>(a.a_bias + hc + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            bias[e] = b0[e];
+            bias[4 + e] = b1[e];
+        }
+    }
+    // the block's rows as buffer resources (32-bit offsets; lanes past the
+    // last head read 0 and their stores are dropped)
+    const uint32_t es = (uint32_t)sizeof(TIn);
+    const uint32_t blk_bytes = (uint32_t)((t1 - t0) * HD) * es;
+    const rsrc_t xr = make_rsrc_u32(x + (size_t)t0 * HD, blk_bytes);
+    const rsrc_t outr = make_rsrc_u32(out + (size_t)t0 * HD, blk_bytes);
+    const uint32_t lane_off = live ? (uint32_t)hc * es : 0x80000000u;
+    const uint32_t row_b = (uint32_t)HD * es;
+    const TIn* braw = static_cast<const TIn*>(a.b_raw);
+    TIn* beta = static_cast<TIn*>(a.beta);
+    const uint32_t bblk = (uint32_t)((t1 - t0) * a.H) * es;
+    const rsrc_t br = make_rsrc_u32(braw + (size_t)t0 * a.H, bblk);
+    const rsrc_t bw = make_rsrc_u32(beta + (size_t)t0 * a.H, bblk);
+    // one lane per head writes beta; the others point past the end
+    const uint32_t blane_off = (live && c8 == 0) ? (uint32_t)h * es : 0x80000000u;
+    const uint32_t brow_b = (uint32_t)a.H * es;
+    for (int64_t tb = t0; tb < t1; tb += kPU) {
+        Raw8<TIn> xv[kPU];
+        TIn bv[kPU];
+        const uint32_t to = (uint32_t)(tb - t0);
+#pragma unroll
+        for (int u = 0; u < kPU; ++u) {
+            xv[u] = buf_raw8(xr, lane_off + (to + u) * row_b, (const TIn*)nullptr);
+            bv[u] = buf_elem(br, blane_off + (to + u) * brow_b, (const TIn*)nullptr);
+        }
+#pragma unroll
+        for (int u = 0; u < kPU; ++u) {
+            float y[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = -5.f * sigmoid(xv[u][e] + bias[e]);
+            buf_store8(outr, lane_off + (to + u) * row_b, y, (TIn*)nullptr);
+            buf_store_elem(bw, blane_off + (to + u) * brow_b, sigmoid(to_f32(bv[u])),
+                           (TIn*)nullptr);
+            // one token's arithmetic live at a time (the loads stay in flight)
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+// q, k, v: short convolution, Swish, L2 norm (q, k); conv history
+template <typename TIn>
+__device__ __forceinline__ void prologue_conv(const PrologueArgs& a, int64_t wid, int lane) {
+    constexpr int kLA = conv_lookahead<TIn>();
+    const int HD = a.H * kHeadDim;
+    const int nslice = (a.H + 1) / 2;
     const int64_t per_tensor = (int64_t)a.n_tblocks * nslice;
 
-    if (wid >= 4 * per_tensor) {
+    if (wid >= 3 * per_tensor) {
         // ---- history of empty sequences: carried over (or zero) ----
-        const int64_t n = wid - 4 * per_tensor;
+        const int64_t n = wid - 3 * per_tensor;
         if (n >= a.N || !a.state_out) return;
         const int64_t bos = a.cu_seqlens ? a.cu_seqlens[n] : 0;
         const int64_t eos = a.cu_seqlens ? a.cu_seqlens[n + 1] : a.T_total;
@@ -116,66 +295,25 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
         return;
     }
 
-    const int tensor = (int)(wid / per_tensor);            // 0 q, 1 k, 2 v, 3 decay
+    const int tensor = (int)(wid / per_tensor);            // 0 q, 1 k, 2 v
     const int64_t rest = wid % per_tensor;
     const int64_t tblock = rest / nslice;
     const int slice = (int)(rest % nslice);
-    const int row = lane >> 4;
-    const int h = 4 * slice + row;
-    const int c8 = 8 * (lane & 15);
+    const int h = 2 * slice + (lane >> 5);
+    const int c4 = 4 * (lane & 31);
     const bool live = h < a.H;
-    const int hc = live ? h * kHeadDim + c8 : c8;           // channel offset in a token row
+    const int hc = live ? h * kHeadDim + c4 : c4;           // channel offset in a token row
 
     const int64_t t0 = tblock * a.tb;
     const int64_t t1 = t0 + a.tb < a.T_total ? t0 + a.tb : a.T_total;
     const TIn* x = static_cast<const TIn*>(a.x[tensor]);
     TIn* out = static_cast<TIn*>(a.out[tensor]);
 
-    if (tensor == 3) {
-        // ---- log alpha = -5 sigmoid(a + bias); beta = sigmoid(b) ----
-        float bias[8];
-        {
-            const floatx4 b0 = *reinterpret_cast<const floatx4*>(a.a_bias + hc);
-            const floatx4 b1 = *reinterpret_cast<const floatx4*>(a.a_bias + hc + 4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                bias[e] = b0[e];
-                bias[4 + e] = b1[e];
-            }
-        }
-        const TIn* braw = static_cast<const TIn*>(a.b_raw);
-        TIn* beta = static_cast<TIn*>(a.beta);
-        const bool blane = live && c8 == 0;
-        for (int64_t tb = t0; tb < t1; tb += kPU) {
-            Raw8<TIn> xv[kPU];
-            float bv[kPU];
-#pragma unroll
-            for (int u = 0; u < kPU; ++u) {
-                const int64_t t = tb + u;
-                if (t < t1 && live) xv[u].load(x + (size_t)t * HD + hc);
-                bv[u] = (t < t1 && blane) ? to_f32(braw[(size_t)t * a.H + h]) : 0.f;
-            }
-#pragma unroll
-            for (int u = 0; u < kPU; ++u) {
-                const int64_t t = tb + u;
-                if (t < t1 && live) {
-                    float y[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) y[e] = -5.f * sigmoid(xv[u][e] + bias[e]);
-                    store8(out + (size_t)t * HD + hc, y);
-                    if (blane) beta[(size_t)t * a.H + h] = from_f32<TIn>(sigmoid(bv[u]));
-                }
-            }
-        }
-        return;
-    }
-
-    // ---- q, k, v: convolution window, Swish, L2 norm (q, k) ----
-    float w[4][8];  // w[j][e]: tap j multiplies the input 3 - j tokens back
+    float w[4][4];  // w[j][e]: tap j multiplies the input 3 - j tokens back
     {
         const float* wp = a.conv_w + ((size_t)tensor * HD + hc) * kConvW;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < 4; ++e) {
             const floatx4 t = *reinterpret_cast<const floatx4*>(wp + e * kConvW);
 #pragma unroll
             for (int j = 0; j < 4; ++j) w[j][e] = t[j];
@@ -202,74 +340,106 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
         bos = a.cu_seqlens[n];
         eos = a.cu_seqlens[n + 1];
     }
-    float win[kHist][8];   // inputs t-3, t-2, t-1
+    float win[kHist][4];   // inputs t-3, t-2, t-1
 #pragma unroll
     for (int p = 0; p < kHist; ++p) {
         const int64_t tp = t0 - kHist + p;
         if (tp >= bos) {
-            if (live) load8(x + (size_t)tp * HD + hc, win[p]);
+            if (live) load4(x + (size_t)tp * HD + hc, win[p]);
         } else if (si) {
-            if (live) load8(si + hist_off(n, (int)(tp - bos + kHist)), win[p]);
+            if (live) load4(si + hist_off(n, (int)(tp - bos + kHist)), win[p]);
         } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) win[p][e] = 0.f;
+            for (int e = 0; e < 4; ++e) win[p][e] = 0.f;
         }
     }
 
-    for (int64_t tb = t0; tb < t1; tb += kPU) {
-        Raw8<TIn> xv[kPU];
+    // the block's rows of x and of the output as buffer resources (32-bit
+    // offsets; a lane past the last head gets an offset past the end, so its
+    // loads read 0 and its stores are dropped)
+    const uint32_t blk_bytes = (uint32_t)((t1 - t0) * HD * (int64_t)sizeof(TIn));
+    const rsrc_t xr = make_rsrc_u32(x + (size_t)t0 * HD, blk_bytes);
+    const rsrc_t outr = make_rsrc_u32(out + (size_t)t0 * HD, blk_bytes);
+    const uint32_t lane_off = live ? (uint32_t)(hc * (int)sizeof(TIn)) : 0x80000000u;
+    const uint32_t row_b = (uint32_t)(HD * (int)sizeof(TIn));
+    // one token: convolution window, Swish, L2 norm, store
+    auto token = [&](int64_t t, const Raw4<TIn>& xt) {
+        float y[4], ss = 0.f;
 #pragma unroll
-        for (int u = 0; u < kPU; ++u)
-            if (tb + u < t1 && live) xv[u].load(x + (size_t)(tb + u) * HD + hc);
+        for (int e = 0; e < 4; ++e) {
+            const float c = w[3][e] * xt[e] + w[2][e] * win[2][e] + w[1][e] * win[1][e] +
+                            w[0][e] * win[0][e];
+            y[e] = c * sigmoid(c);
+            ss += y[e] * y[e];
+            win[0][e] = win[1][e];
+            win[1][e] = win[2][e];
+            win[2][e] = xt[e];
+        }
+        if (norm) {
+            const float r = __builtin_amdgcn_rsqf(row32_sum(ss) + a.l2_eps);
 #pragma unroll
-        for (int u = 0; u < kPU; ++u) {
-            const int64_t t = tb + u;
-            if (t >= t1) break;
-            while (t == eos) {   // a new sequence starts here (skipping empty ones)
+            for (int e = 0; e < 4; ++e) y[e] *= r;
+        }
+        buf_store4(outr, lane_off + (uint32_t)(t - t0) * row_b, y, (TIn*)nullptr);
+    };
+    auto store_hist = [&]() {
+        if (so && live) {
+#pragma unroll
+            for (int p = 0; p < kHist; ++p) store4(so + hist_off(n, p), win[p]);
+        }
+    };
+    for (int64_t tb = t0; tb < t1;) {
+        if (tb + kLA <= t1 && tb + kLA <= eos) {
+            // a run of kLA tokens inside one sequence: all loads in flight,
+            // then the tokens in order, one token's arithmetic live at a time
+            Raw4<TIn> xv[kLA];
+            const uint32_t ob = lane_off + (uint32_t)(tb - t0) * row_b;
+#pragma unroll
+            for (int u = 0; u < kLA; ++u) xv[u] = buf_raw4(xr, ob + u * row_b, (const TIn*)nullptr);
+#pragma unroll
+            for (int u = 0; u < kLA; ++u) {
+                token(tb + u, xv[u]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            tb += kLA;
+            if (tb == eos) store_hist();
+        } else {
+            // a sequence boundary or the block's end is near: one token
+            while (tb == eos) {   // a new sequence starts here (skipping empty ones)
                 ++n;
                 bos = eos;
                 eos = a.cu_seqlens[n + 1];
 #pragma unroll
                 for (int p = 0; p < kHist; ++p) {
-                    if (si && live) load8(si + hist_off(n, p), win[p]);
+                    if (si && live) load4(si + hist_off(n, p), win[p]);
                     else {
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) win[p][e] = 0.f;
+                        for (int e = 0; e < 4; ++e) win[p][e] = 0.f;
                     }
                 }
             }
-            float y[8], ss = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float c = w[3][e] * xv[u][e] + w[2][e] * win[2][e] + w[1][e] * win[1][e] +
-                                w[0][e] * win[0][e];
-                y[e] = c * sigmoid(c);
-                ss += y[e] * y[e];
-                win[0][e] = win[1][e];
-                win[1][e] = win[2][e];
-                win[2][e] = xv[u][e];
-            }
-            if (norm) {
-                const float r = __builtin_amdgcn_rsqf(row16_sum(ss) + a.l2_eps);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) y[e] *= r;
-            }
-            if (live) {
-                store8(out + (size_t)t * HD + hc, y);
-                if (t == eos - 1 && so) {
-#pragma unroll
-                    for (int p = 0; p < kHist; ++p) store8(so + hist_off(n, p), win[p]);
-                }
-            }
+            token(tb, buf_raw4(xr, lane_off + (uint32_t)(tb - t0) * row_b, (const TIn*)nullptr));
+            ++tb;
+            if (tb == eos) store_hist();
         }
     }
+}
+
+// One launch: the convolution waves (q, k, v and the history of empty
+// sequences), then the gate waves.
+template <typename TIn>
+__global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a, int64_t conv_waves) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int64_t wid = (int64_t)blockIdx.x * 4 + wave;
+    if (wid < conv_waves) prologue_conv<TIn>(a, wid, lane);
+    else prologue_gate<TIn>(a, wid - conv_waves, lane);
 }
 
 template <typename TIn>
 __global__ __launch_bounds__(256) void epilogue_kernel(EpilogueArgs a) {
     // rows = (token, head) pairs; a wave covers 4 rows per step, kEU steps
     constexpr int kEU = 4;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int64_t rows = a.T_total * a.H;
     const int64_t r0 = ((int64_t)blockIdx.x * 4 + wave) * (4 * kEU) + (lane >> 4);
     const int c8 = 8 * (lane & 15);
@@ -313,11 +483,11 @@ __global__ __launch_bounds__(256) void epilogue_kernel(EpilogueArgs a) {
 
 template <typename TIn>
 hipError_t launch_prologue_t(const PrologueArgs& a, hipStream_t stream) {
-    const int64_t nslice = (a.H + 3) / 4;
-    const int64_t waves = 4 * (int64_t)a.n_tblocks * nslice + (a.state_out ? a.N : 0);
+    const int64_t cw = prologue_conv_waves(a.n_tblocks, a.H, a.state_out ? a.N : 0);
+    const int64_t waves = cw + prologue_gate_waves(a.n_tblocks, a.H);
     const int64_t wgs = (waves + 3) / 4;
     if (wgs == 0) return hipSuccess;
-    prologue_kernel<TIn><<<dim3((unsigned)wgs), dim3(256), 0, stream>>>(a);
+    prologue_kernel<TIn><<<dim3((unsigned)wgs), dim3(256), 0, stream>>>(a, cw);
     return hipGetLastError();
 }
 
