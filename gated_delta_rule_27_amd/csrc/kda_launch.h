@@ -229,7 +229,7 @@ constexpr int kPrologueLookahead = 8;   // tokens the prologue loads ahead per l
 // overhead.
 inline int32_t prologue_tokens_per_wave(int64_t T_total, int32_t H) {
     const int64_t nslice = (H + 3) / 4;
-    int32_t tb = 32;
+    int32_t tb = 64;
     while (tb > kPrologueLookahead && 4 * nslice * ((T_total + tb - 1) / tb) < 8192) tb /= 2;
     return tb;
 }

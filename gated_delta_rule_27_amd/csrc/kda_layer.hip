@@ -12,20 +12,21 @@
 // Epilogue ("A third gate: control what leaves the module"; "Inside a KDA
 // Layer"): y = RMSNorm_head(o) * w * sigmoid(g).
 //
-// Both are HBM-bound streams (a few flops per byte): what sets their speed
-// is the number of bytes each CU keeps in flight, so the kernels are shaped
-// for registers (occupancy) and long load runs.  Convolution kernel: one
-// wave per (tensor q / k / v, 256-channel slice of a token row = 2 heads,
-// block of consecutive tokens).  Lane l holds channels 4 (l % 32) .. +3 of
-// head 2 slice + l / 32, so every wave-wide load is 512 contiguous bytes
-// (bf16) and all 64 lanes sit at the same token: the sequence bookkeeping of
-// a packed batch (where a sequence starts, where it ends) is wave-uniform
-// scalar work.  Each lane walks its token block in order, keeping the last
-// three inputs in registers (the convolution window), with 16 tokens of
-// loads in flight, so every input is loaded once, plus three rows of history
-// per block.  The L2 norm of a head is a 32-lane butterfly.  Gate kernel
-// (decay and write gates): one wave per 4 heads of a token block, lane =
-// 8 channels.  The epilogue maps one 16-lane group per (token, head) row.
+// Both are HBM-bound streams (a few flops per byte), addressed through
+// buffer resources with 32-bit offsets.  Prologue, one launch: gate waves
+// (decay and write gates: one wave per 4 heads of a token block, lane = 8
+// channels), then convolution waves: one per (tensor q / k / v, 256-channel
+// slice of a token row = 2 heads, block of consecutive tokens).  Lane l
+// holds channels 4 (l % 32) .. +3 of head 2 slice + l / 32, so every
+// wave-wide load is 512 contiguous bytes (bf16) and all 64 lanes sit at the
+// same token: the sequence bookkeeping of a packed batch (where a sequence
+// starts, where it ends) is wave-uniform scalar work.  Each lane walks its
+// token block in order, keeping the last three inputs in registers (the
+// convolution window), in runs of 8 tokens whose loads are issued one run
+// ahead, so every input is loaded once, plus three rows of history per
+// block.  The L2 norm of a head is a DPP row sum plus a 16-lane swizzle.
+// Epilogue: persistent waves over batches of 16 (token, head) rows, one
+// 16-lane group per row, the next batch's loads in flight.
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -100,7 +101,7 @@ struct Raw4<float> {
 };
 // tokens of loads in flight per lane of the convolution kernel
 template <typename T>
-constexpr int conv_lookahead() { return sizeof(T) == 2 ? 16 : 8; }
+constexpr int conv_lookahead() { return 8; }
 
 // 8 consecutive elements as loaded (kept packed until used, so a lane can
 // hold many tokens in flight in few registers)
@@ -363,14 +364,19 @@ __device__ __forceinline__ void prologue_conv(const PrologueArgs& a, int64_t wid
     const uint32_t lane_off = live ? (uint32_t)(hc * (int)sizeof(TIn)) : 0x80000000u;
     const uint32_t row_b = (uint32_t)(HD * (int)sizeof(TIn));
     // one token: convolution window, Swish, L2 norm, store
+    // (every multiply-add spelled out as one fused operation: the pipelined
+    // and the single-token paths must round identically, so that a sequence
+    // run in pieces reproduces the whole bit for bit)
     auto token = [&](int64_t t, const Raw4<TIn>& xt) {
         float y[4], ss = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float c = w[3][e] * xt[e] + w[2][e] * win[2][e] + w[1][e] * win[1][e] +
-                            w[0][e] * win[0][e];
+            const float c = __builtin_fmaf(
+                w[3][e], xt[e],
+                __builtin_fmaf(w[2][e], win[2][e],
+                               __builtin_fmaf(w[1][e], win[1][e], w[0][e] * win[0][e])));
             y[e] = c * sigmoid(c);
-            ss += y[e] * y[e];
+            ss = __builtin_fmaf(y[e], y[e], ss);
             win[0][e] = win[1][e];
             win[1][e] = win[2][e];
             win[2][e] = xt[e];
@@ -388,22 +394,38 @@ __device__ __forceinline__ void prologue_conv(const PrologueArgs& a, int64_t wid
             for (int p = 0; p < kHist; ++p) store4(so + hist_off(n, p), win[p]);
         }
     };
-    for (int64_t tb = t0; tb < t1;) {
-        if (tb + kLA <= t1 && tb + kLA <= eos) {
-            // a run of kLA tokens inside one sequence: all loads in flight,
-            // then the tokens in order, one token's arithmetic live at a time
-            Raw4<TIn> xv[kLA];
-            const uint32_t ob = lane_off + (uint32_t)(tb - t0) * row_b;
+    // runs of kLA tokens inside one sequence are software-pipelined: the
+    // next run's loads are issued before the current run is computed
+    auto run_ok = [&](int64_t tt) { return tt + kLA <= t1 && tt + kLA <= eos; };
+    auto load_run = [&](int64_t tt, Raw4<TIn> (&buf)[kLA]) {
+        const uint32_t ob = lane_off + (uint32_t)(tt - t0) * row_b;
 #pragma unroll
-            for (int u = 0; u < kLA; ++u) xv[u] = buf_raw4(xr, ob + u * row_b, (const TIn*)nullptr);
+        for (int u = 0; u < kLA; ++u) buf[u] = buf_raw4(xr, ob + u * row_b, (const TIn*)nullptr);
+    };
+    Raw4<TIn> cur[kLA];
+    bool have = false;   // cur holds the run starting at tb (wave-uniform)
+    for (int64_t tb = t0; tb < t1;) {
+        if (run_ok(tb)) {
+            if (!have) load_run(tb, cur);
+            const int64_t tn = tb + kLA;
+            const bool pre = run_ok(tn);
+            Raw4<TIn> nxt[kLA];
+            if (pre) load_run(tn, nxt);
+            // the tokens in order, one token's arithmetic live at a time
 #pragma unroll
             for (int u = 0; u < kLA; ++u) {
-                token(tb + u, xv[u]);
+                token(tb + u, cur[u]);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            tb += kLA;
+            tb = tn;
             if (tb == eos) store_hist();
+            have = pre;
+            if (pre) {
+#pragma unroll
+                for (int u = 0; u < kLA; ++u) cur[u] = nxt[u];
+            }
         } else {
+            have = false;
             // a sequence boundary or the block's end is near: one token
             while (tb == eos) {   // a new sequence starts here (skipping empty ones)
                 ++n;
@@ -425,48 +447,78 @@ __device__ __forceinline__ void prologue_conv(const PrologueArgs& a, int64_t wid
     }
 }
 
-// One launch: the convolution waves (q, k, v and the history of empty
-// sequences), then the gate waves.
+// One launch: the gate waves first (fewer and shorter), then the
+// convolution waves (q, k, v and the history of empty sequences), so that
+// the launch does not end on a tail of gate waves.
 template <typename TIn>
-__global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a, int64_t conv_waves) {
+__global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a, int64_t gate_waves) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int64_t wid = (int64_t)blockIdx.x * 4 + wave;
-    if (wid < conv_waves) prologue_conv<TIn>(a, wid, lane);
-    else prologue_gate<TIn>(a, wid - conv_waves, lane);
+    if (wid < gate_waves) prologue_gate<TIn>(a, wid, lane);
+    else prologue_conv<TIn>(a, wid - gate_waves, lane);
 }
+
+// Epilogue rows per 16-lane group of a wave and batch (rows 4 u + group)
+constexpr int kEU = 4;
+constexpr int kEpiRows = 4 * kEU;   // rows per wave and batch
 
 template <typename TIn>
 __global__ __launch_bounds__(256) void epilogue_kernel(EpilogueArgs a) {
-    // rows = (token, head) pairs; a wave covers 4 rows per step, kEU steps
-    constexpr int kEU = 4;
+    // rows = (token, head) pairs, in batches of kEpiRows consecutive rows;
+    // persistent waves take batches w, w + waves, ... with the next batch's
+    // loads in flight while the current one is computed.  A batch's o, g
+    // and y are buffer resources (32-bit offsets; rows past the end read 0
+    // and drop their stores).
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int64_t rows = a.T_total * a.H;
-    const int64_t r0 = ((int64_t)blockIdx.x * 4 + wave) * (4 * kEU) + (lane >> 4);
-    const int c8 = 8 * (lane & 15);
+    const int64_t nb = (rows + kEpiRows - 1) / kEpiRows;
+    const int64_t nw = (int64_t)gridDim.x * 4;
+    int64_t b = (int64_t)blockIdx.x * 4 + wave;
+    if (b >= nb) return;
+    const uint32_t es = (uint32_t)sizeof(TIn);
+    const int grp = lane >> 4, c8 = 8 * (lane & 15);
+    const uint32_t lane_off = (uint32_t)(grp * kHeadDim + c8) * es;
+    const uint32_t step = 4u * kHeadDim * es;
     const TIn* o = static_cast<const TIn*>(a.o);
     const TIn* g = static_cast<const TIn*>(a.g);
     TIn* y = static_cast<TIn*>(a.y);
-    float ov[kEU][8], gv[kEU][8];
+    auto rsrcs = [&](int64_t bb, rsrc_t& ro, rsrc_t& rg, rsrc_t& ry) {
+        const int64_t r0 = bb * kEpiRows;
+        const int64_t n = rows - r0 < kEpiRows ? rows - r0 : kEpiRows;
+        const uint32_t nbytes = (uint32_t)n * kHeadDim * es;
+        const size_t base = (size_t)r0 * kHeadDim;
+        ro = make_rsrc_u32(o + base, nbytes);
+        rg = make_rsrc_u32(g + base, nbytes);
+        ry = make_rsrc_u32(y + base, nbytes);
+    };
+    Raw8<TIn> ov[kEU], gv[kEU];
+    rsrc_t ro, rg, ry;
+    rsrcs(b, ro, rg, ry);
 #pragma unroll
     for (int u = 0; u < kEU; ++u) {
-        const int64_t r = r0 + 4 * u;
-        if (r < rows) {
-            load8(o + (size_t)r * kHeadDim + c8, ov[u]);
-            load8(g + (size_t)r * kHeadDim + c8, gv[u]);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ov[u][e] = gv[u][e] = 0.f;
-        }
+        ov[u] = buf_raw8(ro, lane_off + u * step, (const TIn*)nullptr);
+        gv[u] = buf_raw8(rg, lane_off + u * step, (const TIn*)nullptr);
     }
+    for (; b < nb; b += nw) {
+        // the next batch's loads first
+        const int64_t bn = b + nw;
+        Raw8<TIn> ov2[kEU], gv2[kEU];
+        rsrc_t ro2, rg2, ry2;
+        if (bn < nb) {
+            rsrcs(bn, ro2, rg2, ry2);
 #pragma unroll
-    for (int u = 0; u < kEU; ++u) {
-        const int64_t r = r0 + 4 * u;
-        float ss = 0.f;
+            for (int u = 0; u < kEU; ++u) {
+                ov2[u] = buf_raw8(ro2, lane_off + u * step, (const TIn*)nullptr);
+                gv2[u] = buf_raw8(rg2, lane_off + u * step, (const TIn*)nullptr);
+            }
+        }
+        int h = (int)((b * kEpiRows + grp) % a.H);   // head of this lane's first row
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ss += ov[u][e] * ov[u][e];
-        const float inv = __builtin_amdgcn_rsqf(row16_sum(ss) * (1.f / kHeadDim) + a.eps);
-        if (r < rows) {
-            const int h = (int)(r % a.H);
+        for (int u = 0; u < kEU; ++u) {
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss += ov[u][e] * ov[u][e];
+            const float inv = __builtin_amdgcn_rsqf(row16_sum(ss) * (1.f / kHeadDim) + a.eps);
             const float* wp = a.norm_w + (size_t)h * kHeadDim + c8;
             const floatx4 w0 = *reinterpret_cast<const floatx4*>(wp);
             const floatx4 w1 = *reinterpret_cast<const floatx4*>(wp + 4);
@@ -476,25 +528,39 @@ __global__ __launch_bounds__(256) void epilogue_kernel(EpilogueArgs a) {
                 const float wt = e < 4 ? w0[e] : w1[e - 4];
                 out[e] = ov[u][e] * inv * wt * sigmoid(gv[u][e]);
             }
-            store8(y + (size_t)r * kHeadDim + c8, out);
+            buf_store8(ry, lane_off + u * step, out, (TIn*)nullptr);
+            h += 4;
+            while (h >= a.H) h -= a.H;
+        }
+        if (bn < nb) {
+#pragma unroll
+            for (int u = 0; u < kEU; ++u) {
+                ov[u] = ov2[u];
+                gv[u] = gv2[u];
+            }
+            ro = ro2;
+            rg = rg2;
+            ry = ry2;
         }
     }
 }
 
 template <typename TIn>
 hipError_t launch_prologue_t(const PrologueArgs& a, hipStream_t stream) {
-    const int64_t cw = prologue_conv_waves(a.n_tblocks, a.H, a.state_out ? a.N : 0);
-    const int64_t waves = cw + prologue_gate_waves(a.n_tblocks, a.H);
+    const int64_t gw = prologue_gate_waves(a.n_tblocks, a.H);
+    const int64_t waves = gw + prologue_conv_waves(a.n_tblocks, a.H, a.state_out ? a.N : 0);
     const int64_t wgs = (waves + 3) / 4;
     if (wgs == 0) return hipSuccess;
-    prologue_kernel<TIn><<<dim3((unsigned)wgs), dim3(256), 0, stream>>>(a, cw);
+    prologue_kernel<TIn><<<dim3((unsigned)wgs), dim3(256), 0, stream>>>(a, gw);
     return hipGetLastError();
 }
 
 template <typename TIn>
 hipError_t launch_epilogue_t(const EpilogueArgs& a, hipStream_t stream) {
     const int64_t rows = a.T_total * a.H;
-    const int64_t wgs = (rows + 63) / 64;   // 4 waves x 16 rows
+    // persistent: at most 5 workgroups (20 waves) per compute unit
+    const int64_t need = (rows + 4 * kEpiRows - 1) / (4 * kEpiRows);
+    const int64_t wgs = need < 256 * 5 ? need : 256 * 5;
     if (wgs == 0) return hipSuccess;
     epilogue_kernel<TIn><<<dim3((unsigned)wgs), dim3(256), 0, stream>>>(a);
     return hipGetLastError();
