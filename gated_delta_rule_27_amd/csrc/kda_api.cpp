@@ -389,14 +389,16 @@ namespace {
 
 // kda_chunk_bwd's validation and launches.  no_workspace: validate every
 // argument except the workspace (which the caller supplies afterwards);
-// check_only: return after validation, before any HIP call.
+// check_only: return after validation, before any HIP call; side_stream:
+// the reverse recursion may run on the library's side stream (created on
+// first use), else everything runs in order on `stream`.
 kda_status chunk_bwd_impl(const void* q, const void* k, const void* v, const void* log_alpha,
                           const void* beta, const float* h0, const int32_t* cu_seqlens,
                           int32_t N, int64_t T_total, int32_t H, int32_t Dk, int32_t Dv,
                           kda_dtype dt, const void* dout, const float* dhT, void* dq, void* dk,
                           void* dv, void* dlog_alpha, void* dbeta, float* dh0, void* workspace,
                           size_t workspace_bytes, hipStream_t stream, bool check_only,
-                          bool no_workspace) {
+                          bool no_workspace, bool side_stream = true) {
     if (!valid_dtype(dt)) return KDA_ERR_BAD_DTYPE;
     if (N < 1 || T_total < 0 || H < 1 || H > KDA_MAX_HEADS || Dk != kda::kHeadDim ||
         Dv != kda::kHeadDim)
@@ -461,9 +463,6 @@ kda_status chunk_bwd_impl(const void* q, const void* k, const void* v, const voi
     if (overlaps_any(sws, {sdo, sdhT})) return KDA_ERR_ALIAS;
     if (check_only) return KDA_OK;
 
-    st = chunk_fwd_impl(q, k, v, log_alpha, beta, h0, cu_seqlens, N, T_total, H, Dk, Dv, dt,
-                        nullptr, nullptr, nullptr, 0, kda::kChunk, 0, sr, fflags, stream);
-    if (st != KDA_OK) return st;
     kda::BwdArgs a;
     a.q = q;
     a.k = k;
@@ -486,7 +485,29 @@ kda_status chunk_bwd_impl(const void* q, const void* k, const void* v, const voi
     a.states = states;
     a.dstates = dstates;
     a.n_slots = n_slots;
-    if (kda::launch_bwd(a, (int)dt, stream) != hipSuccess) return KDA_ERR_DEVICE;
+    // R (reverse recursion) on a side stream next to F (forward recursion,
+    // state table), G (gradients) after both.  For bf16 each recursion then
+    // takes one workgroup per (sequence, head), so that both sets of chains
+    // are resident together.  The allocation-free entry point runs F, R, G
+    // in order on the caller's stream.
+    hipStream_t side = side_stream ? kda::bwd_fork(stream) : nullptr;
+    if (side) {
+        const int split = dt == KDA_BF16 ? 1 : 0;
+        const bool r_ok = kda::launch_bwd_rev(a, (int)dt, split, side) == hipSuccess;
+        st = chunk_fwd_impl(q, k, v, log_alpha, beta, h0, cu_seqlens, N, T_total, H, Dk, Dv, dt,
+                            nullptr, nullptr, nullptr, 0, kda::kChunk, split, sr, fflags, stream);
+        const bool j_ok = kda::bwd_join(stream) == hipSuccess;
+        if (st != KDA_OK) return st;
+        if (!r_ok || !j_ok) return KDA_ERR_DEVICE;
+        if (kda::launch_bwd_grad(a, (int)dt, stream) != hipSuccess) return KDA_ERR_DEVICE;
+        return KDA_OK;
+    }
+    st = chunk_fwd_impl(q, k, v, log_alpha, beta, h0, cu_seqlens, N, T_total, H, Dk, Dv, dt,
+                        nullptr, nullptr, nullptr, 0, kda::kChunk, 0, sr, fflags, stream);
+    if (st != KDA_OK) return st;
+    if (kda::launch_bwd_rev(a, (int)dt, 0, stream) != hipSuccess ||
+        kda::launch_bwd_grad(a, (int)dt, stream) != hipSuccess)
+        return KDA_ERR_DEVICE;
     return KDA_OK;
 }
 
@@ -524,7 +545,7 @@ kda_status kda_chunk_bwd_noalloc(const void* q, const void* k, const void* v,
     if (kda::noalloc_scratch(&scratch) != hipSuccess || !scratch) return KDA_ERR_DEVICE;
     return chunk_bwd_impl(q, k, v, log_alpha, beta, h0, cu_seqlens, N, T_total, H, Dk, Dv, dt,
                           dout, dhT, dq, dk, dv, dlog_alpha, dbeta, dh0, scratch,
-                          KDA_BWD_NOALLOC_MAX_BYTES, stream, false, false);
+                          KDA_BWD_NOALLOC_MAX_BYTES, stream, false, false, false);
 }
 
 kda_status kda_prologue(const void* xq, const void* xk, const void* xv, const void* a_raw,

@@ -45,6 +45,8 @@
 // Precision as the forward: bf16 inputs use bf16 MFMA operands with fp32
 // accumulation, fp32 inputs fp32 MFMA; the chain rule and the 16 x 16
 // algebra run in fp32.
+#include <mutex>
+
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -1235,19 +1237,24 @@ hipError_t launch_dh(const BwdArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// (R): the reverse recursion of the state gradient; split = workgroups per
+// (sequence, head) for bf16 (0: by the number of chains)
 template <typename TIn>
-hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
+hipError_t launch_bwd_rev_t(const BwdArgs& a, int split, hipStream_t stream) {
     // enough chains of the recursion to fill the chip: split the value
     // columns (independent in it) when there are few (sequence, head) pairs
     const int64_t chains = (int64_t)a.N * a.H;
-    hipError_t e;
     if constexpr (sizeof(TIn) == 2)
-        e = launch_bwd_dh_ws(a, stream);   // pipelined, kda_bwd_ws.hip
+        return launch_bwd_dh_ws(a, split, stream);   // pipelined, kda_bwd_ws.hip
     else
-        e = chains >= 512   ? launch_dh<TIn, 4, 2>(a, stream)
-            : chains >= 256 ? launch_dh<TIn, 4, 1>(a, stream)
-                            : launch_dh<TIn, 2, 1>(a, stream);
-    if (e != hipSuccess) return e;
+        return chains >= 512   ? launch_dh<TIn, 4, 2>(a, stream)
+               : chains >= 256 ? launch_dh<TIn, 4, 1>(a, stream)
+                               : launch_dh<TIn, 2, 1>(a, stream);
+}
+
+// (G): every chunk's gradients, given both tables
+template <typename TIn>
+hipError_t launch_bwd_grad_t(const BwdArgs& a, hipStream_t stream) {
     const int64_t nwg = a.n_slots * a.H;
     if (a.T_total == 0 || nwg == 0) return hipSuccess;
     if constexpr (sizeof(TIn) == 2) {
@@ -1265,8 +1272,67 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+hipError_t launch_bwd_rev(const BwdArgs& a, int dtype, int split, hipStream_t stream) {
+    return dtype == 0 ? launch_bwd_rev_t<float>(a, split, stream)
+                      : launch_bwd_rev_t<bf16>(a, split, stream);
+}
+
+hipError_t launch_bwd_grad(const BwdArgs& a, int dtype, hipStream_t stream) {
+    return dtype == 0 ? launch_bwd_grad_t<float>(a, stream) : launch_bwd_grad_t<bf16>(a, stream);
+}
+
 hipError_t launch_bwd(const BwdArgs& a, int dtype, hipStream_t stream) {
-    return dtype == 0 ? launch_bwd_t<float>(a, stream) : launch_bwd_t<bf16>(a, stream);
+    const hipError_t e = launch_bwd_rev(a, dtype, 0, stream);
+    return e != hipSuccess ? e : launch_bwd_grad(a, dtype, stream);
+}
+
+// ---- a second stream per device for the recursion ---------------------------
+// The forward recursion (F, the state table) and the reverse one (R, the
+// state-gradient table) read only the inputs and write disjoint tables, so
+// R runs on a side stream next to F.  One side stream and two events per
+// device, created on first use and kept until the process ends; a mutex
+// held from fork to join keeps concurrent callers on one device from
+// interleaving their event records.
+namespace {
+constexpr int kMaxSideDevices = 64;
+std::mutex g_side_mu[kMaxSideDevices];
+hipStream_t g_side[kMaxSideDevices];
+hipEvent_t g_fork[kMaxSideDevices], g_join[kMaxSideDevices];
+}  // namespace
+
+hipStream_t bwd_fork(hipStream_t stream) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxSideDevices) return nullptr;
+    g_side_mu[dev].lock();
+    if (!g_side[dev]) {
+        hipStream_t st = nullptr;
+        hipEvent_t f = nullptr, j = nullptr;
+        if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess ||
+            hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess) {
+            g_side_mu[dev].unlock();
+            return nullptr;
+        }
+        g_side[dev] = st;
+        g_fork[dev] = f;
+        g_join[dev] = j;
+    }
+    if (hipEventRecord(g_fork[dev], stream) != hipSuccess ||
+        hipStreamWaitEvent(g_side[dev], g_fork[dev], 0) != hipSuccess) {
+        g_side_mu[dev].unlock();
+        return nullptr;
+    }
+    return g_side[dev];
+}
+
+hipError_t bwd_join(hipStream_t stream) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= kMaxSideDevices) return hipErrorInvalidDevice;
+    e = hipEventRecord(g_join[dev], g_side[dev]);
+    if (e == hipSuccess) e = hipStreamWaitEvent(stream, g_join[dev], 0);
+    g_side_mu[dev].unlock();
+    return e;
 }
 
 }  // namespace kda

@@ -385,10 +385,11 @@ hipError_t launch_rws(const BwdArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_bwd_dh_ws(const BwdArgs& a, hipStream_t stream) {
+hipError_t launch_bwd_dh_ws(const BwdArgs& a, int split, hipStream_t stream) {
     // as the forward: all 128 columns per workgroup from 256 chains, else two
     // workgroups of 64 columns per (sequence, head)
-    return (int64_t)a.N * a.H >= 256 ? launch_rws<8>(a, stream) : launch_rws<4>(a, stream);
+    if (split == 0) split = (int64_t)a.N * a.H >= 256 ? 1 : 2;
+    return split == 1 ? launch_rws<8>(a, stream) : launch_rws<4>(a, stream);
 }
 
 }  // namespace kda

@@ -216,11 +216,23 @@ struct BwdArgs {
 };
 
 hipError_t launch_bwd(const BwdArgs& a, int dtype, hipStream_t stream);
+// its two parts: the reverse recursion (split = workgroups per (sequence,
+// head), 0 = by the number of chains; bf16 only, fp32 chooses its own) and
+// the per-chunk gradients
+hipError_t launch_bwd_rev(const BwdArgs& a, int dtype, int split, hipStream_t stream);
+hipError_t launch_bwd_grad(const BwdArgs& a, int dtype, hipStream_t stream);
+// Work on a side stream of the current device: bwd_fork makes the side
+// stream wait for `stream`'s work so far and returns it (null if it cannot
+// be had: then run everything on `stream`); bwd_join makes `stream` wait for
+// the side stream's work so far.  A successful fork must be joined, on the
+// same host thread, before the next fork on that device.
+hipStream_t bwd_fork(hipStream_t stream);
+hipError_t bwd_join(hipStream_t stream);
 // The current device's address of the library's static scratch array of
 // KDA_BWD_NOALLOC_MAX_BYTES (kda_noalloc.hip), looked up once per device.
 hipError_t noalloc_scratch(void** ptr);
 // the reverse recursion for bf16 inputs, pipelined (kda_bwd_ws.hip)
-hipError_t launch_bwd_dh_ws(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_dh_ws(const BwdArgs& a, int split, hipStream_t stream);
 
 constexpr int kPrologueLookahead = 8;   // tokens the prologue loads ahead per lane
 

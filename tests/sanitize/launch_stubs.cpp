@@ -22,7 +22,11 @@ hipError_t launch_segment_scan(const float*, const float*, const float*, int32_t
 hipError_t launch_prologue(const PrologueArgs&, int, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_epilogue(const EpilogueArgs&, int, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_bwd(const BwdArgs&, int, hipStream_t) { return hipErrorInvalidValue; }
-hipError_t launch_bwd_dh_ws(const BwdArgs&, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_bwd_rev(const BwdArgs&, int, int, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_bwd_grad(const BwdArgs&, int, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_bwd_dh_ws(const BwdArgs&, int, hipStream_t) { return hipErrorInvalidValue; }
+hipStream_t bwd_fork(hipStream_t) { return nullptr; }
+hipError_t bwd_join(hipStream_t) { return hipErrorInvalidValue; }
 hipError_t noalloc_scratch(void** ptr) {
     *ptr = nullptr;
     return hipErrorInvalidValue;
