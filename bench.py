@@ -666,7 +666,7 @@ def main():
                    "dv_split": args.split or "auto"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "kda::chunk_ws_kernel",
+                     "traffic": traffic, "kernel": "kda::chunk_ws2_kernel",
                      "kernel_ms": round(avg_ms, 5), "kernel_ms_median": round(median(ms), 5),
                      "algorithmic_bytes": nbytes},
         "mfma": {"chunk_run": fr["chunk_run"],

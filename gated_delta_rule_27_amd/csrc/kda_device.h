@@ -14,6 +14,15 @@
 // directly a B operand over its 16 rows, so products that chain (state ->
 // pseudo-values -> new state) never leave registers.  An A operand is read
 // from LDS as a row with k contiguous.
+//
+// Invariant for every kernel of the library: an accumulator chain uses one
+// MFMA opcode.  A bf16 16x16x16 product accumulated straight onto the result
+// of a 16x16x32 chain (or the reverse) gave run-to-run wrong outputs on
+// MI355X; the hazard between different MFMA opcodes writing and reading one
+// accumulator was not characterised further.  Where a k = 16 product joins
+// a k = 32 chain it is issued as the k = 32 instruction with a zero upper
+// half (mma_bf16_k16_as_k32), or it starts a fresh accumulator that is added
+// on the VALU; fp32 16x16x4 products likewise keep accumulators of their own.
 #pragma once
 
 #include <hip/hip_runtime.h>
