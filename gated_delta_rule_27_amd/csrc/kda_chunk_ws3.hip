@@ -102,24 +102,6 @@ __device__ __forceinline__ bf16x8 to_bf16x8(floatx4 lo, floatx4 hi) {
     return __builtin_shufflevector(to_bf16x4(lo), to_bf16x4(hi), 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// One step of forward elimination on a column held down a row of 16 lanes:
-// x += x[I] * a (the pivot x[I] broadcast from lane I of the row), issued as
-// one VALU instruction with the broadcast folded into its first operand.
-// The leading two wait states cover the write of x by the previous step.
-template <int I>
-__device__ __forceinline__ void elim_step(float& x, float a) {
-    asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %0, %1 row_newbcast:%2 row_mask:0xf bank_mask:0xf"
-                 : "+v"(x)
-                 : "v"(a), "i"(I));
-}
-// The same pivot applied to a second column y from column x: y += x[I] * a.
-template <int I>
-__device__ __forceinline__ void elim_step2(float& y, float x, float a) {
-    asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
-                 : "+v"(y)
-                 : "v"(x), "v"(a), "i"(I));
-}
-
 // Values a prep lane carries from the prep of a chunk to the iteration that
 // writes the chunk's state operands (two iterations later).
 struct Held {
@@ -592,15 +574,15 @@ __global__ __launch_bounds__(Ws3Cfg::NT) void chunk_ws3_kernel(
                 float xb = 0.f;                      // column j, row 16 + r
                 float yb = xt;                       // column 16 + j, row 16 + r
                 // pivots 0..15 (rows of sub-tile a): both rows of column j
-#define KDA_SOLVE_A(I) elim_step2<I>(xb, xt, aba[I]); elim_step<I>(xt, aaa[I]);
+#define KDA_SOLVE_A(I) row_bcast_fmac2<I>(xb, xt, aba[I]); row_bcast_fmac<I>(xt, aaa[I]);
                 KDA_SOLVE_A(0) KDA_SOLVE_A(1) KDA_SOLVE_A(2) KDA_SOLVE_A(3)
                 KDA_SOLVE_A(4) KDA_SOLVE_A(5) KDA_SOLVE_A(6) KDA_SOLVE_A(7)
                 KDA_SOLVE_A(8) KDA_SOLVE_A(9) KDA_SOLVE_A(10) KDA_SOLVE_A(11)
                 KDA_SOLVE_A(12) KDA_SOLVE_A(13) KDA_SOLVE_A(14)
 #undef KDA_SOLVE_A
-                elim_step2<15>(xb, xt, aba[15]);
+                row_bcast_fmac2<15>(xb, xt, aba[15]);
                 // pivots 16..30 (rows of sub-tile b): columns j and 16 + j
-#define KDA_SOLVE_B(I) elim_step<I>(xb, abb[I]); elim_step<I>(yb, abb[I]);
+#define KDA_SOLVE_B(I) row_bcast_fmac<I>(xb, abb[I]); row_bcast_fmac<I>(yb, abb[I]);
                 KDA_SOLVE_B(0) KDA_SOLVE_B(1) KDA_SOLVE_B(2) KDA_SOLVE_B(3)
                 KDA_SOLVE_B(4) KDA_SOLVE_B(5) KDA_SOLVE_B(6) KDA_SOLVE_B(7)
                 KDA_SOLVE_B(8) KDA_SOLVE_B(9) KDA_SOLVE_B(10) KDA_SOLVE_B(11)

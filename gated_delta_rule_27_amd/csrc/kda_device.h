@@ -154,6 +154,36 @@ __device__ __forceinline__ float row_bcast(float x) {
         float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + N, 0xF, 0xF, true));
 }
 
+// One step of forward elimination on a column held down a row of 16 lanes:
+// x += x[I] * a (the pivot x[I] broadcast from lane I of the row), issued as
+// one VALU instruction with the broadcast folded into its first operand.
+// The leading two wait states cover the write of x by the previous step.
+template <int I>
+__device__ __forceinline__ void row_bcast_fmac(float& x, float a) {
+    asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %0, %1 row_newbcast:%2 row_mask:0xf bank_mask:0xf"
+                 : "+v"(x)
+                 : "v"(a), "i"(I));
+}
+// The same pivot applied to a second column y from column x: y += x[I] * a.
+template <int I>
+__device__ __forceinline__ void row_bcast_fmac2(float& y, float x, float a) {
+    asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+                 : "+v"(y)
+                 : "v"(x), "v"(a), "i"(I));
+}
+
+// Two independent columns x, y eliminated by the same pivot I (each with its
+// own pivot value): x += x[I] * a, y += y[I] * a, so that the two chains
+// interleave.
+template <int I>
+__device__ __forceinline__ void row_bcast_fmac_x2(float& x, float& y, float a) {
+    asm volatile(
+        "s_nop 1\n\tv_fmac_f32_dpp %0, %0, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+        : "+v"(x), "+v"(y)
+        : "v"(a), "i"(I));
+}
+
 // Shift with zero fill (lanes whose source is outside the row read 0); the
 // compiler fuses these into the consuming add (v_add_f32_dpp).
 template <int N>
