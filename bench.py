@@ -90,29 +90,34 @@ def time_launches(fn, steps, warmup, stream, ahead=False):
 
     With `ahead`, for kernels shorter than the host's own cost of a launch
     through Python: each group of launches is queued behind a spin kernel
-    long enough for the host to enqueue the whole group, so that every event
-    pair brackets the kernel alone and not the host's gaps (wall is then
-    None)."""
+    long enough for the host to enqueue the whole group, and a launch's time
+    is the spacing of its end event from the previous launch's end event in
+    the same group (the first launch of a group only opens it), so that the
+    host's gaps are not counted (wall is then None)."""
     import torch
     th = time.perf_counter()
     for i in range(warmup):
         fn(i)
     host_ms = (time.perf_counter() - th) * 1e3 / max(warmup, 1)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
     if ahead:
         cyc_per_ms = sleep_rate(torch, stream)
-        group = 20
-        for g0 in range(0, steps, group):
-            n = min(group, steps - g0)
+        group = 21
+        out = []
+        done = 0
+        while done < steps:
+            n = min(group, steps - done + 1)
+            ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
             torch.cuda._sleep(int(cyc_per_ms * (3.0 * n * host_ms + 0.5)))
-            for i in range(g0, g0 + n):
-                ev[i][0].record(stream)
-                fn(warmup + i)
-                ev[i][1].record(stream)
-        torch.cuda.synchronize()
-        return None, [a.elapsed_time(b) for a, b in ev]
+            for j in range(n):
+                fn(warmup + done + j)
+                ends[j].record(stream)
+            torch.cuda.synchronize()
+            out += [ends[j - 1].elapsed_time(ends[j]) for j in range(1, n)]
+            done += n - 1
+        return None, out
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
         ev[i][0].record(stream)
