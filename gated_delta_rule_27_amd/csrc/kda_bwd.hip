@@ -810,40 +810,59 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
         const bf16* S16;    // the state table entry (later chunks), or null
         const bf16* Dd;
     };
-    auto locate = [&](int64_t id) {
+    // This workgroup's items are ids blockIdx.x + k gridDim.x, in order, with
+    // (slot, head) = divmod(id, H) and n the sequence whose slots hold the
+    // slot.  Both only grow, so a cursor advances them incrementally (a step
+    // adds gridDim.x to the id; the sequence moves on while the next one's
+    // first slot is reached) instead of dividing and searching per item.
+    const int64_t gsz = gridDim.x;
+    const int64_t g_q = gsz / a.H;
+    const int g_r = (int)(gsz - g_q * a.H);
+    int64_t c_id = blockIdx.x, c_slot = c_id / a.H;
+    int c_h = (int)(c_id - c_slot * a.H);
+    int64_t c_n = 0, c_bos = 0, c_eos = a.T_total, c_next = INT64_MAX;
+    auto set_seq = [&](int64_t n) {
+        c_n = n;
+        c_bos = a.cu_seqlens[n];
+        c_eos = a.cu_seqlens[n + 1];
+        c_next = n + 1 < a.N ? chunk_slot(a.cu_seqlens[n + 1], n + 1) : INT64_MAX;
+    };
+    if (a.cu_seqlens && c_id < n_items) {
+        int64_t lo = 0, hi = a.N - 1;
+        while (lo < hi) {
+            const int64_t mid = (lo + hi + 1) >> 1;
+            if (chunk_slot(a.cu_seqlens[mid], mid) <= c_slot) lo = mid;
+            else hi = mid - 1;
+        }
+        set_seq(lo);
+    }
+    auto step = [&]() {
+        c_id += gsz;
+        c_slot += g_q;
+        c_h += g_r;
+        if (c_h >= a.H) {
+            c_h -= a.H;
+            ++c_slot;
+        }
+    };
+    // the item at the cursor or the first after it that is not in a gap of
+    // the table (a slot past the last chunk of a sequence); the cursor then
+    // moves past it
+    auto locate_next = [&]() {
         Item it{-1, 0, 0, 0, nullptr, nullptr, nullptr};
-        for (; id < n_items; id += gridDim.x) {
-            int64_t slot;
-            int h;
-            if (n_items <= 0x7fffffff) {
-                const uint32_t u = (uint32_t)id, hh = (uint32_t)a.H;
-                slot = (int64_t)(u / hh);
-                h = (int)(u - (uint32_t)slot * hh);
-            } else {
-                slot = id / a.H;
-                h = (int)(id % a.H);
-            }
-            int64_t n = 0;
-            if (a.cu_seqlens) {
-                int64_t lo = 0, hi = a.N - 1;
-                while (lo < hi) {
-                    const int64_t mid = (lo + hi + 1) >> 1;
-                    if (chunk_slot(a.cu_seqlens[mid], mid) <= slot) lo = mid;
-                    else hi = mid - 1;
-                }
-                n = lo;
-            }
-            const int64_t bos = a.cu_seqlens ? (int64_t)a.cu_seqlens[n] : 0;
-            const int64_t eos = a.cu_seqlens ? (int64_t)a.cu_seqlens[n + 1] : a.T_total;
-            const int64_t c = slot - chunk_slot(bos, n);
-            if (c < 0 || C * c >= eos - bos) continue;
-            it.id = id;
-            it.t0 = bos + C * c;
-            it.len = (int)((eos - it.t0) < C ? (eos - it.t0) : C);
-            it.h = h;
-            if (c == 0) it.S32 = a.h0 ? a.h0 + ((size_t)n * a.H + h) * kState : nullptr;
-            else it.S16 = static_cast<const bf16*>(a.states) + ((size_t)(slot - 1) * a.H + h) * kState;
-            it.Dd = static_cast<const bf16*>(a.dstates) + ((size_t)slot * a.H + h) * kState;
+        for (; c_id < n_items; step()) {
+            if (a.cu_seqlens)
+                while (c_slot >= c_next) set_seq(c_n + 1);
+            const int64_t c = c_slot - chunk_slot(c_bos, c_n);
+            if (c < 0 || C * c >= c_eos - c_bos) continue;
+            it.id = c_id;
+            it.t0 = c_bos + C * c;
+            it.len = (int)((c_eos - it.t0) < C ? (c_eos - it.t0) : C);
+            it.h = c_h;
+            if (c == 0) it.S32 = a.h0 ? a.h0 + ((size_t)c_n * a.H + c_h) * kState : nullptr;
+            else it.S16 = static_cast<const bf16*>(a.states) + ((size_t)(c_slot - 1) * a.H + c_h) * kState;
+            it.Dd = static_cast<const bf16*>(a.dstates) + ((size_t)c_slot * a.H + c_h) * kState;
+            step();
             break;
         }
         return it;
@@ -862,24 +881,26 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
     // the state rows are requested separately (load_s), a few phases later,
     // so that the two batches of requests overlap different phases
     auto load_s = [&](const Item& it) {
-        if (it.S16) {
+        const bf16* src = it.S16 ? it.S16 : it.Dd;   // (a first chunk's rows are replaced in pack)
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
-                sr8[m] = *reinterpret_cast<const bf16x8*>(it.S16 + state_off(m));
-        }
+        for (int m = 0; m < 4; ++m) sr8[m] = *reinterpret_cast<const bf16x8*>(src + state_off(m));
     };
     auto load = [&](const Item& it) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) dr8[m] = *reinterpret_cast<const bf16x8*>(it.Dd + state_off(m));
-        if (tid < 256 && tr < it.len) {
-            const size_t off = (size_t)(it.t0 + tr) * rowstride + (size_t)it.h * kHeadDim + tc8;
+        if (tid < 256) {
+            const int row = tr < it.len ? tr : it.len - 1;   // rows past the end are zeroed in store
+            const size_t off = (size_t)(it.t0 + row) * rowstride + (size_t)it.h * kHeadDim + tc8;
             rq = *reinterpret_cast<const bf16x8*>(q + off);
             rk = *reinterpret_cast<const bf16x8*>(k + off);
             rg = *reinterpret_cast<const bf16x8*>(lg + off);
             rv = *reinterpret_cast<const bf16x8*>(v + off);
             rdo = *reinterpret_cast<const bf16x8*>(dout + off);
         }
-        if (tid < it.len) rb = bt[(size_t)(it.t0 + tid) * a.H + it.h];
+        {
+            const int row = (tid & 15) < it.len ? (tid & 15) : it.len - 1;
+            rb = bt[(size_t)(it.t0 + row) * a.H + it.h];
+        }
     };
     // a sequence's first chunk starts from h0 (fp32, rows i) or zero; read
     // when the item is packed: 32 loads (8 rows i of this thread's columns
@@ -957,7 +978,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
         }
     };
 
-    Item cur = locate(blockIdx.x), prev{-1, 0, 0, 0, nullptr, nullptr, nullptr};
+    Item cur = locate_next(), prev{-1, 0, 0, 0, nullptr, nullptr, nullptr};
     if (cur.id >= 0) {
         load(cur);
         load_s(cur);
@@ -976,7 +997,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
     if (prev.id >= 0) write_out(prev);
     store(cur);
     __syncthreads();
-    const Item nxt = locate(cur.id + gridDim.x);
+    const Item nxt = locate_next();
 
     // ---- phase 1: decay and scaled operands (thread = key channel i and
     // rows 4 qr .. 4 qr + 3; the running sum is taken from row 0 in order) ----
@@ -1020,7 +1041,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
         for (int e = 0; e < 4; ++e) sg[(4 * qr + e) * kHeadDim + i] = Eq[e];
     }
 
-    if (nxt.id >= 0) load(nxt);   // in flight during phases 2 to 5 (state rows: 3 to 5)
+    load(nxt.id >= 0 ? nxt : cur);   // in flight during phases 2 to 5 (state rows: 3 to 5)
 
     // ---- phase 2: Gram tiles (waves 0, 1) ----
     if (wave < 2) {
@@ -1052,7 +1073,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
     }
     __syncthreads();
 
-    if (nxt.id >= 0) load_s(nxt);
+    load_s(nxt.id >= 0 ? nxt : cur);
 
     // ---- phase 3: column tile J = 16 wave .. +15 (state tiles from LDS) ----
     {

@@ -174,10 +174,13 @@ __device__ __forceinline__ void row_bcast_fmac2(float& y, float x, float a) {
 
 // Two independent columns x, y eliminated by the same pivot I (each with its
 // own pivot value): x += x[I] * a, y += y[I] * a, so that the two chains
-// interleave.
+// interleave.  Not volatile: the statement only reads and writes its
+// operands, so the compiler may schedule the wave's other work around the
+// chain (the register dependencies keep the steps in order, and anything it
+// places between two steps only adds wait states).
 template <int I>
 __device__ __forceinline__ void row_bcast_fmac_x2(float& x, float& y, float a) {
-    asm volatile(
+    asm(
         "s_nop 1\n\tv_fmac_f32_dpp %0, %0, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf\n\t"
         "v_fmac_f32_dpp %1, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
         : "+v"(x), "+v"(y)
