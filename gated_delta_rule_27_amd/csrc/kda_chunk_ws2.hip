@@ -98,7 +98,7 @@ __global__ __launch_bounds__((Ws2Cfg<NSW>::NT)) void chunk_ws2_kernel(
     const bf16* __restrict__ log_alpha, const bf16* __restrict__ beta,
     const float* __restrict__ h0, const int32_t* __restrict__ cu_seqlens, int64_t T_total,
     int32_t H, int32_t split, int32_t units, bf16* __restrict__ o, float* __restrict__ h_T,
-    int32_t flags) {
+    SnapArgs snap, int32_t flags) {
     typedef Ws2Cfg<NSW> K;
     constexpr int KP = K::KP, TP = K::TP, AP = K::AP, DV = K::DV, VP = K::VP;
 
@@ -196,8 +196,15 @@ __global__ __launch_bounds__((Ws2Cfg<NSW>::NT)) void chunk_ws2_kernel(
         const bool write_o = !(flags & kChunkNoOutput);
         const bool v_zero = flags & kChunkVZero;
         const bf16 z = (bf16)0.f;
+        // fp32 prefix snapshots: the state after every `every_chunks` full
+        // chunks of the sequence, entry snap_cu[n] + j - 1 for the j-th; the
+        // chunk after which the next one is due is counted down, so the
+        // test per chunk is one comparison
+        const int64_t snap_base = snap.snap_cu ? (int64_t)snap.snap_cu[n] : 0;
+        const uint32_t snap_lane = (uint32_t)((4 * g * kHeadDim + col0 + 16 * wave + l16) * 4);
+        int next_snap = snap.snap ? snap.every_chunks - 1 : 0x7fffffff;
 
-        auto state_iter = [&](auto kc, auto gram) {
+        auto state_iter = [&](auto kc, auto gram, int c) {
             constexpr int KK = decltype(kc)::value;
             constexpr int sc = slot4<KK, 0>();      // chunk c
             constexpr int sc2 = slot2<KK, 0>();
@@ -256,6 +263,21 @@ __global__ __launch_bounds__((Ws2Cfg<NSW>::NT)) void chunk_ws2_kernel(
             scale_row(std::integral_constant<int, 5>{});
             scale_row(std::integral_constant<int, 6>{});
             scale_row(std::integral_constant<int, 7>{});
+            if (c == next_snap) {   // uniform branch; rare
+                if ((int64_t)kC2 * (c + 1) <= seqlen) {
+                    const int64_t idx = snap_base + (c + 1) / snap.every_chunks - 1;
+                    if (idx < snap.n_snap) {
+                        const size_t eo = ((size_t)idx * (size_t)H + h) * (kHeadDim * kHeadDim);
+                        const rsrc_t rs = make_rsrc(snap.snap + eo, kHeadDim * kHeadDim * 4);
+#pragma unroll
+                        for (int it = 0; it < 8; ++it)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                buf_store_f32(S[it][e], rs, snap_lane, ((16 * it + e) * kHeadDim) * 4);
+                    }
+                }
+                next_snap += snap.every_chunks;
+            }
             // Gram tiles of chunk c+2: wave 0 A (stored negated), wave 1 P
             if constexpr (decltype(gram)::value) {
                 constexpr int sg = slot4<KK, 2>();
@@ -283,11 +305,11 @@ __global__ __launch_bounds__((Ws2Cfg<NSW>::NT)) void chunk_ws2_kernel(
             __syncthreads();
         };
         auto state_loop = [&](auto gram) {
-            for (int t = 0; t < trips; ++t) {
-                state_iter(std::integral_constant<int, 0>{}, gram);
-                state_iter(std::integral_constant<int, 1>{}, gram);
-                state_iter(std::integral_constant<int, 2>{}, gram);
-                state_iter(std::integral_constant<int, 3>{}, gram);
+            for (int t = 0, c = -3; t < trips; ++t, c += 4) {
+                state_iter(std::integral_constant<int, 0>{}, gram, c);
+                state_iter(std::integral_constant<int, 1>{}, gram, c + 1);
+                state_iter(std::integral_constant<int, 2>{}, gram, c + 2);
+                state_iter(std::integral_constant<int, 3>{}, gram, c + 3);
             }
         };
         if (wave < 2) state_loop(std::true_type{});
@@ -464,14 +486,14 @@ hipError_t launch_ws2_t(const ChunkArgs& a, hipStream_t stream) {
     kern<<<dim3((unsigned)nwg), dim3(K::NT), K::bytes, stream>>>(
         (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.log_alpha,
         (const bf16*)a.beta, a.h0, a.cu_seqlens, a.T_total, a.H, split, (int32_t)units,
-        (bf16*)a.o, a.h_T, a.flags);
+        (bf16*)a.o, a.h_T, a.snap, a.flags);
     return hipGetLastError();
 }
 
 }  // namespace
 
 bool chunk_ws2_supports(const ChunkArgs& a, int split) {
-    return split == 2 && !a.snap.snap && !(a.flags & (kChunkDualBM | kChunkSnapBf16 | kChunkSnapSlots));
+    return split == 2 && !(a.flags & (kChunkDualBM | kChunkSnapBf16 | kChunkSnapSlots));
 }
 
 hipError_t launch_chunk_ws2(const ChunkArgs& a, int split, hipStream_t stream) {
