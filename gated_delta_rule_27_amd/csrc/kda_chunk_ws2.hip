@@ -467,9 +467,14 @@ __global__ __launch_bounds__((Ws2Cfg<NSW>::NT)) void chunk_ws2_kernel(
             prep_iter(std::integral_constant<int, 3>{}, c + 3, solve, io);
         }
     };
-    if (pw < 2) prep_loop(std::true_type{}, std::false_type{});
-    else if (pw < 4) prep_loop(std::false_type{}, std::true_type{});
-    else prep_loop(std::false_type{}, std::false_type{});
+    if (pw < 2) {
+        if (io_wave) prep_loop(std::true_type{}, std::true_type{});
+        else prep_loop(std::true_type{}, std::false_type{});
+    } else if (io_wave) {
+        prep_loop(std::false_type{}, std::true_type{});
+    } else {
+        prep_loop(std::false_type{}, std::false_type{});
+    }
 }
 
 template <int NSW>
@@ -493,12 +498,12 @@ hipError_t launch_ws2_t(const ChunkArgs& a, hipStream_t stream) {
 }  // namespace
 
 bool chunk_ws2_supports(const ChunkArgs& a, int split) {
-    return split == 2 && !(a.flags & (kChunkDualBM | kChunkSnapBf16 | kChunkSnapSlots));
+    return (split == 1 || split == 2) && !(a.flags & (kChunkDualBM | kChunkSnapBf16 | kChunkSnapSlots));
 }
 
 hipError_t launch_chunk_ws2(const ChunkArgs& a, int split, hipStream_t stream) {
     if (!chunk_ws2_supports(a, split)) return hipErrorInvalidValue;
-    return launch_ws2_t<4>(a, stream);
+    return split == 1 ? launch_ws2_t<8>(a, stream) : launch_ws2_t<4>(a, stream);
 }
 
 }  // namespace kda
