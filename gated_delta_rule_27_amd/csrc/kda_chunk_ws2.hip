@@ -81,7 +81,8 @@ struct Ws2Cfg {
     static constexpr size_t T0 = P0 + 4 * szTile;           //  T, 2 slots
     static constexpr size_t VT0 = T0 + 2 * szTile;          //  V, 4 slots
     static constexpr size_t OT0 = VT0 + 4 * szVO;           //  O, 2 slots
-    static constexpr size_t bytes = OT0 + 2 * szVO;
+    static constexpr size_t TILE0 = OT0 + 2 * szVO;         //  per state wave: bf16 table staging
+    static constexpr size_t bytes = TILE0 + NSW * kC2 * kTileTP * 2;
     static_assert(bytes <= 160 * 1024, "LDS budget");
     static_assert(bytes % 16 == 0, "16-byte initialisation");
 };
@@ -196,11 +197,14 @@ __global__ __launch_bounds__((Ws2Cfg<NSW>::NT)) void chunk_ws2_kernel(
         const bool write_o = !(flags & kChunkNoOutput);
         const bool v_zero = flags & kChunkVZero;
         const bf16 z = (bf16)0.f;
-        // fp32 prefix snapshots: the state after every `every_chunks` full
-        // chunks of the sequence, entry snap_cu[n] + j - 1 for the j-th; the
-        // chunk after which the next one is due is counted down, so the
-        // test per chunk is one comparison
-        const int64_t snap_base = snap.snap_cu ? (int64_t)snap.snap_cu[n] : 0;
+        // Snapshots: the state after every `every_chunks` full chunks of the
+        // sequence, the j-th into entry base + j - 1 (base = snap_cu[n], or
+        // the sequence's first table slot for the backward's per-chunk
+        // tables); fp32 row-major, or bf16 transposed through a wave-private
+        // LDS tile (kChunkSnapBf16).  The chunk after which the next one is
+        // due is counted down, so the test per chunk is one comparison.
+        int64_t snap_idx = (flags & kChunkSnapSlots) ? chunk_slot(bos, n)
+                           : snap.snap_cu ? (int64_t)snap.snap_cu[n] : 0;
         const uint32_t snap_lane = (uint32_t)((4 * g * kHeadDim + col0 + 16 * wave + l16) * 4);
         int next_snap = snap.snap ? snap.every_chunks - 1 : 0x7fffffff;
 
@@ -263,11 +267,18 @@ __global__ __launch_bounds__((Ws2Cfg<NSW>::NT)) void chunk_ws2_kernel(
             scale_row(std::integral_constant<int, 5>{});
             scale_row(std::integral_constant<int, 6>{});
             scale_row(std::integral_constant<int, 7>{});
-            if (c == next_snap) {   // uniform branch; rare
-                if ((int64_t)kC2 * (c + 1) <= seqlen) {
-                    const int64_t idx = snap_base + (c + 1) / snap.every_chunks - 1;
-                    if (idx < snap.n_snap) {
-                        const size_t eo = ((size_t)idx * (size_t)H + h) * (kHeadDim * kHeadDim);
+            if (c == next_snap) {   // uniform branch
+                if ((int64_t)kC2 * (c + 1) <= seqlen && snap_idx < snap.n_snap) {
+                    const size_t eo = ((size_t)snap_idx * (size_t)H + h) * (kHeadDim * kHeadDim);
+                    if (flags & kChunkSnapBf16) {
+                        // transposed entry: this wave's 16 columns are 16
+                        // contiguous rows of 128
+                        const rsrc_t rs = make_rsrc(reinterpret_cast<bf16*>(snap.snap) + eo,
+                                                    kHeadDim * kHeadDim * 2);
+                        bf16* tile = reinterpret_cast<bf16*>(smem + K::TILE0) +
+                                     (size_t)wave * kC2 * kTileTP;
+                        store_tile_t(S, tile, rs, (uint32_t)((col0 + 16 * wave) * kHeadDim * 2), lane);
+                    } else {
                         const rsrc_t rs = make_rsrc(snap.snap + eo, kHeadDim * kHeadDim * 4);
 #pragma unroll
                         for (int it = 0; it < 8; ++it)
@@ -276,6 +287,7 @@ __global__ __launch_bounds__((Ws2Cfg<NSW>::NT)) void chunk_ws2_kernel(
                                 buf_store_f32(S[it][e], rs, snap_lane, ((16 * it + e) * kHeadDim) * 4);
                     }
                 }
+                ++snap_idx;
                 next_snap += snap.every_chunks;
             }
             // Gram tiles of chunk c+2: wave 0 A (stored negated), wave 1 P
@@ -498,7 +510,7 @@ hipError_t launch_ws2_t(const ChunkArgs& a, hipStream_t stream) {
 }  // namespace
 
 bool chunk_ws2_supports(const ChunkArgs& a, int split) {
-    return (split == 1 || split == 2) && !(a.flags & (kChunkDualBM | kChunkSnapBf16 | kChunkSnapSlots));
+    return (split == 1 || split == 2) && !(a.flags & kChunkDualBM);
 }
 
 hipError_t launch_chunk_ws2(const ChunkArgs& a, int split, hipStream_t stream) {
