@@ -93,7 +93,10 @@ constexpr int slot4() { return (K + OFF + 1) & 3; }
 template <int K, int OFF>
 constexpr int slot2() { return (K + OFF + 1) & 1; }
 
-template <int NSW>
+// NOOUT: a pass without outputs (the backward's forward recursion, segment
+// summaries): the state waves skip the Qtil S and P U products and the P
+// Gram tile, which only feed o.
+template <int NSW, bool NOOUT>
 __global__ __launch_bounds__((Ws2Cfg<NSW>::NT)) void chunk_ws2_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ log_alpha, const bf16* __restrict__ beta,
@@ -214,7 +217,8 @@ __global__ __launch_bounds__((Ws2Cfg<NSW>::NT)) void chunk_ws2_kernel(
             constexpr int sc2 = slot2<KK, 0>();
             const bf16* Kn = kn_s(sc) + l16 * KP;
             const bf16* Qs = qs_s(sc) + l16 * KP;
-            floatx4 X, Ov = zero4();
+            floatx4 X;
+            [[maybe_unused]] floatx4 Ov = zero4();
             if (v_zero) {
                 X = zero4();
             } else {
@@ -227,17 +231,19 @@ __global__ __launch_bounds__((Ws2Cfg<NSW>::NT)) void chunk_ws2_kernel(
             for (int b = 0; b < 4; ++b) {
                 const bf16x8 sb = acc_frag_k32(S[2 * b], S[2 * b + 1]);
                 X = mma_bf16_k32(frag_k32(Kn, 32 * b, g), sb, X);
-                Ov = mma_bf16_k32(frag_k32(Qs, 32 * b, g), sb, Ov);
+                if constexpr (!NOOUT) Ov = mma_bf16_k32(frag_k32(Qs, 32 * b, g), sb, Ov);
             }
             // U = T X, O += P U (as the k = 32 product with a zero upper half,
             // the same opcode as the Qtil S chain on this accumulator)
             const bf16x4 at = frag_k16(t_s(sc2) + l16 * TP, 0, g);
-            const bf16x4 ap = frag_k16(p_s(sc) + l16 * TP, 0, g);
             const floatx4 U = mma_bf16_k16(at, acc_frag_k16(X), zero4());
             const bf16x4 ub = acc_frag_k16(U);
-            Ov = mma_bf16_k32(bf16x8{ap[0], ap[1], ap[2], ap[3], z, z, z, z},
-                              bf16x8{ub[0], ub[1], ub[2], ub[3], z, z, z, z}, Ov);
-            if (write_o) {
+            if constexpr (!NOOUT) {
+                const bf16x4 ap = frag_k16(p_s(sc) + l16 * TP, 0, g);
+                Ov = mma_bf16_k32(bf16x8{ap[0], ap[1], ap[2], ap[3], z, z, z, z},
+                                  bf16x8{ub[0], ub[1], ub[2], ub[3], z, z, z, z}, Ov);
+            }
+            if (!NOOUT && write_o) {
                 bf16* ot = ot_s(sc2) + 16 * wave + l16;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) ot[(4 * g + e) * VP] = (bf16)Ov[e];
@@ -324,7 +330,8 @@ __global__ __launch_bounds__((Ws2Cfg<NSW>::NT)) void chunk_ws2_kernel(
                 state_iter(std::integral_constant<int, 3>{}, gram, c + 3);
             }
         };
-        if (wave < 2) state_loop(std::true_type{});
+        // (without outputs P is not needed: wave 1 forms no tile)
+        if (wave == 0 || (!NOOUT && wave == 1)) state_loop(std::true_type{});
         else state_loop(std::false_type{});
         if (h_T) {
             float* dst = h_T + ((size_t)n * (size_t)H + h) * (kHeadDim * kHeadDim);
@@ -489,11 +496,11 @@ __global__ __launch_bounds__((Ws2Cfg<NSW>::NT)) void chunk_ws2_kernel(
     }
 }
 
-template <int NSW>
+template <int NSW, bool NOOUT>
 hipError_t launch_ws2_t(const ChunkArgs& a, hipStream_t stream) {
     typedef Ws2Cfg<NSW> K;
     const int split = kHeadDim / K::DV;
-    auto kern = chunk_ws2_kernel<NSW>;
+    auto kern = chunk_ws2_kernel<NSW, NOOUT>;
     static std::atomic<uint64_t> lds_set{0};
     hipError_t e = raise_lds_limit_once((const void*)kern, (int)K::bytes, lds_set);
     if (e != hipSuccess) return e;
@@ -515,7 +522,9 @@ bool chunk_ws2_supports(const ChunkArgs& a, int split) {
 
 hipError_t launch_chunk_ws2(const ChunkArgs& a, int split, hipStream_t stream) {
     if (!chunk_ws2_supports(a, split)) return hipErrorInvalidValue;
-    return split == 1 ? launch_ws2_t<8>(a, stream) : launch_ws2_t<4>(a, stream);
+    if (a.flags & kChunkNoOutput)
+        return split == 1 ? launch_ws2_t<8, true>(a, stream) : launch_ws2_t<4, true>(a, stream);
+    return split == 1 ? launch_ws2_t<8, false>(a, stream) : launch_ws2_t<4, false>(a, stream);
 }
 
 }  // namespace kda
