@@ -226,15 +226,18 @@ __global__ __launch_bounds__((RwsCfg<NSW>::NT)) void bwd_dh_ws_kernel(BwdArgs a,
                 const float* Gm = gam_s(y);
                 const bf16* Qs = qs_s(y);
                 const bf16* Kn = kn_s(y);
+                // both terms as one k = 32 product: this lane's eight k slots are
+                // (dO, token 4g + e) and (dX, token 4g + e), e = 0..3, matched by
+                // the Qt^T and -Kt^T rows 16 it .. +15 over the same tokens
                 const bf16x4 dob16 = acc_frag_k16(dob), dX16 = acc_frag_k16(dX);
+                const bf16x8 bx{dob16[0], dob16[1], dob16[2], dob16[3], dX16[0], dX16[1], dX16[2], dX16[3]};
 #pragma unroll
                 for (int it = 0; it < 8; ++it) {
                     const floatx4 gm = *reinterpret_cast<const floatx4*>(Gm + 16 * it + 4 * g);
-                    floatx4 d = D[it] * gm;
-                    // Qt^T and -Kt^T rows 16 it .. +15 over tokens 4g .. 4g+3
-                    d = mma_bf16_k16(lds_col4(Qs + 4 * g * KP + 16 * it, KP, l16), dob16, d);
-                    d = mma_bf16_k16(lds_col4(Kn + 4 * g * KP + 16 * it, KP, l16), dX16, d);
-                    D[it] = d;
+                    const bf16x4 qa = lds_col4(Qs + 4 * g * KP + 16 * it, KP, l16);
+                    const bf16x4 ka = lds_col4(Kn + 4 * g * KP + 16 * it, KP, l16);
+                    D[it] = mma_bf16_k32(bf16x8{qa[0], qa[1], qa[2], qa[3], ka[0], ka[1], ka[2], ka[3]},
+                                         bx, D[it] * gm);
                 }
             }
             if (wave < 2) {
