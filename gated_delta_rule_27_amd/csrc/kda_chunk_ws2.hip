@@ -52,11 +52,12 @@ constexpr int kC2 = 16;       // tokens per chunk
 constexpr int kXcd2 = 8;      // MI355X accelerator complex dies
 constexpr float kLog2e2 = 1.4426950408889634f;
 
-template <int NSW_>
+template <int NSW_, bool DUAL = false>
 struct Ws2Cfg {
-    static constexpr int NSW = NSW_;             // state waves (16 value columns each)
+    static constexpr int NSW = NSW_;             // state waves per pass (16 value columns each)
+    static constexpr int NSA = DUAL ? 2 * NSW : NSW;   // state waves in all
     static constexpr int NPW = 8;                // prep waves
-    static constexpr int NT = 64 * (NSW + NPW);  // threads
+    static constexpr int NT = 64 * (NSA + NPW);  // threads
     static constexpr int DV = 16 * NSW;          // value columns per workgroup
     // bf16 stride of [token][channel] rows: 280 bytes, 6 banks apart, which
     // keeps 8-byte row reads, transposed column reads and 8-byte row writes
@@ -95,15 +96,19 @@ constexpr int slot2() { return (K + OFF + 1) & 1; }
 
 // NOOUT: a pass without outputs (the backward's forward recursion, segment
 // summaries): the state waves skip the Qtil S and P U products and the P
-// Gram tile, which only feed o.
-template <int NSW, bool NOOUT>
-__global__ __launch_bounds__((Ws2Cfg<NSW>::NT)) void chunk_ws2_kernel(
+// Gram tile, which only feed o.  DUAL (segment summaries, implies NOOUT):
+// two groups of NSW state waves share the prep waves' operands: waves
+// 0 .. NSW-1 run the B pass (h0 or zero start, V, h_T), waves
+// NSW .. 2 NSW-1 the M pass (identity start, V = 0, h_T2).
+template <int NSW, bool NOOUT, bool DUAL>
+__global__ __launch_bounds__((Ws2Cfg<NSW, DUAL>::NT)) void chunk_ws2_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ log_alpha, const bf16* __restrict__ beta,
     const float* __restrict__ h0, const int32_t* __restrict__ cu_seqlens, int64_t T_total,
     int32_t H, int32_t split, int32_t units, bf16* __restrict__ o, float* __restrict__ h_T,
-    SnapArgs snap, int32_t flags) {
-    typedef Ws2Cfg<NSW> K;
+    float* __restrict__ h_T2, SnapArgs snap, int32_t flags) {
+    typedef Ws2Cfg<NSW, DUAL> K;
+    static_assert(!DUAL || NOOUT, "the paired passes write no outputs");
     constexpr int KP = K::KP, TP = K::TP, AP = K::AP, DV = K::DV, VP = K::VP;
 
     // XCD-aware id: the column slices of one (sequence, head) share the
@@ -147,12 +152,14 @@ __global__ __launch_bounds__((Ws2Cfg<NSW>::NT)) void chunk_ws2_kernel(
     // nch - 1), rounded up to whole trips of four
     const int trips = (nch + 4 + 3) / 4;
 
-    if (nch == 0) {   // empty sequence: h_T = h0 (or zero / identity)
-        if (wave < NSW && h_T) {
-            const float* src = h0 ? h0 + ((size_t)n * (size_t)H + h) * (kHeadDim * kHeadDim) : nullptr;
-            const bool ident = flags & kChunkH0Identity;
-            float* dst = h_T + ((size_t)n * (size_t)H + h) * (kHeadDim * kHeadDim);
-            const int j = col0 + 16 * wave + l16;
+    if (nch == 0) {   // empty sequence: h_T = h0 (or zero / identity); the M pass: I
+        const bool mp = DUAL && wave >= NSW;
+        float* hT = mp ? h_T2 : h_T;
+        if (wave < K::NSA && hT) {
+            const float* src = (h0 && !mp) ? h0 + ((size_t)n * (size_t)H + h) * (kHeadDim * kHeadDim) : nullptr;
+            const bool ident = mp || (flags & kChunkH0Identity);
+            float* dst = hT + ((size_t)n * (size_t)H + h) * (kHeadDim * kHeadDim);
+            const int j = col0 + 16 * (mp ? wave - NSW : wave) + l16;
 #pragma unroll
             for (int it = 0; it < 8; ++it)
 #pragma unroll
@@ -175,21 +182,26 @@ __global__ __launch_bounds__((Ws2Cfg<NSW>::NT)) void chunk_ws2_kernel(
         __syncthreads();
     }
 
-    if (wave < NSW) {
+    if (wave < K::NSA) {
         // ======================= state waves =======================
         // the state chain is the pipeline's longest dependency path: its
         // waves win issue arbitration against the prep waves of their SIMD
         __builtin_amdgcn_s_setprio(3);
+        // sw: the wave's index within its pass (the M pass of DUAL takes
+        // the identity start and V = 0)
+        const bool mpass = DUAL && wave >= NSW;
+        const int sw = mpass ? wave - NSW : wave;
         floatx4 S[8];
         {
-            const float* src = h0 ? h0 + ((size_t)n * (size_t)H + h) * (kHeadDim * kHeadDim) : nullptr;
-            const int j = col0 + 16 * wave + l16;
+            const float* src = (h0 && !mpass) ? h0 + ((size_t)n * (size_t)H + h) * (kHeadDim * kHeadDim)
+                                              : nullptr;
+            const int j = col0 + 16 * sw + l16;
 #pragma unroll
             for (int it = 0; it < 8; ++it)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     S[it][e] = src ? src[(16 * it + 4 * g + e) * kHeadDim + j] : 0.f;
-            if (!src && (flags & kChunkH0Identity)) {
+            if (!src && (mpass || (flags & kChunkH0Identity))) {
 #pragma unroll
                 for (int it = 0; it < 8; ++it)
 #pragma unroll
@@ -198,7 +210,7 @@ __global__ __launch_bounds__((Ws2Cfg<NSW>::NT)) void chunk_ws2_kernel(
             }
         }
         const bool write_o = !(flags & kChunkNoOutput);
-        const bool v_zero = flags & kChunkVZero;
+        const bool v_zero = mpass || (flags & kChunkVZero);
         const bf16 z = (bf16)0.f;
         // Snapshots: the state after every `every_chunks` full chunks of the
         // sequence, the j-th into entry base + j - 1 (base = snap_cu[n], or
@@ -208,7 +220,7 @@ __global__ __launch_bounds__((Ws2Cfg<NSW>::NT)) void chunk_ws2_kernel(
         // due is counted down, so the test per chunk is one comparison.
         int64_t snap_idx = (flags & kChunkSnapSlots) ? chunk_slot(bos, n)
                            : snap.snap_cu ? (int64_t)snap.snap_cu[n] : 0;
-        const uint32_t snap_lane = (uint32_t)((4 * g * kHeadDim + col0 + 16 * wave + l16) * 4);
+        const uint32_t snap_lane = (uint32_t)((4 * g * kHeadDim + col0 + 16 * sw + l16) * 4);
         int next_snap = snap.snap ? snap.every_chunks - 1 : 0x7fffffff;
 
         auto state_iter = [&](auto kc, auto gram, int c) {
@@ -222,7 +234,7 @@ __global__ __launch_bounds__((Ws2Cfg<NSW>::NT)) void chunk_ws2_kernel(
             if (v_zero) {
                 X = zero4();
             } else {
-                const bf16x4 v4 = lds_col4(vt_s(sc) + 4 * g * VP + 16 * wave, VP, l16);
+                const bf16x4 v4 = lds_col4(vt_s(sc) + 4 * g * VP + 16 * sw, VP, l16);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) X[e] = (float)v4[e];
             }
@@ -244,7 +256,7 @@ __global__ __launch_bounds__((Ws2Cfg<NSW>::NT)) void chunk_ws2_kernel(
                                   bf16x8{ub[0], ub[1], ub[2], ub[3], z, z, z, z}, Ov);
             }
             if (!NOOUT && write_o) {
-                bf16* ot = ot_s(sc2) + 16 * wave + l16;
+                bf16* ot = ot_s(sc2) + 16 * sw + l16;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) ot[(4 * g + e) * VP] = (bf16)Ov[e];
             }
@@ -283,7 +295,7 @@ __global__ __launch_bounds__((Ws2Cfg<NSW>::NT)) void chunk_ws2_kernel(
                                                     kHeadDim * kHeadDim * 2);
                         bf16* tile = reinterpret_cast<bf16*>(smem + K::TILE0) +
                                      (size_t)wave * kC2 * kTileTP;
-                        store_tile_t(S, tile, rs, (uint32_t)((col0 + 16 * wave) * kHeadDim * 2), lane);
+                        store_tile_t(S, tile, rs, (uint32_t)((col0 + 16 * sw) * kHeadDim * 2), lane);
                     } else {
                         const rsrc_t rs = make_rsrc(snap.snap + eo, kHeadDim * kHeadDim * 4);
 #pragma unroll
@@ -333,9 +345,10 @@ __global__ __launch_bounds__((Ws2Cfg<NSW>::NT)) void chunk_ws2_kernel(
         // (without outputs P is not needed: wave 1 forms no tile)
         if (wave == 0 || (!NOOUT && wave == 1)) state_loop(std::true_type{});
         else state_loop(std::false_type{});
-        if (h_T) {
-            float* dst = h_T + ((size_t)n * (size_t)H + h) * (kHeadDim * kHeadDim);
-            const int j = col0 + 16 * wave + l16;
+        float* hT = mpass ? h_T2 : h_T;
+        if (hT) {
+            float* dst = hT + ((size_t)n * (size_t)H + h) * (kHeadDim * kHeadDim);
+            const int j = col0 + 16 * sw + l16;
 #pragma unroll
             for (int it = 0; it < 8; ++it)
 #pragma unroll
@@ -345,7 +358,7 @@ __global__ __launch_bounds__((Ws2Cfg<NSW>::NT)) void chunk_ws2_kernel(
     }
 
     // ========================= prep waves =========================
-    const int pw = wave - NSW;          // 0..7
+    const int pw = wave - K::NSA;       // 0..7
     const int r = l16;                  // token of the chunk
     const int ch0 = 16 * pw + 4 * g;    // first of this lane's 4 key channels
     bf16x4 rq[4], rk[4], rg[4];
@@ -496,11 +509,11 @@ __global__ __launch_bounds__((Ws2Cfg<NSW>::NT)) void chunk_ws2_kernel(
     }
 }
 
-template <int NSW, bool NOOUT>
+template <int NSW, bool NOOUT, bool DUAL = false>
 hipError_t launch_ws2_t(const ChunkArgs& a, hipStream_t stream) {
-    typedef Ws2Cfg<NSW> K;
+    typedef Ws2Cfg<NSW, DUAL> K;
     const int split = kHeadDim / K::DV;
-    auto kern = chunk_ws2_kernel<NSW, NOOUT>;
+    auto kern = chunk_ws2_kernel<NSW, NOOUT, DUAL>;
     static std::atomic<uint64_t> lds_set{0};
     hipError_t e = raise_lds_limit_once((const void*)kern, (int)K::bytes, lds_set);
     if (e != hipSuccess) return e;
@@ -510,18 +523,20 @@ hipError_t launch_ws2_t(const ChunkArgs& a, hipStream_t stream) {
     kern<<<dim3((unsigned)nwg), dim3(K::NT), K::bytes, stream>>>(
         (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.log_alpha,
         (const bf16*)a.beta, a.h0, a.cu_seqlens, a.T_total, a.H, split, (int32_t)units,
-        (bf16*)a.o, a.h_T, a.snap, a.flags);
+        (bf16*)a.o, a.h_T, a.h_T2, a.snap, a.flags);
     return hipGetLastError();
 }
 
 }  // namespace
 
 bool chunk_ws2_supports(const ChunkArgs& a, int split) {
-    return (split == 1 || split == 2) && !(a.flags & kChunkDualBM);
+    if (a.flags & kChunkDualBM) return split == 2 && !a.snap.snap && (a.flags & kChunkNoOutput);
+    return split == 1 || split == 2;
 }
 
 hipError_t launch_chunk_ws2(const ChunkArgs& a, int split, hipStream_t stream) {
     if (!chunk_ws2_supports(a, split)) return hipErrorInvalidValue;
+    if (a.flags & kChunkDualBM) return launch_ws2_t<4, true, true>(a, stream);
     if (a.flags & kChunkNoOutput)
         return split == 1 ? launch_ws2_t<8, true>(a, stream) : launch_ws2_t<4, true>(a, stream);
     return split == 1 ? launch_ws2_t<8, false>(a, stream) : launch_ws2_t<4, false>(a, stream);
