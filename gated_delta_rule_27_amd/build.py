@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libkda.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["kda_api.cpp", "kda_chunk.hip", "kda_chunk_ws.hip", "kda_chunk_ws2.hip", "kda_chunk_ws3.hip",
+SOURCES = ["kda_api.cpp", "kda_chunk.hip", "kda_chunk_ws2.hip", "kda_chunk_ws3.hip",
            "kda_decode.hip",
            "kda_segment.hip", "kda_layer.hip", "kda_bwd.hip",
            "kda_bwd_ws.hip", "kda_noalloc.hip"]

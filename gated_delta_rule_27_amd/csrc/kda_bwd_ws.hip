@@ -1,6 +1,6 @@
 // kda_bwd_ws.hip -- the reverse recursion of the KDA backward pass for bf16
 // inputs, wave-specialised and software-pipelined like the bf16 prefill
-// kernel (kda_chunk_ws.hip), walking the chunks of a sequence backwards.
+// kernel (kda_chunk_ws2.hip), walking the chunks of a sequence backwards.
 //
 // For a chunk with the decay-scaled operands of the forward (kda_bwd.hip,
 // header) and the state gradient D arriving from later chunks:

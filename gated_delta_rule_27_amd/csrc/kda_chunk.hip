@@ -604,7 +604,7 @@ hipError_t launch_chunk(const ChunkArgs& a, int dtype, int chunk, int split,
         return chunk == 16 ? launch_split<float, 16>(a, split, stream)
                            : launch_split<float, 32>(a, split, stream);
     }
-    if (chunk == 16 && split <= 2) return launch_chunk_ws(a, split, stream);
+    if (chunk == 16 && chunk_ws2_supports(a, split)) return launch_chunk_ws2(a, split, stream);
     if (chunk == 32 && chunk_ws3_supports(a, split)) return launch_chunk_ws3(a, split, stream);
     return chunk == 16 ? launch_split<bf16, 16>(a, split, stream)
                        : launch_split<bf16, 32>(a, split, stream);

@@ -1,14 +1,42 @@
-// kda_chunk_ws2.hip -- the wave-specialised bf16 prefill of kda_chunk_ws.hip,
-// cut down to the instructions the plain prefill needs (gfx950).
+// kda_chunk_ws2.hip -- wave-specialised, software-pipelined chunkwise KDA
+// prefill for bf16 inputs on gfx950 (CDNA4).
 //
-// Same mathematics and wave roles as kda_chunk_ws.hip (see its header): per
-// 16-token chunk with incoming state S0,
-//   Ktil = K o E, Qtil = Q o E, Khat = K / E, Kvec = K o Gamma / E,
-//   A = strict_lower(diag(beta) Ktil Khat^T), P = lower_incl(Qtil Khat^T),
-//   T = (I + A)^{-1} diag(beta), U = T (V - Ktil S0),
-//   O = Qtil S0 + P U,  S_C = Diag(Gamma) S0 + Kvec^T U,
-// with the decay reference at the chunk start, so every factor is <= e^80
-// ("From GPT-2 to Kimi K3", ch. 5 "K3's lower-bounded decay").
+// Same mathematics as kda_chunk.hip (chunkwise KDA with a UT transform and
+// pseudo-values; see that file), with chunks of C = 16 tokens: one 16-token
+// tile per chunk, so the decay reference point is the chunk start and every
+// right-hand decay factor is at most e^80 ("From GPT-2 to Kimi K3", ch. 5
+// "K3's lower-bounded decay"; "An infra-oriented diagram of Kimi K3", KDA
+// card).  For a chunk with incoming state S0:
+//   E_r = exp(G_r),  Gamma = exp(G_C)  (per key channel)
+//   Ktil = K o E, Qtil = Q o E, Khat = K / E, Kvec = K o Gamma / E
+//   A = strict_lower(diag(beta) Ktil Khat^T),  P = lower_incl(Qtil Khat^T)
+//   T = (I + A)^{-1} diag(beta)
+//   U = T (V - Ktil S0),  O = Qtil S0 + P U,  S_C = Diag(Gamma) S0 + Kvec^T U.
+//
+// Per chunk, the state-independent work (decay factors, operand scaling,
+// Gram tiles, the triangular solve) is a chain of short dependent steps with
+// little parallelism inside one chunk, while the state update is a chain
+// over chunks.  The pages' FlashKDA note describes overlapping the
+// token-parallel work with the head-parallel state propagation ("From GPT-2
+// to Kimi K3", ch. 6 "Training, prefill, and decode use different paths").
+// Here the overlap is inside one workgroup of NSW state waves and 8 prep
+// waves (12 waves for a 64-column slice, 16 for all 128 columns):
+//   state waves: each owns 16 value columns of the 128 x 128 state in MFMA
+//     accumulators for the whole sequence and runs the state chain of chunk
+//     c with no global memory operation of its own (V comes from an LDS
+//     ring, O goes to an LDS tile); state wave 0 (and 1, when o is written)
+//     then forms a Gram tile of chunk c+2 (A, P);
+//   prep waves, lane = (token r, 4 key channels): load q, k, log_alpha of a
+//     chunk four chunks ahead straight into the lanes that use them, take
+//     the cumulative log-decay over the chunk's 16 tokens as a DPP scan
+//     across the 16 lanes of a row and write the decay-scaled operands of
+//     chunk c+3 in token rows; prep waves 0 and 1 also run the UT solve of
+//     chunk c+1 (two columns of the 16 x 16 inverse per lane), and prep
+//     waves 2-3 (0-3 for all 128 columns) move V in and O out as 16-byte
+//     row pieces.
+// Every stage reads only what an earlier iteration wrote, so one barrier
+// per chunk is the only synchronisation; the state waves carry the chain
+// from chunk to chunk and issue at a raised priority.
 //
 // No unit bounds the per-chunk iteration: on MI355X (SQ counters, 4096
 // tokens x 96 heads) the VALU is about half busy, the LDS under half and the
@@ -16,8 +44,7 @@
 // issuing, a third waiting for issue behind the other waves of its SIMD and
 // the rest waiting on dependencies and the barrier.  The iteration is set
 // by the longest dependency chains and the instruction streams of the
-// busiest waves.  This version removes the per-iteration bookkeeping of the
-// general kernel:
+// busiest waves, hence:
 //   * every ring buffer holds 2 or 4 chunks and the loop is unrolled four
 //     times, so each ring slot is a compile-time constant (no modular
 //     arithmetic on the scalar unit);
@@ -27,18 +54,23 @@
 //     through their buffer resources (log alpha = 0, beta = 0, V = 0), which
 //     is again the identity; their outputs fall outside the resources and
 //     are dropped.
-//   * every wave runs a loop of its own role (state waves with or without
-//     the Gram tiles; prep waves with the UT solve, with V / O, or with the
+//   * every wave runs a loop of its own role (state waves with or without a
+//     Gram tile; prep waves with the UT solve, with V / O, or with the
 //     scaled operands alone), so that each loop body is one basic block per
 //     chunk and the compiler interleaves the long dependency chains (the
 //     solve, the state chain) with the independent work of the same wave.
 //     On MI355X this took the 4096-token, 96-head prefill from 245 us to
 //     229 us; spreading the same work over 16 waves was slower (260 us).
-// Pipeline: iteration c forms the scaled operands of chunk c+3 (prep waves),
-// the Gram tiles of chunk c+2 (state waves 0 and 1), the UT solve of chunk
-// c+1 (prep waves 0 and 1, two columns per lane) and the state update of
-// chunk c (state waves); one barrier per iteration.  The state waves carry
-// the chain from chunk to chunk and issue at a raised priority.
+// Variants, chosen at launch: NSW = 4 (split 2) or 8 (split 1); NOOUT for
+// passes without outputs (the backward's forward recursion, segment
+// summaries); DUAL (segment summaries, split 2) runs two groups of 4 state
+// waves, one per summary pass, over the operands the prep waves form once.
+// The state waves also write snapshots: fp32 states straight from their
+// accumulators, bf16 per-chunk tables through an LDS staging tile.
+//
+// Workgroup order is XCD-aware: the `split` workgroups that share one
+// (sequence, head) get ids with the same residue mod 8, i.e. the same XCD
+// and L2, where their identical q / k / log_alpha reads hit.
 #include <type_traits>
 
 #include "kda_device.h"

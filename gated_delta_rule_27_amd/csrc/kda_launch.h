@@ -121,9 +121,9 @@ struct DecodeMultiArgs {
 // dtype: 0 = fp32, 1 = bf16 (kda_dtype values).
 // chunk in {16, 32}; split = workgroups per head (value-column slices).
 // bf16 with chunk 16 and split 1 or 2 runs the wave-specialised pipelined
-// kernels (kda_chunk_ws.hip, kda_chunk_ws2.hip), bf16 with chunk 32 and split
-// 2 the pipelined 32-token kernel (kda_chunk_ws3.hip); every other
-// combination runs the phase-serial kernel (kda_chunk.hip).
+// kernel (kda_chunk_ws2.hip), bf16 with chunk 32 and split 2 the pipelined
+// 32-token kernel (kda_chunk_ws3.hip); every other combination runs the
+// phase-serial kernel (kda_chunk.hip).
 // (host-only choices, inline so that the C ABI's validation builds without
 // the kernels, e.g. for the host sanitizer tests)
 inline bool chunk_config_supported(int dtype, int chunk, int split) {
@@ -142,9 +142,8 @@ inline void chunk_default_config(int dtype, int64_t T_total, int32_t N, int32_t 
         *split = chains >= 256 ? 1 : 2;
     }
 }
-hipError_t launch_chunk_ws(const ChunkArgs& a, int split, hipStream_t stream);
-// the plain bf16 prefill at split 2 (no snapshots, no paired summaries), with
-// compile-time ring slots and no per-stage range checks (kda_chunk_ws2.hip)
+// the bf16 16-token prefill at split 1 or 2, with snapshots, pass flags and
+// (split 2 only, no snapshots) the paired summary passes (kda_chunk_ws2.hip)
 bool chunk_ws2_supports(const ChunkArgs& a, int split);
 hipError_t launch_chunk_ws2(const ChunkArgs& a, int split, hipStream_t stream);
 // the same cases with 32-token chunks of two 16-token sub-tiles

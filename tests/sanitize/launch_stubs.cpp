@@ -7,7 +7,6 @@
 
 namespace kda {
 
-hipError_t launch_chunk_ws(const ChunkArgs&, int, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_chunk(const ChunkArgs&, int, int, int, hipStream_t) {
     return hipErrorInvalidValue;
 }
