@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libkda.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["kda_api.cpp", "kda_chunk.hip", "kda_chunk_ws2.hip", "kda_chunk_ws3.hip",
+SOURCES = ["kda_api.cpp", "kda_chunk.hip", "kda_chunk_ws2.hip", "kda_chunk_ws2_s2.hip", "kda_chunk_ws3.hip",
            "kda_decode.hip",
            "kda_segment.hip", "kda_layer.hip", "kda_bwd.hip",
            "kda_bwd_ws.hip", "kda_noalloc.hip"]
@@ -28,11 +28,15 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wall", "-Wno-unused-result"]
+# per-source additions: the half-head prefill with outputs is scheduled by
+# LLVM's iterative ILP strategy (faster there, slower or spilling for the
+# other variants of the kernel)
+EXTRA = {"kda_chunk_ws2_s2.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 
 
 def _compile(src):
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + COMMON + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + COMMON + EXTRA.get(src, []) + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
@@ -58,7 +62,7 @@ def resource_usage(src):
     "scratch", "occupancy"}} (scratch in bytes per lane; non-zero means
     spills or a stack)."""
     import re
-    cmd = [HIPCC] + COMMON + ["-x", "hip", "--cuda-device-only", "-c", os.path.join(CSRC, src),
+    cmd = [HIPCC] + COMMON + EXTRA.get(src, []) + ["-x", "hip", "--cuda-device-only", "-c", os.path.join(CSRC, src),
                               "-o", os.devnull, "-Rpass-analysis=kernel-resource-usage"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

@@ -146,6 +146,8 @@ inline void chunk_default_config(int dtype, int64_t T_total, int32_t N, int32_t 
 // (split 2 only, no snapshots) the paired summary passes (kda_chunk_ws2.hip)
 bool chunk_ws2_supports(const ChunkArgs& a, int split);
 hipError_t launch_chunk_ws2(const ChunkArgs& a, int split, hipStream_t stream);
+// its split-2 launch with outputs (kda_chunk_ws2_s2.hip), arguments already checked
+hipError_t launch_chunk_ws2_split2(const ChunkArgs& a, hipStream_t stream);
 // the same cases with 32-token chunks of two 16-token sub-tiles
 // (kda_chunk_ws3.hip)
 bool chunk_ws3_supports(const ChunkArgs& a, int split);
