@@ -55,11 +55,14 @@ def prefill_bytes(T, H, N, esize=2, h0=False):
 
 
 def kernel_source_hash():
+    # the kernel sources and the build script (which holds the compiler flags)
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "gated_delta_rule_27_amd", "csrc")
-    for fn in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, fn), "rb") as f:
-            h.update(fn.encode())
+    pkg = os.path.join(ROOT, "gated_delta_rule_27_amd")
+    csrc = os.path.join(pkg, "csrc")
+    paths = [os.path.join(csrc, fn) for fn in sorted(os.listdir(csrc))]
+    for p in paths + [os.path.join(pkg, "build.py")]:
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
             h.update(f.read())
     return h.hexdigest()[:16]
 
