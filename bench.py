@@ -96,7 +96,11 @@ def time_launches(fn, steps, warmup, stream, ahead=False):
     long enough for the host to enqueue the whole group, and a launch's time
     is the spacing of its end event from the previous launch's end event in
     the same group (the first launch of a group only opens it), so that the
-    host's gaps are not counted (wall is then None)."""
+    host's gaps are not counted (wall is then None).  Callers of the ahead
+    mode take the median of the spacings: now and then (MI355X, ROCm 7.2)
+    a queue stalls for tens of milliseconds between two launches, one long
+    gap among back-to-back kernels, which alone would dominate the mean of
+    a 50 us kernel."""
     import torch
     th = time.perf_counter()
     for i in range(warmup):
@@ -403,7 +407,7 @@ def verify_replay(torch, kda, kda_inputs, dev, stream, steps, warmup):
     for name, fn in (("multi_verify", mverify), ("multi_replay", mreplay),
                      ("chunk_verify", cverify), ("chunk_replay", creplay)):
         _, ms = time_launches(fn, steps, warmup, stream, ahead=True)
-        res[name] = sum(ms) / len(ms)
+        res[name] = median(ms)
     state = B * H * D * D * 4
     out = {"requests": B, "H": H, "draft_tokens": draft, "accepted": acc,
            "kernel": "kda::decode_multi_kernel",
@@ -459,7 +463,7 @@ def context_parallel(torch, kda, kda_inputs, dev, stream, steps, warmup):
     for name, fn in (("summary_MB", summary_MB), ("summary_B", summary_B),
                      ("summary_M", summary_M), ("scan", scan), ("pass2", pass2), ("plain", plain)):
         _, ms = time_launches(fn, steps, warmup, stream, ahead=True)
-        res[name] = sum(ms) / len(ms)
+        res[name] = median(ms)
     tok = T * H * 2
     state = H * D * D * 4
     total = res["summary_MB"] + res["scan"] + res["pass2"]
@@ -509,7 +513,7 @@ def layer_elementwise(torch, kda, kda_inputs, dev, stream, steps, warmup, chunk_
 
         _, pms = time_launches(pro, steps, warmup, stream, ahead=True)
         _, ems = time_launches(epi, steps, warmup, stream, ahead=True)
-        pavg, eavg = sum(pms) / len(pms), sum(ems) / len(ems)
+        pavg, eavg = median(pms), median(ems)
         row = H * D * 2
         hist = 0 if so is None else 2 * d["N"] * 9 * row      # history read + written
         pbytes = T * (8 * row + 4 * H) + hist + (3 * 4 + 1) * H * D * 4
