@@ -772,9 +772,12 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) bf16 sU[C * KP];
     __shared__ __attribute__((aligned(16))) bf16 sdU[C * KP];
     __shared__ __attribute__((aligned(16))) bf16 sdX[C * KP];
-    __shared__ __attribute__((aligned(16))) float sq[C * kHeadDim];
-    __shared__ __attribute__((aligned(16))) float sk[C * kHeadDim];
-    __shared__ __attribute__((aligned(16))) float sg[C * kHeadDim];  // log alpha, then E
+    // fp32 token rows of q, k and log alpha (then E), padded by 4 floats so
+    // that rows fall 4 banks apart
+    constexpr int GP = kHeadDim + 4;
+    __shared__ __attribute__((aligned(16))) float sq[C * GP];
+    __shared__ __attribute__((aligned(16))) float sk[C * GP];
+    __shared__ __attribute__((aligned(16))) float sg[C * GP];  // log alpha, then E
     __shared__ __attribute__((aligned(16))) float sW[C * FP];
     __shared__ __attribute__((aligned(16))) float sM[C * FP];
     __shared__ __attribute__((aligned(16))) float sMt[C * FP];
@@ -785,7 +788,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) bf16 sT[C * CP];
     __shared__ __attribute__((aligned(16))) bf16 sTt[C * CP];
     __shared__ __attribute__((aligned(16))) bf16 sPt[C * CP];
-    __shared__ float sGam[kHeadDim];
+    __shared__ __attribute__((aligned(16))) float sGam[kHeadDim];
     __shared__ __attribute__((aligned(16))) float sBeta[C];
 
     const bf16* q = static_cast<const bf16*>(a.q);
@@ -947,9 +950,9 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
                              : float4{0.f, 0.f, 0.f, 0.f};
                 fg[hh] = tok ? float4{(float)rg[e], (float)rg[e + 1], (float)rg[e + 2], (float)rg[e + 3]}
                              : float4{0.f, 0.f, 0.f, 0.f};
-                *reinterpret_cast<float4*>(sq + tr * kHeadDim + tc8 + e) = fq[hh];
-                *reinterpret_cast<float4*>(sk + tr * kHeadDim + tc8 + e) = fk[hh];
-                *reinterpret_cast<float4*>(sg + tr * kHeadDim + tc8 + e) = fg[hh];
+                *reinterpret_cast<float4*>(sq + tr * GP + tc8 + e) = fq[hh];
+                *reinterpret_cast<float4*>(sk + tr * GP + tc8 + e) = fk[hh];
+                *reinterpret_cast<float4*>(sg + tr * GP + tc8 + e) = fg[hh];
             }
             *reinterpret_cast<bf16x8*>(sV + tr * KP + tc8) = tok ? rv : bf16x8{z, z, z, z, z, z, z, z};
             *reinterpret_cast<bf16x8*>(sdO + tr * KP + tc8) =
@@ -999,47 +1002,38 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
     __syncthreads();
     const Item nxt = locate_next();
 
-    // ---- phase 1: decay and scaled operands (thread = key channel i and
-    // rows 4 qr .. 4 qr + 3; the running sum is taken from row 0 in order) ----
-    float Eq[4];
+    // ---- phase 1: decay and scaled operands (lane = token row l16 and key
+    // channels 16 wave + 4 g .. +3; the running sum over the chunk's rows is
+    // a DPP prefix sum across the 16 lanes of a row, Gamma = E of row 15) ----
+    floatx4 Eq;
     {
-        const int i = tid & 127;
-        const int qr = __builtin_amdgcn_readfirstlane(tid >> 7);   // wave-uniform
-        float x[C], run[C], tot = 0.f;
-#pragma unroll
-        for (int r = 0; r < C; ++r) {
-            x[r] = sg[r * kHeadDim + i];
-            tot += x[r];
-            run[r] = tot;
-        }
-        const float gam = __expf(tot);
-        if (qr == 0) sGam[i] = gam;
-        // the running sum before row 4 qr, and the rows' log decays
-        const float pre = qr == 0 ? 0.f : qr == 1 ? run[3] : qr == 2 ? run[7] : run[11];
-        float xr[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            xr[e] = qr == 0 ? x[e] : qr == 1 ? x[4 + e] : qr == 2 ? x[8 + e] : x[12 + e];
-        float cum = pre;
+        const int c0 = 16 * wave + 4 * g;
+        const floatx4 lg4 = *reinterpret_cast<const floatx4*>(sg + l16 * GP + c0);
+        const floatx4 q4 = *reinterpret_cast<const floatx4*>(sq + l16 * GP + c0);
+        const floatx4 k4 = *reinterpret_cast<const floatx4*>(sk + l16 * GP + c0);
+        bf16x4 oq, okt, okh, okv;
+        floatx4 gm4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int r = 4 * qr + e;
-            cum += xr[e];
+            const float cum = row_prefix_sum(lg4[e]);
             const float E = __expf(cum), inv = __builtin_amdgcn_rcpf(E);
+            const float gam = row_bcast<15>(E);
             Eq[e] = E;
-            const float qv = sq[r * kHeadDim + i], kv = sk[r * kHeadDim + i];
-            sQt[r * KP + i] = (bf16)(qv * E);
-            sKt[r * KP + i] = (bf16)(kv * E);
-            sKh[r * KP + i] = (bf16)(kv * inv);
-            sKv[r * KP + i] = (bf16)(kv * gam * inv);
+            gm4[e] = gam;
+            oq[e] = (bf16)(q4[e] * E);
+            okt[e] = (bf16)(k4[e] * E);
+            okh[e] = (bf16)(k4[e] * inv);
+            okv[e] = (bf16)(k4[e] * gam * inv);
         }
+        *reinterpret_cast<bf16x4*>(sQt + l16 * KP + c0) = oq;
+        *reinterpret_cast<bf16x4*>(sKt + l16 * KP + c0) = okt;
+        *reinterpret_cast<bf16x4*>(sKh + l16 * KP + c0) = okh;
+        *reinterpret_cast<bf16x4*>(sKv + l16 * KP + c0) = okv;
+        if (l16 == C - 1) *reinterpret_cast<floatx4*>(sGam + c0) = gm4;
     }
     __syncthreads();
-    {   // log alpha is no longer read: keep E in its place
-        const int i = tid & 127, qr = tid >> 7;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sg[(4 * qr + e) * kHeadDim + i] = Eq[e];
-    }
+    // log alpha is no longer read: keep E in its place
+    *reinterpret_cast<floatx4*>(sg + l16 * GP + 16 * wave + 4 * g) = Eq;
 
     load(nxt.id >= 0 ? nxt : cur);   // in flight during phases 2 to 5 (state rows: 3 to 5)
 
@@ -1196,10 +1190,10 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int sr2 = 4 * g + e;
-            cE[e] = sg[sr2 * kHeadDim + i];
+            cE[e] = sg[sr2 * GP + i];
             cInv[e] = __builtin_amdgcn_rcpf(cE[e]);
-            cq[e] = sq[sr2 * kHeadDim + i];
-            ck[e] = sk[sr2 * kHeadDim + i];
+            cq[e] = sq[sr2 * GP + i];
+            ck[e] = sk[sr2 * GP + i];
             cKh[e] = ck[e] * cInv[e];
             cQt[e] = cq[e] * cE[e];
             cKt[e] = ck[e] * cE[e];
