@@ -875,7 +875,9 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
     // the current item is computed.  State tables (transposed, rows j):
     // instruction m of wave w reads the contiguous kilobyte (4 w + m) of the
     // entry, lane = key channels 8 (lane % 16) .. +7 of row j = (4 w + m) * 4
-    // + lane / 16; token rows: thread t < 256 takes row t / 16, 8 channels.
+    // + lane / 16; token rows: thread t >= 256 takes row (t - 256) / 16, 8
+    // channels (waves 4-7, which have room for the requests; waves 0 and 1
+    // carry the Gram tiles and the 16 x 16 chains).
     const int tr = (tid & 255) >> 4, tc8 = (tid & 15) * 8;
     bf16x8 sr8[4], dr8[4];  // this thread's four 8-column pieces of the state and its gradient
     bf16x8 rq, rk, rg, rv, rdo;
@@ -891,7 +893,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
     auto load = [&](const Item& it) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) dr8[m] = *reinterpret_cast<const bf16x8*>(it.Dd + state_off(m));
-        if (tid < 256) {
+        if (tid >= 256) {
             const int row = tr < it.len ? tr : it.len - 1;   // rows past the end are zeroed in store
             const size_t off = (size_t)(it.t0 + row) * rowstride + (size_t)it.h * kHeadDim + tc8;
             rq = *reinterpret_cast<const bf16x8*>(q + off);
@@ -900,7 +902,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
             rv = *reinterpret_cast<const bf16x8*>(v + off);
             rdo = *reinterpret_cast<const bf16x8*>(dout + off);
         }
-        {
+        if (tid >= 256 && tid < 256 + C) {
             const int row = (tid & 15) < it.len ? (tid & 15) : it.len - 1;
             rb = bt[(size_t)(it.t0 + row) * a.H + it.h];
         }
@@ -937,7 +939,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
             *reinterpret_cast<bf16x8*>(sSt + row * KP + col) = sr8[m];
             *reinterpret_cast<bf16x8*>(sDt + row * KP + col) = dr8[m];
         }
-        if (tid < 256) {
+        if (tid >= 256) {
             const bool tok = tr < it.len;
             const bf16 z = (bf16)0.f;
             float4 fq[2], fk[2], fg[2];
@@ -958,7 +960,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
             *reinterpret_cast<bf16x8*>(sdO + tr * KP + tc8) =
                 tok ? rdo : bf16x8{z, z, z, z, z, z, z, z};
         }
-        if (tid < C) sBeta[tid] = tid < it.len ? (float)rb : 0.f;
+        if (tid >= 256 && tid < 256 + C) sBeta[tid - 256] = (tid - 256) < it.len ? (float)rb : 0.f;
         for (int idx = tid; idx < C * CP; idx += 512) sT[idx] = sTt[idx] = sPt[idx] = z16();
     };
     // dq, dk and dlog alpha of an item are staged in LDS (over its Q~, K~
@@ -1035,7 +1037,12 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
     // log alpha is no longer read: keep E in its place
     *reinterpret_cast<floatx4*>(sg + l16 * GP + 16 * wave + 4 * g) = Eq;
 
-    load(nxt.id >= 0 ? nxt : cur);   // in flight during phases 2 to 5 (state rows: 3 to 5)
+    // the next item's reads, in flight during phases 2 to 5 (state rows: 3 to
+    // 5); waves 0 and 1 issue theirs after their own work of phase 2 (wave 0)
+    // and 4 (wave 1), so that the memory pipeline, busy with the other waves'
+    // requests, does not hold up the Gram products
+    const Item& ld_it = nxt.id >= 0 ? nxt : cur;
+    if (wave >= 2) load(ld_it);
 
     // ---- phase 2: Gram tiles (waves 0, 1) ----
     if (wave < 2) {
@@ -1053,6 +1060,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
             if (!isP) sW[r * FP + s] = (s < r) ? acc[e] : 0.f;
             else sPt[s * CP + r] = (bf16)((s <= r) ? acc[e] : 0.f);
         }
+        if (!isP) load(ld_it);
     }
     __syncthreads();
     // M = (I + A)^{-1} with A = diag(beta) W (waves 0-3, one element per lane)
@@ -1161,6 +1169,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel_bf16(BwdArgs a) {
             sdPo[r * FP + rp] = dp;
             sdPt[rp * FP + r] = dp;
         }
+        load(ld_it);
     }
     __syncthreads();
 
