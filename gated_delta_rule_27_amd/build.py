@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libkda.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = ["kda_api.cpp", "kda_chunk.hip", "kda_chunk_ws2.hip", "kda_chunk_ws2_s2.hip", "kda_chunk_ws3.hip",
-           "kda_decode.hip",
+           "kda_decode.hip", "kda_decode_multi.hip",
            "kda_segment.hip", "kda_layer.hip", "kda_bwd.hip",
            "kda_bwd_ws.hip", "kda_noalloc.hip"]
 ARCH = "gfx950"
@@ -28,10 +28,12 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wall", "-Wno-unused-result"]
-# per-source additions: the half-head prefill with outputs is scheduled by
-# LLVM's iterative ILP strategy (faster there, slower or spilling for the
-# other variants of the kernel)
-EXTRA = {"kda_chunk_ws2_s2.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
+# per-source additions: the half-head prefill with outputs and the
+# single-step decode are scheduled by LLVM's iterative ILP strategy (faster
+# there; slower or spilling for the other variants of the prefill kernel
+# and for the multi-token decode, which stay with the default)
+EXTRA = {"kda_chunk_ws2_s2.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+         "kda_decode.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 
 
 def _compile(src):
