@@ -265,9 +265,9 @@ def copy_bandwidth(torch, dev, stream):
 
 def mfma_fracs(T, H, ms, chunk_run=RUN_CHUNK, peak_tflops=BF16_PEAK_TFLOPS):
     """%MFMA of a prefill taking `ms`: at the chunk length the kernel runs
-    (the flops it executes) and, labelled, at F(64) (the survey's fixed
-    yardstick, which counts more chunk-local work than a 16-token kernel
-    does)."""
+    (the flops it executes) and, labelled, at F(64) (a fixed yardstick
+    that does not move with the chunk length; it counts more chunk-local
+    work than a 16-token kernel does)."""
     f_run = T * H * flops_per_head_token(chunk_run)
     f64 = T * H * flops_per_head_token(64)
     s = ms * 1e-3 * peak_tflops * 1e12
