@@ -45,6 +45,13 @@ def flops_per_head_token(C=64):
     return 6 * D * D + D * (5 * C + 3) + C * C / 3.0
 
 
+def decode_bytes(B, H, esize=2):
+    """Algorithmic HBM bytes of one decode step: every (sequence, head) state
+    read and written once (128 x 128 fp32 each way) plus the token's q, k,
+    v, log_alpha, beta in and o out."""
+    return B * H * (D * D * 4 * 2 + esize * (4 * D + 1 + D))
+
+
 def prefill_bytes(T, H, N, esize=2, h0=False):
     """Algorithmic HBM bytes of one prefill: q, k, v, log_alpha (d each),
     beta, o (d) per (token, head), plus 64 KiB per (sequence, head) for h_T
@@ -571,7 +578,7 @@ def decode_section(torch, kda, kda_inputs, dev, stream, steps, warmup, H=96):
     _, dms = time_launches(dstep, steps, warmup, stream)
     davg = sum(dms) / len(dms)
     state_bytes = B * H * D * D * 4 * 2
-    total_bytes = B * H * (D * D * 4 * 2 + 2 * (4 * D + 1 + D))
+    total_bytes = decode_bytes(B, H)
     del dd
     torch.cuda.empty_cache()
     return {
