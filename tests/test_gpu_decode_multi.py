@@ -118,3 +118,27 @@ def test_decode_multi_clamps_token_counts():
     torch.cuda.synchronize()
     assert torch.equal(Sa, Sb)
     assert torch.equal(oa[1:3], ob[1:3])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_multi_at_the_decay_bound(dtype):
+    """log alpha = -5 on every channel of every token (the bound of the input
+    contract): the kernel holds the state divided by the running decay of
+    each block of 8 tokens, so here that product falls to e^-40 before the
+    block ends; three blocks (K = 20) check the rescaling at every block
+    boundary against the oracle."""
+    kda = need_gpu()
+    B, K, H = 4, 20, 2
+    case(f"decode_multi at the decay bound dtype={dtype} B={B} K={K} H={H}")
+    d, w = _window_inputs(B, K, H, dtype, seed=777)
+    d["log_alpha"].fill_(-5.0)
+    S = d["h0"].clone()
+    o = torch.empty((B, K, H, 128), dtype=w["q"].dtype, device="cuda")
+    kda.kda_decode_multi(w["q"], w["k"], w["v"], w["log_alpha"], w["beta"], S, None,
+                         update_state=True, o=o)
+    torch.cuda.synchronize()
+    got_o, got_S = np_(o), np_(S)
+    for b in range(B):
+        ro, rh = _oracle_window(d, B, K, K, b)
+        check(f"o of sequence {b}", got_o[b], ro, TOL[dtype])
+        check(f"S of sequence {b}", got_S[b], rh[0], TOL[dtype])
